@@ -1,0 +1,217 @@
+"""Benchmark of the streaming-prefill attention hot path on one MI355X.
+
+One step = one window of the 36-layer backbone, for every layer:
+    fd_kv_insert_frame   new frame of 4 views -> ring slot           (insert)
+    fd_stream_attn       1,024 new-frame queries over 4,608 keys      (config 3)
+    fd_verify_attn       8-token block over 4,608 + 200 + 8 keys      (config 4)
+with 36 independent per-layer caches (717 MB of K/V, beyond the 256 MB Infinity Cache),
+the ring advancing one frame per step.  Inputs are synthetic, seeded, resident in HBM.
+
+Prints one JSON line.  `value` is the streaming-prefill attention throughput over the
+whole step (algorithmic FLOPs = 4*D*Hq*unmasked (q,k) pairs, divided by the step time);
+`roofline` is the streaming-prefill kernel alone (its launches timed with HIP events on
+the stream they run on); `roofline_verify` the verify call (split + merge kernels).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "streaming-prefill attn TFLOP/s + verify KV GB/s, % of MI355X roofline"
+
+
+def stream_pairs(g) -> int:
+    """Unmasked (query, key) pairs per head: token i of view v sees P + v*F*T + (F-1)*T + i + 1 keys."""
+    tot = 0
+    for v in range(g.n_views):
+        base = g.prefix_len + v * g.n_frames * g.tok_per_frame + (g.n_frames - 1) * g.tok_per_frame
+        tot += g.tok_per_frame * base + g.tok_per_frame * (g.tok_per_frame + 1) // 2
+    return tot
+
+
+def verify_pairs(g, n_tail, blk) -> int:
+    return blk * (g.window + n_tail) + blk * (blk + 1) // 2
+
+
+def cpu_baseline(layers_sample: int = 3):
+    """The fp64 oracle (as it stands) on a bounded sample: config-3 streaming layers + config-4 verifies."""
+    import numpy as np
+    import oracle.fd_oracle as fd_oracle
+    from streaming_kv_cache_view_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    w3, w4 = synth.CONFIGS[3], synth.CONFIGS[4]
+    g = w3.geom
+    flops = 0
+    t0 = time.perf_counter()
+    for layer in range(layers_sample):
+        for _t, _out in fd_oracle.run_stream_workload(w3, layer, [w3.first_t], synth):
+            flops += 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
+    t_stream = time.perf_counter() - t0
+    return {
+        "value": flops / t_stream / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(cores, blas_threads) if blas_threads > 1 else 1,
+        "kind": "oracle",
+        "sample": f"fp64 oracle streaming prefill of config 3, {layers_sample} of 36 layers "
+                  f"(window build + full re-rotation + explicit mask), {t_stream:.1f} s; "
+                  f"host cores visible {cores}, BLAS threads {blas_threads}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU leg (heads would shard "
+              "across GPUs with no exchange inside attention); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from streaming_kv_cache_view_amd import fd, synth
+
+    dev = "cuda"
+    w3, w4 = synth.CONFIGS[3], synth.CONFIGS[4]
+    g = w3.geom
+    assert w4.geom == g
+    L = args.layers
+    n_tail, blk = w4.n_tail, w4.blk_len
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    rnd = lambda *s: torch.randn(*s, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(L)]
+    vc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(L)]
+    kn = [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    vn = [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    qn = [rnd(g.n_new, g.n_q_heads, g.head_dim) for _ in range(L)]
+    out = [torch.empty(g.n_new, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
+    qb = [rnd(blk, g.n_q_heads, g.head_dim) for _ in range(L)]
+    kb = [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    vb = [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    vout = [torch.empty(blk, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
+    ws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    frame = [g.n_frames]   # newest frame index; the window starts full
+
+    def step(ev=None):
+        t = frame[0]
+        for l in range(L):
+            if ev is not None:
+                ev[0][l].record()
+            fd.kv_insert_frame(g, kc[l], vc[l], kn[l], vn[l], t)
+            if ev is not None:
+                ev[1][l].record()
+            fd.stream_attn(g, qn[l], kc[l], vc[l], t, out[l])
+            if ev is not None:
+                ev[2][l].record()
+            fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
+            if ev is not None:
+                ev[3][l].record()
+        frame[0] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-call timing (events on the stream the kernels are launched on)
+    ins_ms, att_ms, ver_ms = [], [], []
+    for _ in range(max(1, args.steps // 2)):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L)] for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        for l in range(L):
+            ins_ms.append(ev[0][l].elapsed_time(ev[1][l]))
+            att_ms.append(ev[1][l].elapsed_time(ev[2][l]))
+            ver_ms.append(ev[2][l].elapsed_time(ev[3][l]))
+    mean = lambda a: sum(a) / len(a)
+    att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
+
+    esz = 2
+    flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
+    vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
+                    + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+    ibytes_layer = 2 * 2 * g.n_views * g.tok_per_frame * g.n_kv_heads * g.head_dim * esz
+    value = flops_layer * L / (ms_per_step * 1e-3) / 1e12
+    att_tflops = flops_layer / (att_us * 1e-6) / 1e12
+    ver_gbs = vbytes_layer / (ver_us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16, resident in HBM)",
+        "config": {
+            "workload": f"backbone window step: {L} layers x (insert 4x256-token frame + streaming-prefill "
+                        f"attention, 1024 queries over 4608 keys, 32/8 heads, D=128 + 8-token verify over "
+                        f"4608+{n_tail}+{blk} keys)",
+            "layers": L, "views": g.n_views, "frames": g.n_frames, "tok_per_frame": g.tok_per_frame,
+            "prefix": g.prefix_len, "heads_q_kv": [g.n_q_heads, g.n_kv_heads], "head_dim": g.head_dim,
+            "parallelism": "1 GPU",
+        },
+        "roofline": {
+            "kernel": "stream_attn_kernel<bf16,128>",
+            "bound": "mfma",
+            "achieved": round(att_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "roofline_verify": {
+            "kernel": "fd_verify_attn (verify_split_kernel + verify_merge_kernel)",
+            "bound": "hbm",
+            "achieved": round(ver_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(ver_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
+                        "verify_attn": round(ver_us, 2)},
+        "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_layers)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * fdattn.h -- C ABI of the MI355X (gfx950) streaming-prefill attention library.
+ *
+ * The library implements the attention hot path of FlashDrive's streaming
+ * inference:
+ *   - a new window prefills only the newest frame of every camera view and
+ *     reuses the K/V of the earlier frames (FlashDrive README, technique list,
+ *     "Streaming inference"; FlashDrive technical summary, Methodology
+ *     section 1, "Algorithmic Shortcut");
+ *   - the token order is view-major and the new frame is placed at the end of
+ *     its own view's segment; a streaming mask keeps cross-view causality
+ *     (technical summary, Methodology section 1, "Token Layout");
+ *   - keys are cached before rotary embedding and rotated on the fly at the
+ *     position they hold in the current window (technical summary,
+ *     Methodology section 1, "Positional Encoding");
+ *   - the target model verifies an 8-token draft block in one forward pass
+ *     (README technique list, "Speculative reasoning"; technical summary,
+ *     Methodology section 2).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *   - Every pointer argument except `g` is a DEVICE pointer on the current
+ *     HIP device, 16-byte aligned.  The caller owns every buffer (caches,
+ *     inputs, outputs, workspace); the library allocates nothing and keeps no
+ *     state between calls, so calls on different streams with disjoint
+ *     buffers may run concurrently.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t, NULL = default
+ *     stream), like any kernel launch.
+ *   - Validation runs on the host before anything is enqueued; on error the
+ *     call returns a negative fd_status and has no effect.  A failed launch
+ *     returns FD_ERR_HIP.
+ *   - One call handles one layer; a multi-layer model loops over layers.
+ *
+ * Geometry and the physical K/V cache (one layer)
+ * -----------------------------------------------
+ *   N       = P + V*F*T           window rows (keys) per head
+ *   S_cap   = N + tail_cap        cache rows per head (fd_cache_rows)
+ *   k_cache, v_cache : [Hkv][S_cap][D] of in_dtype, row-major
+ *     rows [0, P)                      text prefix, written by the caller
+ *     rows P + (v*F + s)*T + i         token i of the frame held in slot s of view v
+ *     rows N + r, r < tail_cap         reasoning tokens then the verify block
+ *   Frame g of a view lives in slot g mod F (fd_kv_insert_frame).  At newest
+ *   frame t, slot s holds frame t - ((t - s) mod F); its age inside the view
+ *   is j = F-1 - ((t - s) mod F), and its token i sits at logical position
+ *       pos = pos_base + P + (v*F + j)*T + i.
+ *   Prefix row i sits at pos_base + i; tail row r at pos_base + N + r.
+ *   Keys are stored pre-RoPE; every kernel rotates them at these positions.
+ *
+ * RoPE and attention
+ * ------------------
+ *   Rotate-half RoPE with inverse frequency theta^(-2i/D): the pair
+ *   (x[i], x[i+D/2]) is rotated by pos * theta^(-2i/D).  Query head h reads
+ *   kv head h / (Hq/Hkv).  Scores are scaled by 1/sqrt(D); query position p_q
+ *   sees key position p_k iff p_k <= p_q.  Accumulation is fp32 throughout.
+ *   bf16 inputs: rotated Q and K are rounded to fp16 for Q K^T (fp16 matrix
+ *   cores; elements of rotated Q/K must stay within fp16 range, |x| < 65504),
+ *   softmax probabilities to bf16 for P V (bf16 matrix cores, V exact).
+ *   fp32 inputs: both products on the fp32 matrix cores.  Outputs are fp32
+ *   unless out_dtype is FD_BF16.
+ */
+#ifndef FDATTN_H
+#define FDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FD_F32 = 0, FD_BF16 = 1 } fd_dtype;
+
+typedef enum {
+  FD_OK = 0,
+  FD_ERR_NULL = -1,       /* a required pointer is NULL                              */
+  FD_ERR_GEOM = -2,       /* geometry out of range (see fd_geom)                     */
+  FD_ERR_DTYPE = -3,      /* in_dtype / out_dtype not an fd_dtype                    */
+  FD_ERR_FRAME = -4,      /* frame index < 0, or newest frame < F-1 (window not full) */
+  FD_ERR_ALIGN = -5,      /* a device pointer is not 16-byte aligned                 */
+  FD_ERR_TAIL = -6,       /* n_tail < 0, blk_len < 1, or n_tail + blk_len > tail_cap  */
+  FD_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than fd_verify_workspace_bytes */
+  FD_ERR_HIP = -8         /* the kernel launch failed                                */
+} fd_status;
+
+/* One layer's geometry.  Constraints checked by every call:
+ *   n_views, n_frames, tok_per_frame, n_q_heads, n_kv_heads >= 1; prefix_len, tail_cap >= 0;
+ *   n_q_heads % n_kv_heads == 0 and the group G = n_q_heads / n_kv_heads is 1, 2 or a
+ *   multiple of 4; head_dim is 64 or 128; rope_theta finite and > 1;
+ *   0 <= pos_base < 2^31; S_cap * head_dim < 2^31.                                         */
+typedef struct fd_geom {
+  int32_t n_views;        /* V: camera views                                  */
+  int32_t n_frames;       /* F: frames per view in one window (ring slots)    */
+  int32_t tok_per_frame;  /* T: tokens per frame                              */
+  int32_t prefix_len;     /* P: static text-prefix tokens before the views    */
+  int32_t n_q_heads;      /* Hq                                               */
+  int32_t n_kv_heads;     /* Hkv                                              */
+  int32_t head_dim;       /* D: 64 or 128                                     */
+  int32_t tail_cap;       /* rows after the window: reasoning tokens + block  */
+  double rope_theta;      /* RoPE base                                        */
+  int64_t pos_base;       /* position of the window's first token (0 normally) */
+  int32_t in_dtype;       /* fd_dtype of queries, keys, values and caches     */
+  int32_t out_dtype;      /* fd_dtype of attention outputs                    */
+} fd_geom;
+
+/* Rows of one head's K (or V) cache: P + V*F*T + tail_cap; -1 on invalid geometry. */
+int64_t fd_cache_rows(const fd_geom* g);
+
+/* Logical position of physical cache row `row` (0 <= row < S_cap) at newest frame
+ * `newest_frame`, as defined above.  Host-side helper; returns an fd_status. */
+int fd_key_position(const fd_geom* g, int64_t newest_frame, int64_t row, int64_t* pos);
+
+/* Insert the new frame of every view into its ring slot (Token Layout passage:
+ * the new frame goes to the end of each view's segment, the oldest one drops out).
+ *   k_new, v_new : [V][T][Hkv][D] in_dtype, pre-RoPE K and V of frame `frame_idx`.
+ *   Writes k_cache/v_cache rows P + (v*F + frame_idx mod F)*T + i for every v, i, head:
+ *   a bit-exact copy.  No other cache row is touched.  frame_idx >= 0.              */
+int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
+                       const void* k_new, const void* v_new,
+                       int64_t frame_idx, void* hip_stream);
+
+/* Streaming-prefill attention of the new frame of every view (Token Layout and
+ * Positional Encoding passages).
+ *   q_new  : [V*T][Hq][D] in_dtype, pre-RoPE; row v*T + i is token i of view v's
+ *            newest frame, which sits at position pos_base + P + (v*F + F-1)*T + i.
+ *   k_cache, v_cache : as above, holding frames newest_frame-F+1 .. newest_frame in
+ *            their slots (the caller inserts in order; the library does not check).
+ *   out    : [V*T][Hq][D] out_dtype.
+ *   Keys seen by token i of view v: the prefix, every frame of views < v, frames
+ *   of view v older than the newest, and tokens <= i of view v's newest frame.
+ *   newest_frame >= F-1 (full window); tail rows are not read.                      */
+int fd_stream_attn(const fd_geom* g, const void* q_new,
+                   const void* k_cache, const void* v_cache,
+                   int64_t newest_frame, void* out, void* hip_stream);
+
+/* Bytes of workspace fd_verify_attn needs for blocks of up to blk_len tokens
+ * (any n_tail with n_tail + blk_len <= tail_cap); 0 on invalid arguments.          */
+size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len);
+
+/* Speculative-verify attention of a draft block of blk_len tokens (README technique
+ * list, "Speculative reasoning"; technical summary, Methodology section 2).
+ *   q_blk  : [B][Hq][D] in_dtype, pre-RoPE; token b sits at pos_base + N + n_tail + b.
+ *   k_blk, v_blk : [B][Hkv][D] in_dtype, pre-RoPE.  They are copied bit-exactly into
+ *            cache rows N + n_tail + b (the tail), and attended from the inputs.
+ *   k_cache, v_cache : window at newest_frame plus n_tail valid reasoning rows
+ *            N .. N+n_tail-1 (written by the caller).
+ *   out    : [B][Hq][D] out_dtype.  Block token b sees the whole window, all n_tail
+ *            reasoning rows and block tokens <= b.
+ *   ws     : device workspace of ws_bytes >= fd_verify_workspace_bytes(g, blk_len);
+ *            scratch for split-KV partial results, no initial contents required.
+ *            Calls that share one workspace must not overlap.
+ *   Requires (Hq/Hkv) * blk_len <= 32, 1 <= blk_len, n_tail >= 0,
+ *   n_tail + blk_len <= tail_cap, newest_frame >= F-1.                              */
+int fd_verify_attn(const fd_geom* g, const void* q_blk,
+                   const void* k_blk, const void* v_blk,
+                   void* k_cache, void* v_cache, int64_t newest_frame,
+                   int32_t n_tail, int32_t blk_len,
+                   void* out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Static description of a status code. */
+const char* fd_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDATTN_H */

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (fd_api.cpp) and the kernels (fd_kernels.hip).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fdattn.h"
+
+namespace fd {
+
+constexpr int kMaxHalf = 64;      // D/2 for D = 128
+constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
+constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
+constexpr int kVerifyBlocksPerWave = 1;
+constexpr int kVerifyWaves = 4;
+
+// Everything a kernel needs about one call, passed by value as a kernel argument.
+struct KParams {
+  int32_t V, F, T, P, Hq, Hkv, D, G;
+  int32_t W;          // window rows P + V*F*T
+  int32_t S_cap;      // cache rows per head
+  int32_t s_new;      // slot of the newest frame: t mod F
+  int32_t out_bf16;   // 1 -> bf16 output, 0 -> fp32
+  // streaming kernel work decomposition
+  int32_t HPW;        // query heads per workgroup (min(G, 4))
+  int32_t TBW;        // 32-token query blocks per workgroup (4 / HPW)
+  int32_t n_hsub;     // G / HPW
+  int32_t nqb;        // ceil(T / (32*TBW))
+  // verify
+  int32_t n_tail, B, nblk, n_split;
+  int32_t pad0;
+  int64_t pos_base;
+  int64_t t;          // newest frame
+  float sm_scale_log2;  // log2(e) / sqrt(D)
+  float pad1;
+  double inv_freq[kMaxHalf];  // theta^(-2i/D), fp64
+};
+
+// Verify split bookkeeping shared by host and kernels.
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
+  return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock) + ceil_div(tail_rows, kVerifyBlock);
+}
+inline int verify_splits(int nblk) { return ceil_div(nblk, kVerifyWaves * kVerifyBlocksPerWave); }
+// fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
+constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
+constexpr size_t kVerifyWsHeader = 256;
+
+int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
+                  int slot, void* stream);
+int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,
+                  void* out, void* stream);
+int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb,
+                  void* kc, void* vc, void* out, void* ws, void* stream);
+
+}  // namespace fd

@@ -1,0 +1,134 @@
+"""Thin ctypes binding of libfdattn.so (C ABI in include/fdattn.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels.
+Tensors are torch tensors on the current HIP device (torch is used for device
+memory and streams); the call is enqueued on torch's current stream unless a
+stream handle is given.  There is no CPU fallback: importing this module
+raises if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfdattn.so")
+
+FD_F32, FD_BF16 = 0, 1
+STATUS = {0: "FD_OK", -1: "FD_ERR_NULL", -2: "FD_ERR_GEOM", -3: "FD_ERR_DTYPE", -4: "FD_ERR_FRAME",
+          -5: "FD_ERR_ALIGN", -6: "FD_ERR_TAIL", -7: "FD_ERR_WORKSPACE", -8: "FD_ERR_HIP"}
+
+
+class FdGeom(ctypes.Structure):
+    _fields_ = [
+        ("n_views", ctypes.c_int32), ("n_frames", ctypes.c_int32), ("tok_per_frame", ctypes.c_int32),
+        ("prefix_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("tail_cap", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+        ("pos_base", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+    ]
+
+
+class FdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({lib().fd_status_str(status).decode()})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfdattn.so once; raise (no fallback) if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built: run `python -m streaming_kv_cache_view_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        G = ctypes.POINTER(FdGeom)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.fd_cache_rows.argtypes, L.fd_cache_rows.restype = [G], i64
+        L.fd_key_position.argtypes, L.fd_key_position.restype = [G, i64, i64, ctypes.POINTER(i64)], ctypes.c_int
+        L.fd_kv_insert_frame.argtypes = [G, vp, vp, vp, vp, i64, vp]
+        L.fd_kv_insert_frame.restype = ctypes.c_int
+        L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp]
+        L.fd_stream_attn.restype = ctypes.c_int
+        L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
+        L.fd_verify_attn.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
+        L.fd_verify_attn.restype = ctypes.c_int
+        L.fd_status_str.argtypes, L.fd_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_stream_attn",
+           "fd_verify_workspace_bytes", "fd_verify_attn", "fd_status_str")
+
+
+def make_geom(g, out_dtype: str = "f32") -> FdGeom:
+    """FdGeom from any object with the fd_geom field names (dtype given as 'f32' / 'bf16')."""
+    if isinstance(g, FdGeom):
+        return g
+    code = {"f32": FD_F32, "bf16": FD_BF16}
+    return FdGeom(g.n_views, g.n_frames, g.tok_per_frame, g.prefix_len, g.n_q_heads, g.n_kv_heads,
+                  g.head_dim, g.tail_cap, float(g.rope_theta), int(g.pos_base), code[g.dtype],
+                  code[out_dtype])
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FdError(fn, status)
+
+
+def cache_rows(g) -> int:
+    return lib().fd_cache_rows(ctypes.byref(make_geom(g)))
+
+
+def key_position(g, newest_frame: int, row: int) -> int:
+    pos = ctypes.c_int64()
+    _check("fd_key_position", lib().fd_key_position(ctypes.byref(make_geom(g)), newest_frame, row,
+                                                    ctypes.byref(pos)))
+    return pos.value
+
+
+def kv_insert_frame(g, k_cache, v_cache, k_new, v_new, frame_idx: int, stream=None):
+    """k_new/v_new [V][T][Hkv][D] -> ring slot frame_idx mod F of k_cache/v_cache [Hkv][S_cap][D]."""
+    _check("fd_kv_insert_frame", lib().fd_kv_insert_frame(
+        ctypes.byref(make_geom(g)), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        int(frame_idx), _stream(stream)))
+
+
+def stream_attn(g, q_new, k_cache, v_cache, newest_frame: int, out, out_dtype: str = "f32", stream=None):
+    """out [V*T][Hq][D] = streaming-prefill attention of the new frame's queries q_new [V*T][Hq][D]."""
+    _check("fd_stream_attn", lib().fd_stream_attn(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(q_new), _ptr(k_cache), _ptr(v_cache),
+        int(newest_frame), _ptr(out), _stream(stream)))
+
+
+def verify_workspace_bytes(g, blk_len: int) -> int:
+    return lib().fd_verify_workspace_bytes(ctypes.byref(make_geom(g)), int(blk_len))
+
+
+def verify_attn(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame: int, n_tail: int, blk_len: int,
+                out, ws, ws_bytes: int | None = None, out_dtype: str = "f32", stream=None):
+    """out [B][Hq][D] = verify attention of the draft block; copies k_blk/v_blk into the tail rows."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("fd_verify_attn", lib().fd_verify_attn(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
+        _ptr(v_cache), int(newest_frame), int(n_tail), int(blk_len), _ptr(out), _ptr(ws), int(ws_bytes),
+        _stream(stream)))
