@@ -109,6 +109,7 @@ def main():
     vb = [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
     vout = [torch.empty(blk, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
     ws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=dev)
+    sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=dev)   # shared by layers
     torch.cuda.synchronize()
 
     frame = [g.n_frames]   # newest frame index; the window starts full
@@ -121,7 +122,7 @@ def main():
             fd.kv_insert_frame(g, kc[l], vc[l], kn[l], vn[l], t)
             if ev is not None:
                 ev[1][l].record()
-            fd.stream_attn(g, qn[l], kc[l], vc[l], t, out[l])
+            fd.stream_attn(g, qn[l], kc[l], vc[l], t, out[l], sws)
             if ev is not None:
                 ev[2][l].record()
             fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
@@ -187,7 +188,7 @@ def main():
             "parallelism": "1 GPU",
         },
         "roofline": {
-            "kernel": "stream_attn_kernel<bf16,128>",
+            "kernel": "fd_stream_attn (rope_window_kernel + stream_attn_kernel)",
             "bound": "mfma",
             "achieved": round(att_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -118,6 +118,11 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
                        const void* k_new, const void* v_new,
                        int64_t frame_idx, void* hip_stream);
 
+/* Bytes of workspace fd_stream_attn needs: the window's keys rotated at their current
+ * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); 0 on invalid
+ * geometry.  The size depends on the geometry only, so one workspace serves every layer. */
+size_t fd_stream_workspace_bytes(const fd_geom* g);
+
 /* Streaming-prefill attention of the new frame of every view (Token Layout and
  * Positional Encoding passages).
  *   q_new  : [V*T][Hq][D] in_dtype, pre-RoPE; row v*T + i is token i of view v's
@@ -125,12 +130,17 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
  *   k_cache, v_cache : as above, holding frames newest_frame-F+1 .. newest_frame in
  *            their slots (the caller inserts in order; the library does not check).
  *   out    : [V*T][Hq][D] out_dtype.
+ *   ws     : device workspace of ws_bytes >= fd_stream_workspace_bytes(g); the call first
+ *            rotates every window key at its shifted position into it (the cache keeps
+ *            the pre-RoPE keys), then attends over it.  No initial contents required;
+ *            calls that share one workspace must not overlap.
  *   Keys seen by token i of view v: the prefix, every frame of views < v, frames
  *   of view v older than the newest, and tokens <= i of view v's newest frame.
  *   newest_frame >= F-1 (full window); tail rows are not read.                      */
 int fd_stream_attn(const fd_geom* g, const void* q_new,
                    const void* k_cache, const void* v_cache,
-                   int64_t newest_frame, void* out, void* hip_stream);
+                   int64_t newest_frame, void* out, void* ws, size_t ws_bytes,
+                   void* hip_stream);
 
 /* Bytes of workspace fd_verify_attn needs for blocks of up to blk_len tokens
  * (any n_tail with n_tail + blk_len <= tail_cap); 0 on invalid arguments.          */

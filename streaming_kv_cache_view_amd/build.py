@@ -29,6 +29,9 @@ def command(out: str = LIB, extra=()) -> list[str]:
         f"--offload-arch={ARCH}",
         # packed fp32 VALU forms stay disabled (ordinary float code only)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the softmax reads S and rescales O with VALU
+        # instructions, which cannot address AGPRs; this avoids per-tile AGPR<->VGPR copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -100,16 +100,23 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache, const voi
                            hip_stream);
 }
 
+size_t fd_stream_workspace_bytes(const fd_geom* g) {
+  if (check_geom(g) != FD_OK) return 0;
+  const size_t window = size_t(g->prefix_len) + size_t(g->n_views) * g->n_frames * g->tok_per_frame;
+  return size_t(g->n_kv_heads) * window * g->head_dim * (g->in_dtype == FD_BF16 ? 2 : 4);
+}
+
 int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,
-                   int64_t newest_frame, void* out, void* hip_stream) {
+                   int64_t newest_frame, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
   int st = check_geom(g);
   if (st != FD_OK) return st;
   if (!q_new || !k_cache || !v_cache || !out) return FD_ERR_NULL;
   if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
-  if (!aligned16(q_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+  if (!ws || ws_bytes < fd_stream_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  if (!aligned16(q_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
     return FD_ERR_ALIGN;
   fd::KParams p = make_params(g, newest_frame);
-  return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, hip_stream);
+  return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream);
 }
 
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {

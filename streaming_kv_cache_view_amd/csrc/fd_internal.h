@@ -49,7 +49,7 @@ constexpr size_t kVerifyWsHeader = 256;
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
                   int slot, void* stream);
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,
-                  void* out, void* stream);
+                  void* out, void* ws, void* stream);
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb,
                   void* kc, void* vc, void* out, void* ws, void* stream);
 

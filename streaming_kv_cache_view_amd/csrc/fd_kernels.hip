@@ -44,12 +44,19 @@ constexpr double kTwoPiHi = 6.283185307179586;       // double nearest 2*pi
 constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
 constexpr double kInvTwoPi = 0.15915494309189535;
 
-// (cos a, sin a) of an fp64 angle: reduction to [-pi, pi] in fp64, then fp32 sincos.
+// (cos a, sin a) of an fp64 angle: Cody-Waite reduction by pi/2 in fp64 (exact enough for
+// |a| < 2^31), then fp32 polynomials on [-pi/4, pi/4] (Taylor/minimax, error < 1 ulp of fp32
+// there) and the quadrant's swap / signs.
 __device__ inline float2 cs_angle(double a) {
-  const double k = rint(a * kInvTwoPi);
-  const double r = fma(-k, kTwoPiHi, a) - k * kTwoPiLo;
-  float s, c;
-  sincosf(static_cast<float>(r), &s, &c);
+  const double k = rint(a * 0.63661977236758134);           // 2/pi
+  const double r = fma(-k, 1.5707963267948966, a) - k * 6.123233995736766e-17;
+  const float x = static_cast<float>(r), x2 = x * x;
+  const float sn = x * (1.f + x2 * (-1.6666667163e-1f + x2 * (8.3333337680e-3f + x2 * (-1.9841270114e-4f + x2 * 2.7557314297e-6f))));
+  const float cn = 1.f + x2 * (-0.5f + x2 * (4.1666667908e-2f + x2 * (-1.3888889225e-3f + x2 * (2.4801587642e-5f - x2 * 2.7557314297e-7f))));
+  const int q = static_cast<int>(static_cast<long long>(k) & 3);
+  float c = (q & 1) ? sn : cn, s = (q & 1) ? cn : sn;
+  if (q == 1 || q == 2) c = -c;
+  if (q >= 2) s = -s;
   return make_float2(c, s);
 }
 
@@ -137,6 +144,16 @@ struct Path<float> {
 };
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane j
+// receives, for k = 0..3, element j%4 of the four 16-bit values addressed by lane
+// 4k + j/4 of its group.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 ds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // N contiguous stored elements of T (N * sizeof(T) a multiple of 16) -> floats.
@@ -196,45 +213,191 @@ __global__ __launch_bounds__(256) void insert_kernel(const KParams p, int chunks
 }
 
 // ---------------------------------------------------------------------------------------
-// Streaming-prefill attention.
-// Workgroup = 4 waves = 128 query rows that share one kv head: HPW query heads x (32*TBW)
-// tokens of one view's new frame; wave w owns query head (w % HPW) of the group and
-// tokens [32*(w / HPW), +32).  blockIdx.x = ((view_rank*nqb + qb)*n_hsub + hsub)*Hkv + kvh,
-// so consecutive workgroups (dealt round-robin to the 8 XCDs) take different kv heads and
-// the largest views (the longest key ranges) are dispatched first.
-// Keys are walked as 64-row tiles inside segments with contiguous positions: the prefix,
-// then every slot of views 0..v.  Only the newest slot of view v needs a per-element mask.
+// Swizzle of the V^T tile rows: the 16-byte chunk index is XORed with a function of the
+// row (d), so that both the transposing writes (rows 8 apart) and the PV operand reads
+// (32 consecutive rows) spread over all LDS banks without padding.
+__device__ inline int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
+// Offset (in keys) of the group of 4 consecutive keys 4*kg inside a V^T tile row.  For
+// 16-bit operands the keys of each 16-key block are permuted so that the 8 keys a PV
+// B-operand lane holds (keys 4h..4h+3 and 8+4h..8+4h+3 of the block) are contiguous.
+template <int E>
+__device__ inline int vgroup_pos(int kg) {
+  if constexpr (E == 8) {
+    const int a = kg & 3;
+    return (kg >> 2) * 16 + (a & 1) * 8 + (a >> 1) * 4;
+  } else {
+    return 4 * kg;
+  }
+}
+
+// Write 4 keys x E d-values (one 16-byte chunk per key, in rv[0..3]) into V^T rows
+// d0 .. d0+E-1 of a tile whose rows are `rowb` bytes long.
+template <typename T, int E, int SWM>
+__device__ inline void store_vt(unsigned char* Vb, int rowb, int d0, int kg, const u32x4* rv) {
+  const int bo = vgroup_pos<E>(kg) * static_cast<int>(sizeof(T));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = d0 + e;
+    unsigned char* dst = Vb + d * rowb + ((((bo >> 4) ^ (vswz(d) & SWM)) << 4) | (bo & 15));
+    if constexpr (E == 8) {
+      const uint32_t w0 = rv[0][e >> 1], w1 = rv[1][e >> 1], w2 = rv[2][e >> 1], w3 = rv[3][e >> 1];
+      u32x2 val;
+      if (e & 1) {
+        val[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+        val[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+      } else {
+        val[0] = (w0 & 0xffffu) | (w1 << 16);
+        val[1] = (w2 & 0xffffu) | (w3 << 16);
+      }
+      *reinterpret_cast<u32x2*>(dst) = val;
+    } else {
+      const u32x4 val = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
+      *reinterpret_cast<u32x4*>(dst) = val;
+    }
+  }
+}
+
+struct TileInfo {
+  int row0, len, ktok0;
+  bool diag;
+  int64_t pos0;
+};
+
+// ---------------------------------------------------------------------------------------
+// Window rotation pass of the streaming-prefill call.  Every key of the window is rotated
+// once, in registers, at the position it holds in the current window (technical summary,
+// Methodology 1, "Positional Encoding": keys are cached pre-RoPE and rotated on the fly at
+// shifted positions), and written to the workspace as the QK^T operand format (fp16 for
+// bf16 inputs).  The attention kernel that follows then streams rotated tiles, so a key
+// is rotated once per window instead of once per workgroup that reads it.
+// Workgroup = 256 threads = one kv head x 128 window rows; thread = (row within a block of
+// RPP rows, 16-byte chunk of the first half of the row and its RoPE partner chunk).
+// When P and T are multiples of RPP no block straddles two segments, so the rotation of
+// row base + r is cs(base) (per block) times cs(r) (per thread); otherwise each element's
+// angle is reduced on its own.
+// ---------------------------------------------------------------------------------------
+__device__ inline int64_t row_pos(const KParams& p, int x) {
+  if (x < p.P) return p.pos_base + x;
+  const int rr = x - p.P;
+  const int v = rr / (p.F * p.T), s = (rr / p.T) % p.F, i = rr % p.T;
+  return slot_pos(p, v, s) + i;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
+                                                          typename Path<T>::QKT* __restrict__ krot,
+                                                          int aligned) {
+  using In = typename Path<T>::In;
+  using QK = typename Path<T>::QK;
+  using QKT = typename Path<T>::QKT;
+  constexpr int E = In::E;
+  constexpr int H2 = D / 2;
+  constexpr int CH = H2 / E;
+  constexpr int RPP = 256 / CH;
+  constexpr int ROWS = 128;
+  constexpr int NB = ROWS >= RPP ? ROWS / RPP : 1;
+  __shared__ double sfreq[H2];
+  __shared__ float2 csb[NB][H2];
+  const int tid = threadIdx.x, kvh = blockIdx.y, row_base = blockIdx.x * ROWS;
+  const int rr = tid / CH, c = tid % CH;
+  if (tid < H2) sfreq[tid] = p.inv_freq[tid];
+  for (int e = tid; e < NB * H2; e += 256) {
+    const int b = e / H2, i = e % H2, x0 = row_base + b * RPP;
+    if (x0 < p.W) csb[b][i] = cs_angle(static_cast<double>(row_pos(p, x0)) * p.inv_freq[i]);
+  }
+  __syncthreads();
+  float2 csr[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) csr[e] = cs_angle(static_cast<double>(rr) * sfreq[E * c + e]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int x = row_base + b * RPP + rr;
+    if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
+    const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+    float x1[E], x2[E];
+    In::unpack(ld16(src + E * c), x1);
+    In::unpack(ld16(src + H2 + E * c), x2);
+    const int64_t pos = aligned ? 0 : row_pos(p, x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = E * c + e;
+      const float2 cs = aligned ? cmul(csb[b][i], csr[e]) : cs_angle(static_cast<double>(pos) * sfreq[i]);
+      const float a = x1[e], bb = x2[e];
+      x1[e] = a * cs.x - bb * cs.y;
+      x2[e] = bb * cs.x + a * cs.y;
+    }
+    QKT* dst = krot + (static_cast<int64_t>(kvh) * p.W + x) * D;
+    st16(dst + E * c, QK::pack(x1));
+    st16(dst + H2 + E * c, QK::pack(x2));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Streaming-prefill attention over the rotated window.
+// Workgroup = 8 waves over 128 query rows that share one kv head: HPW query heads x
+// (32*TBW) tokens of one view's new frame.  Waves w and w+4 own the same 32 rows (query
+// head (w%4)%HPW, tokens 32*((w%4)/HPW) + [0, 32)); wave group g = w/4 takes the key
+// tiles t = g, g+2, g+4, ... of the workgroup's key sequence, so every SIMD runs two waves
+// whose MFMA and VALU work interleave; the groups merge (m, l, O) at the end.
+// blockIdx.x = ((view_rank*nqb + qb)*n_hsub + hsub)*Hkv + kvh: consecutive workgroups are
+// dealt round-robin to the 8 XCDs, so each XCD keeps one kv head's K/V in its L2, and the
+// largest views (longest key ranges) are dispatched first.
+// Key sequence: TK-row tiles inside segments of contiguous positions -- the prefix, the
+// slots of views < v, the older slots of view v, and last the newest slot of view v, the
+// only one needing a per-element (causal) mask, generated from indices; its tiles past the
+// workgroup's last query token are skipped.
+// Per group and iteration (one workgroup barrier): MFMA + online softmax on its current
+// tile | copy its next tile from registers into LDS | issue the global loads of the tile
+// after that.  K tiles (already rotated) sit in padded rows; V keeps its natural [key][d]
+// layout with 16-byte chunks XOR-swizzled by key, and for 16-bit inputs the PV operand is
+// read with the transposing LDS load, so no lane shuffles V.
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void stream_attn_kernel(const KParams p, const T* __restrict__ q,
-                                                          const T* __restrict__ kc,
-                                                          const T* __restrict__ vc,
-                                                          void* __restrict__ out) {
+__global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const T* __restrict__ q,
+                                                          const typename Path<T>::QKT* __restrict__ krot,
+                                                          const T* __restrict__ vc, void* __restrict__ out) {
+  using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
   using PV = typename Path<T>::PV;
   using QKT = typename Path<T>::QKT;
   static_assert(QK::E == PV::E, "operand chunk widths must agree");
-  constexpr int E = QK::E;
+  constexpr bool k16 = sizeof(T) == 2;
+  constexpr int E = QK::E;                       // elements per 16-byte chunk
+  constexpr int TK = (!k16 && D == 128) ? 32 : 64;   // keys per tile (LDS budget)
+  constexpr int NKB = TK / 32;                   // 32-key MFMA blocks per tile
   constexpr int H2 = D / 2;
-  constexpr int NU = D / (2 * E);        // 16-byte k-chunks per operand row
-  constexpr int KS = D + E;              // padded LDS row stride of K / Q tiles (elements)
-  constexpr int VS = kTileKeys + E;      // padded LDS row stride of the V^T tile
-  constexpr int ND = D / 32;             // 32-row blocks of O^T
-  constexpr int CPB = 32 / (2 * E);      // PV chunks per 32-key block
-  constexpr int NC = kTileKeys / (2 * E);
-  constexpr int KB = kTileKeys * KS * static_cast<int>(sizeof(QKT));
-  constexpr int QB = 128 * KS * static_cast<int>(sizeof(QKT));
-  constexpr int KVB = KB + D * VS * static_cast<int>(sizeof(T));
-  constexpr int BUF = QB > KVB ? QB : KVB;
+  constexpr int CH = H2 / E;                     // chunks per half row (Q staging)
+  constexpr int NU = CH;                         // k-chunks of the QK^T operands
+  constexpr int RPP = 256 / CH;                  // Q staging rows per pass (256 threads)
+  constexpr int QS = D + E;                      // Q staging row stride (elements, padded)
+  constexpr int KROWB = (D + E) * static_cast<int>(sizeof(QKT));   // padded K tile row bytes
+  constexpr int KCH = D * static_cast<int>(sizeof(QKT)) / 16;      // data chunks per K row
+  constexpr int VROWB = D * static_cast<int>(sizeof(T));
+  constexpr int VCH = VROWB / 16;                // 16-byte chunks per V row
+  constexpr int NKL = TK * KCH / 256;            // K chunks copied per staging thread
+  constexpr int NVL = TK * VCH / 256;            // V chunks copied per staging thread
+  constexpr int KSLOT = TK * KROWB;
+  constexpr int SLOT = KSLOT + TK * VROWB;
+  constexpr int QBYTES = 128 * QS * static_cast<int>(sizeof(QKT));
+  constexpr int MBYTES = 4 * 32 * (D + 4) * 4;   // group merge buffer
+  constexpr int B1 = 4 * SLOT > QBYTES + 16 * H2 * 8 ? 4 * SLOT : QBYTES + 16 * H2 * 8;
+  constexpr int BUFB = B1 > MBYTES ? B1 : MBYTES;
+  constexpr int ND = D / 32;
+  constexpr int CPB = 32 / (2 * E);
+  constexpr int NC = TK / (2 * E);               // PV chunks per tile
+  constexpr float kTau = 8.f;                    // log2 growth of a row max forcing a rescale
+  static_assert(NKL >= 1 && NVL >= 1 && (TK * KCH) % 256 == 0 && (TK * VCH) % 256 == 0,
+                "tile too small for the staging map");
 
-  __shared__ float2 cs_r[kTileKeys][H2];  // cos/sin(r * inv_freq_i), r < 64
-  __shared__ float2 csb[4][H2];           // cos/sin(base position * inv_freq_i)
-  __shared__ __attribute__((aligned(16))) unsigned char buf[BUF];
-  QKT* const Kl = reinterpret_cast<QKT*>(buf);           // rotated K tile [64][KS]
-  T* const Vl = reinterpret_cast<T*>(buf + KB);          // V^T tile [D][VS]
-  QKT* const Ql = reinterpret_cast<QKT*>(buf);           // rotated Q rows [128][KS] (prologue)
+  __shared__ float2 csq[4][H2];                  // cos/sin(query block base * f_i)
+  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ __attribute__((aligned(16))) unsigned char buf[BUFB];
+  float2 (*csA)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES);             // prologue only
+  float2 (*csB)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES + 8 * H2 * 8);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int grp = w >> 2, wr = w & 3, gt = tid & 255;   // group, row set, thread in group
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
@@ -242,198 +405,311 @@ __global__ __launch_bounds__(256) void stream_attn_kernel(const KParams p, const
   bid /= p.n_hsub;
   const int qb = bid % p.nqb;
   const int v = p.V - 1 - bid / p.nqb;
-  const int tok0 = qb * 32 * p.TBW;                      // first token of the workgroup
-  const int head = kvh * p.G + hsub * p.HPW + (w % p.HPW);
-  const int my_tok = tok0 + 32 * (w / p.HPW) + l32;      // this lane's query token
+  const int tok0 = qb * 32 * p.TBW;
+  const int head = kvh * p.G + hsub * p.HPW + (wr % p.HPW);
+  const int my_tok = tok0 + 32 * (wr / p.HPW) + l32;
   const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
   const float sc = p.sm_scale_log2;
 
-  // Per-offset rotation table and the query-block bases.
-  for (int e = tid; e < kTileKeys * H2; e += 256)
-    cs_r[e / H2][e % H2] = cs_angle(static_cast<double>(e / H2) * p.inv_freq[e % H2]);
-  for (int e = tid; e < 4 * H2; e += 256) {
+  // ---- tile sequence
+  const int tps = (p.T + TK - 1) / TK;
+  const int hasP = p.P > 0 ? 1 : 0;
+  const int nfull = v * p.F + p.F - 1;
+  const int tok_end = tok0 + 32 * p.TBW;
+  const int ndiag = (min(p.T, tok_end) + TK - 1) / TK;
+  const int ntiles = hasP * ((p.P + TK - 1) / TK) + nfull * tps + ndiag;
+  struct Cursor {
+    int e, k, nk, seglen, row0;
+    bool diag;
+  };
+  auto enter = [&](Cursor& c, int e) {
+    c.e = e;
+    c.k = 0;
+    if (e < hasP) {
+      c.row0 = 0;
+      c.seglen = p.P;
+      c.nk = (p.P + TK - 1) / TK;
+      c.diag = false;
+      return;
+    }
+    e -= hasP;
+    int u, s;
+    if (e < nfull) {
+      if (e < v * p.F) {
+        u = e / p.F;
+        s = e - u * p.F;
+      } else {
+        u = v;
+        const int j = e - v * p.F;
+        s = j < p.s_new ? j : j + 1;
+      }
+      c.nk = tps;
+      c.diag = false;
+    } else {
+      u = v;
+      s = p.s_new;
+      c.nk = ndiag;
+      c.diag = true;
+    }
+    c.row0 = p.P + (u * p.F + s) * p.T;
+    c.seglen = p.T;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.k == c.nk) enter(c, c.e + 1);
+  };
+
+  // ---- register staging of a tile by the 256 threads of a group (plain copies).  Rows past
+  // the tile's end are clamped to its last row: loads stay in bounds and those keys are
+  // masked (P = 0) before they can contribute.
+  u32x4 rkv[NKL + NVL];
+  auto load_tile = [&](const Cursor& c) {
+    const int row0 = c.row0 + c.k * TK, lastr = min(TK, c.seglen - c.k * TK) - 1;
+    const QKT* kb = krot + (static_cast<int64_t>(kvh) * p.W + row0) * D;
+    const T* vb = vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D;
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int qc = gt + 256 * m;
+      rkv[m] = ld16(kb + min(qc / KCH, lastr) * D + (qc % KCH) * (16 / static_cast<int>(sizeof(QKT))));
+    }
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+      const int qc = gt + 256 * m;
+      rkv[NKL + m] = ld16(vb + min(qc / VCH, lastr) * D + (qc % VCH) * (16 / static_cast<int>(sizeof(T))));
+    }
+  };
+  auto vswz = [](int key) { return (2 * (key & 7)) & (VCH - 1); };
+  auto store_tile = [&](int slot) {
+    unsigned char* Kb = buf + slot * SLOT;
+    unsigned char* Vb = Kb + KSLOT;
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const int qc = gt + 256 * m;
+      st16(Kb + (qc / KCH) * KROWB + (qc % KCH) * 16, rkv[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+      const int qc = gt + 256 * m, key = qc / VCH;
+      st16(Vb + key * VROWB + (((qc % VCH) ^ vswz(key)) << 4), rkv[NKL + m]);
+    }
+  };
+
+  // ---- prologue: query rotation (through LDS into operand registers), first tiles in flight
+  Cursor cn;   // the group's tile whose loads are in flight
+  enter(cn, 0);
+  if (grp == 1) advance(cn);
+  const int ngt = (ntiles - grp + 1) / 2;        // tiles of this group
+  if (ngt > 0) load_tile(cn);
+  for (int e = tid; e < 16 * H2; e += 512) {
+    const int tb = e / (8 * H2), a = (e / H2) % 8, i = e % H2;
+    const float2 v2 = cs_angle((tb == 0 ? 8.0 * a : static_cast<double>(a)) * p.inv_freq[i]);
+    if (tb == 0) csA[a][i] = v2;
+    else csB[a][i] = v2;
+  }
+  for (int e = tid; e < 4 * H2; e += 512) {
     const int ww = e / H2, i = e % H2;
-    csb[ww][i] = cs_angle(static_cast<double>(qpos0 + tok0 + 32 * (ww / p.HPW)) * p.inv_freq[i]);
+    csq[ww][i] = cs_angle(static_cast<double>(qpos0 + tok0 + 32 * (ww / p.HPW)) * p.inv_freq[i]);
   }
   __syncthreads();
-
-  // Stage the 128 query rows (rotated at their positions) in LDS.
   {
-    constexpr int PQ = H2 / 2;
-    const int row = tid >> 1, part = tid & 1;
-    const int ww = row >> 5, r = row & 31;
-    const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-    const int tk = tok0 + 32 * (ww / p.HPW) + r;
-    float x1[PQ], x2[PQ];
-    if (tk < p.T) {
-      const T* src = q + (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
-      load_f<T, PQ>(src + part * PQ, x1);
-      load_f<T, PQ>(src + H2 + part * PQ, x2);
-    } else {
+    QKT* Ql = reinterpret_cast<QKT*>(buf);
+    const int kc_ = gt % CH, kr0 = gt / CH;
 #pragma unroll
-      for (int j = 0; j < PQ; ++j) x1[j] = x2[j] = 0.f;
+    for (int ps = 0; ps < (64 + RPP - 1) / RPP; ++ps) {
+      const int rq = kr0 + ps * RPP;
+      if (RPP > 64 && rq >= 64) continue;
+      const int row = 64 * grp + rq;
+      const int ww = row >> 5, r = row & 31;
+      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+      const int tk = tok0 + 32 * (ww / p.HPW) + r;
+      float x1[E], x2[E];
+      if (tk < p.T) {
+        const T* src = q + (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
+        In::unpack(ld16(src + E * kc_), x1);
+        In::unpack(ld16(src + H2 + E * kc_), x2);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x1[e] = x2[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = E * kc_ + e;
+        const float2 cs = cmul(csq[ww][i], cmul(csA[r >> 3][i], csB[r & 7][i]));
+        const float a = x1[e], b = x2[e];
+        x1[e] = a * cs.x - b * cs.y;
+        x2[e] = b * cs.x + a * cs.y;
+      }
+      st16(Ql + row * QS + E * kc_, QK::pack(x1));
+      st16(Ql + row * QS + H2 + E * kc_, QK::pack(x2));
     }
-    rope_pairs<PQ>(x1, x2, csb[ww], cs_r[r], part * PQ);
-    store_ops<QK, QKT, PQ>(Ql + row * KS + part * PQ, x1);
-    store_ops<QK, QKT, PQ>(Ql + row * KS + H2 + part * PQ, x2);
   }
   __syncthreads();
   u32x4 qf[NU];
+  {
+    const QKT* Ql = reinterpret_cast<const QKT*>(buf);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) qf[u] = ld16(Ql + (32 * w + l32) * KS + 2 * E * u + E * h);
+    for (int u = 0; u < NU; ++u) qf[u] = ld16(Ql + (32 * wr + l32) * QS + 2 * E * u + E * h);
+  }
   __syncthreads();
+
+  // lane constants of the operand reads
+  const int krd = l32 * KROWB + h * 16;                  // QK A operand: row l32, chunk 2u+h
+  const int key0 = 4 * h + ((lane & 15) >> 2);           // PV A operand (16-bit): key 16c+key0 (+8)
+  int voff[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    if constexpr (k16) {
+      const int cb2 = (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+      voff[d] = key0 * VROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+    } else {
+      voff[d] = 32 * d + l32;
+    }
+  }
 
   f32x16 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;   // accumulators refer to m_ref: P = exp2(sc*s - m_ref)
 
-  // One 64-key tile: physical rows [row0, row0+len) of kv head kvh at positions pos0 + r.
-  auto tile = [&](int row0, int len, int64_t pos0, bool diag, int ktok0) {
-    if (w == 0) {
-      for (int i = lane; i < H2; i += 64) csb[0][i] = cs_angle(static_cast<double>(pos0) * p.inv_freq[i]);
+  auto compute = [&](int slot, const Cursor& c) {
+    const unsigned char* Kb = buf + slot * SLOT;
+    const unsigned char* Vb = Kb + KSLOT;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      u32x4 ka[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) ka[u] = ld16(Kb + krd + kb * 32 * KROWB + u * 32);
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) s[kb] = QK::mma(ka[u], qf[u], s[kb]);
     }
-    __syncthreads();
-    {  // K: HBM -> registers, RoPE, -> LDS
-      constexpr int PK = H2 / 4;
-      const int r = tid >> 2, qq = tid & 3;
-      float x1[PK], x2[PK];
-      if (r < len) {
-        const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + row0 + r) * D;
-        load_f<T, PK>(src + qq * PK, x1);
-        load_f<T, PK>(src + H2 + qq * PK, x2);
-      } else {
+    const int ktok0 = c.k * TK, len = min(TK, c.seglen - ktok0);
+    if (c.diag || len < TK) {   // generated mask: tile end, causal newest slot
+      // key kk = 32kb + 8(i/4) + 4h + i%4 is visible iff kk < lim
+      const int lim = (c.diag ? min(len, my_tok - ktok0 + 1) : len) - 4 * h;
 #pragma unroll
-        for (int j = 0; j < PK; ++j) x1[j] = x2[j] = 0.f;
-      }
-      rope_pairs<PK>(x1, x2, csb[0], cs_r[r], qq * PK);
-      store_ops<QK, QKT, PK>(Kl + r * KS + qq * PK, x1);
-      store_ops<QK, QKT, PK>(Kl + r * KS + H2 + qq * PK, x2);
-    }
-    {  // V: HBM -> registers -> LDS transposed (V^T[d][key], keys permuted for bf16)
-      constexpr int DV = D / 16;
-      const int dg = tid & 15, kg = tid >> 4;
-      T vals[4][DV];
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 4 * kg + j;
-        if (key < len) {
-          const T* src = vc + (static_cast<int64_t>(kvh) * p.S_cap + row0 + key) * D + dg * DV;
-          if constexpr (DV * sizeof(T) % 16 == 0) {
-#pragma unroll
-            for (int c = 0; c < DV * static_cast<int>(sizeof(T)) / 16; ++c)
-              *reinterpret_cast<u32x4*>(&vals[j][c * 16 / sizeof(T)]) = ld16(src + c * 16 / sizeof(T));
-          } else {
-            *reinterpret_cast<u32x2*>(&vals[j][0]) = *reinterpret_cast<const u32x2*>(src);
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d < DV; ++d) vals[j][d] = static_cast<T>(0.f);
-        }
-      }
-      int pbase;
-      if constexpr (E == 8) {
-        const int a = kg & 3;
-        pbase = (kg >> 2) * 16 + (a & 1) * 8 + (a >> 1) * 4;
-      } else {
-        pbase = 4 * kg;
-      }
-#pragma unroll
-      for (int d = 0; d < DV; ++d) {
-        T* dst = Vl + (dg * DV + d) * VS + pbase;
-        if constexpr (E == 8) {
-          bf16 t4[4] = {vals[0][d], vals[1][d], vals[2][d], vals[3][d]};
-          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(t4);
-        } else {
-          f32x4 t4 = {vals[0][d], vals[1][d], vals[2][d], vals[3][d]};
-          *reinterpret_cast<f32x4*>(dst) = t4;
-        }
+        for (int i = 0; i < 16; ++i) s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) < lim) ? s[kb][i] : -INFINITY;
       }
     }
-    __syncthreads();
-
-    // S^T = K Q^T for the two 32-key blocks.
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) s[kb] = QK::mma(ld16(Kl + (32 * kb + l32) * KS + 2 * E * u + E * h), qf[u], s[kb]);
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
     }
-    // Mask (generated), online softmax in base 2.
-    float mloc = -INFINITY;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+    if (__ballot(mx > m_ref + kTau) != 0) {   // rare: a row maximum grew by more than 2^kTau
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool ok = kk < len && (!diag || ktok0 + kk <= my_tok);
-        const float x = ok ? s[kb][i] * sc : -INFINITY;
-        s[kb][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
+      for (int d = 0; d < ND; ++d) o[d] *= alpha;
+      m_ref = m_new;
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+    const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(s[kb][i] - mu);
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][i], sc, -mu));
         s[kb][i] = pr;
         lsum += pr;
       }
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    l_run += lsum;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int kb = c / CPB;
+    for (int cc = 0; cc < NC; ++cc) {
+      const int kb = cc / CPB;
       float pv[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) pv[e] = s[kb][E * (c % CPB) + e];
+      for (int e = 0; e < E; ++e) pv[e] = s[kb][E * (cc % CPB) + e];
       const u32x4 bop = PV::pack(pv);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) o[d] = PV::mma(ld16(Vl + (32 * d + l32) * VS + 2 * E * c + E * h), bop, o[d]);
+      for (int d = 0; d < ND; ++d) {
+        u32x4 a;
+        if constexpr (k16) {
+          // A operand = V^T[32d + l%32][keys 16cc + 4h + {0..3}, 16cc + 8 + 4h + {0..3}]
+          const u32x2 lo = ds_read_tr16(Vb + voff[d] + 16 * cc * VROWB);
+          const u32x2 hi = ds_read_tr16(Vb + voff[d] + (16 * cc + 8) * VROWB);
+          a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          // fp32: element e of chunk cc holds key 8cc + 4h + e at column 32d + l%32
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 8 * cc + 4 * h + e, col = voff[d];
+            a[e] = *reinterpret_cast<const uint32_t*>(Vb + key * VROWB + ((((col >> 2) ^ vswz(key)) << 4) | ((col & 3) << 2)));
+          }
+        }
+        o[d] = PV::mma(a, bop, o[d]);
+      }
     }
   };
 
-  for (int st = 0; st < p.P; st += kTileKeys)
-    tile(st, min(kTileKeys, p.P - st), p.pos_base + st, false, 0);
-  const int tok_end = tok0 + 32 * p.TBW;  // keys of the newest slot beyond this are masked for all rows
-  for (int u = 0; u <= v; ++u) {
-    for (int s = 0; s < p.F; ++s) {
-      const int seg = p.P + (u * p.F + s) * p.T;
-      const int64_t segpos = slot_pos(p, u, s);
-      const bool diag = (u == v) && (s == p.s_new);
-      const int tmax = diag ? min(p.T, tok_end) : p.T;
-      for (int st = 0; st < tmax; st += kTileKeys)
-        tile(seg + st, min(kTileKeys, p.T - st), segpos + st, diag, st);
+  // ---- main pipeline (per group: compute tile j, stage tile j+1, load tile j+2)
+  auto slot_of = [&](int j) { return 2 * (j & 1) + grp; };
+  Cursor cc = cn;
+  if (ngt > 0) store_tile(slot_of(0));
+  if (ngt > 1) {
+    advance(cn);
+    advance(cn);
+    load_tile(cn);
+  }
+  __syncthreads();
+  const int niter = (ntiles + 1) / 2;
+  for (int j = 0; j < niter; ++j) {
+    if (j < ngt) compute(slot_of(j), cc);
+    if (j + 1 < ngt) store_tile(slot_of(j + 1));
+    if (j + 2 < ngt) {
+      advance(cn);
+      advance(cn);
+      load_tile(cn);
     }
+    advance(cc);
+    advance(cc);
+    __syncthreads();
   }
 
-  // Epilogue: O / l, this lane's query row.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  if (my_tok < p.T) {
-    const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+  // ---- merge the two groups (same rows, disjoint key tiles), then O / l
+  const float l_half = l_run + __shfl_xor(l_run, 32);
+  float* mb = reinterpret_cast<float*>(buf) + wr * 32 * (D + 4);
+  if (grp == 1) {
+    if (lane < 32) {
+      red_m[wr][l32] = m_ref;
+      red_l[wr][l32] = l_half;
+    }
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const int d0 = 32 * d + 8 * ig + 4 * h;
-        const f32x4 r = {o[d][4 * ig] * inv, o[d][4 * ig + 1] * inv, o[d][4 * ig + 2] * inv, o[d][4 * ig + 3] * inv};
-        if (p.out_bf16) {
-          bf16 b4[4] = {static_cast<bf16>(r[0]), static_cast<bf16>(r[1]), static_cast<bf16>(r[2]), static_cast<bf16>(r[3])};
-          *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + obase + d0) = *reinterpret_cast<const u32x2*>(b4);
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + d0) = r;
+      for (int ig = 0; ig < 4; ++ig)
+        *reinterpret_cast<f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h) =
+            f32x4{o[d][4 * ig], o[d][4 * ig + 1], o[d][4 * ig + 2], o[d][4 * ig + 3]};
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = red_m[wr][l32], l1 = red_l[wr][l32];
+    const float M = fmaxf(m_ref, m1);
+    const float a0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    const float inv = 1.f / (a0 * l_half + a1 * l1);
+    if (my_tok < p.T) {
+      const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int d0 = 32 * d + 8 * ig + 4 * h;
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
+          const f32x4 r = {(o[d][4 * ig] * a0 + ov[0] * a1) * inv, (o[d][4 * ig + 1] * a0 + ov[1] * a1) * inv,
+                           (o[d][4 * ig + 2] * a0 + ov[2] * a1) * inv, (o[d][4 * ig + 3] * a0 + ov[3] * a1) * inv};
+          if (p.out_bf16) {
+            bf16 b4[4] = {static_cast<bf16>(r[0]), static_cast<bf16>(r[1]), static_cast<bf16>(r[2]), static_cast<bf16>(r[3])};
+            *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + obase + d0) = *reinterpret_cast<const u32x2*>(b4);
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + d0) = r;
+          }
         }
       }
     }
@@ -445,8 +721,11 @@ __global__ __launch_bounds__(256) void stream_attn_kernel(const KParams p, const
 // 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W), reasoning rows
 // [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk and copied into
 // the cache here).  They are cut into 32-key blocks inside segments of contiguous
-// positions; wave w of split s takes block (s*4 + w).  The four waves merge in LDS and the
-// workgroup writes one (m, l, O) partial per (kv head, split).
+// positions; wave w of split s takes block (s*4 + w): its K rows are loaded straight into
+// registers (lane l32 holds key l32, both halves of every RoPE pair) and rotated there, its
+// V rows go through a per-wave swizzled V^T tile in LDS.  All global loads are issued
+// before the rotation tables are built.  The four waves merge in LDS and the workgroup
+// writes one (m, l, O) partial per (kv head, split).
 // ---------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, const T* __restrict__ qb,
@@ -461,19 +740,23 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
   constexpr int NU = D / (2 * E);
   constexpr int ND = D / 32;
   constexpr int CPB = 32 / (2 * E);
-  constexpr int VS = 32 + E;
+  constexpr int VROW = 32 * static_cast<int>(sizeof(T));   // V^T row: 32 keys
+  constexpr int SWM = VROW / 16 >= 8 ? 7 : VROW / 16 - 1;  // chunk swizzle mask
+  constexpr int DCH = D / E;
+  constexpr int NVI = (8 * DCH + 63) / 64;
+  constexpr int RS = H2 + 2;                               // padded offset-table row (float2)
   constexpr int OS = D + 4;
-  constexpr int VST_BYTES = 4 * D * VS * static_cast<int>(sizeof(T));
-  constexpr int OB_BYTES = 2 * 32 * OS * 4;
-  constexpr int UB = VST_BYTES > OB_BYTES ? VST_BYTES : OB_BYTES;
+  constexpr int VB = 4 * D * VROW;
+  constexpr int OB = 2 * 32 * OS * 4;
+  constexpr int UB = VB > OB ? VB : OB;
 
-  __shared__ float2 cs_r[32][H2];
-  __shared__ float2 csq[H2];
-  __shared__ float2 csb[4][H2];
+  __shared__ float2 csA[4][H2];     // cos/sin(8a f_i)
+  __shared__ float2 csB[8][H2];     // cos/sin(b f_i)
+  __shared__ __attribute__((aligned(16))) float2 csr[32][RS];  // cos/sin(r f_i), r < 32
+  __shared__ float2 csq[H2];        // cos/sin(first block position * f_i)
+  __shared__ float2 csb[4][H2];     // cos/sin(key block base * f_i), one per wave
   __shared__ float red_m[4][32], red_l[4][32];
   __shared__ __attribute__((aligned(16))) unsigned char ubuf[UB];
-  T* const vst = reinterpret_cast<T*>(ubuf) ;
-  float* const obuf = reinterpret_cast<float*>(ubuf);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int kvh = blockIdx.x % p.Hkv, split = blockIdx.x / p.Hkv;
@@ -483,193 +766,160 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
   const int tailbase = p.W + p.n_tail;  // cache row of block token 0
   const float sc = p.sm_scale_log2;
 
-  for (int e = tid; e < 32 * H2; e += 256)
-    cs_r[e / H2][e % H2] = cs_angle(static_cast<double>(e / H2) * p.inv_freq[e % H2]);
-  if (tid < H2) csq[tid] = cs_angle(static_cast<double>(p.pos_base + tailbase) * p.inv_freq[tid]);
-  __syncthreads();
+  // ---- this wave's key block
+  const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
+  const int j = split * kVerifyWaves + w;
+  int x0 = 0, len = 0;
+  int64_t pos0 = 0;
+  if (j < p.nblk) {
+    if (j < nbp) {
+      x0 = 32 * j;
+      len = min(32, p.P - x0);
+      pos0 = p.pos_base + x0;
+    } else if (j - nbp < nslot * nbs) {
+      const int jj = j - nbp, vs = jj / nbs, st = 32 * (jj % nbs);
+      x0 = p.P + vs * p.T + st;
+      len = min(32, p.T - st);
+      pos0 = slot_pos(p, vs / p.F, vs % p.F) + st;
+    } else {
+      const int st = 32 * (j - nbp - nslot * nbs);
+      x0 = p.W + st;
+      len = min(32, p.n_tail + p.B - st);
+      pos0 = p.pos_base + p.W + st;
+    }
+  }
 
-  // Query fragments, rotated in registers: lane half h holds elements [2E*u + E*h, +E) of
-  // chunk u; chunks u and u + NU/2 hold the two halves of the same RoPE pairs.
-  u32x4 qf[NU];
+  // ---- issue every global load first
+  u32x4 qraw[NU], kraw[NU];
+  const int xk = x0 + l32;
+  const bool kvalid = l32 < len;
+  const bool k_from_blk = xk >= tailbase;
   {
-    float f[NU][E];
+    const T* qsrc = qb + (static_cast<int64_t>(bq) * p.Hq + head) * D;
+    const T* ksrc = k_from_blk ? kb + (static_cast<int64_t>(xk - tailbase) * p.Hkv + kvh) * D
+                               : kc + (static_cast<int64_t>(kvh) * p.S_cap + xk) * D;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      if (qvalid) In::unpack(ld16(qb + (static_cast<int64_t>(bq) * p.Hq + head) * D + 2 * E * u + E * h), f[u]);
-      else {
+      qraw[u] = qvalid ? ld16(qsrc + 2 * E * u + E * h) : u32x4{};
+      kraw[u] = kvalid ? ld16(ksrc + 2 * E * u + E * h) : u32x4{};
+    }
+  }
+  u32x4 rv[NVI][4];
 #pragma unroll
-        for (int e = 0; e < E; ++e) f[u][e] = 0.f;
+  for (int jv = 0; jv < NVI; ++jv) {
+    const int it = lane + 64 * jv;
+    const int dc = it % DCH, kg = it / DCH;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key = 4 * kg + jj, x = x0 + key;
+      rv[jv][jj] = u32x4{};
+      if (it < 8 * DCH && key < len) {
+        const T* src = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
+                                     : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+        rv[jv][jj] = ld16(src + E * dc);
+        if (x >= tailbase) st16(vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D + E * dc, rv[jv][jj]);
       }
+    }
+  }
+  if (kvalid && k_from_blk) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) st16(kc + (static_cast<int64_t>(kvh) * p.S_cap + xk) * D + 2 * E * u + E * h, kraw[u]);
+  }
+
+  // ---- rotation tables (overlap the loads in flight)
+  for (int e = tid; e < 12 * H2; e += 256) {
+    const int a = e / H2, i = e % H2;
+    if (a < 4) csA[a][i] = cs_angle(8.0 * a * p.inv_freq[i]);
+    else csB[a - 4][i] = cs_angle(static_cast<double>(a - 4) * p.inv_freq[i]);
+  }
+  if (tid < H2) csq[tid] = cs_angle(static_cast<double>(p.pos_base + tailbase) * p.inv_freq[tid]);
+  if (lane < H2) csb[w][lane] = cs_angle(static_cast<double>(pos0) * p.inv_freq[lane]);
+  __syncthreads();
+  for (int e = tid; e < 32 * H2; e += 256) {
+    const int r = e / H2, i = e % H2;
+    csr[r][i] = cmul(csA[r >> 3][i], csB[r & 7][i]);
+  }
+  __syncthreads();
+
+  // ---- rotate Q and K in registers (chunks u and u + NU/2 hold the two halves of a pair)
+  u32x4 qf[NU], kf[NU];
+  {
+    float fq[NU][E], fk[NU][E];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      In::unpack(qraw[u], fq[u]);
+      In::unpack(kraw[u], fk[u]);
     }
 #pragma unroll
     for (int u = 0; u < NU / 2; ++u) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int i = 2 * E * u + E * h + e;
-        const float2 cs = cmul(csq[i], cs_r[bq][i]);
-        const float a = f[u][e], b = f[u + NU / 2][e];
-        f[u][e] = a * cs.x - b * cs.y;
-        f[u + NU / 2][e] = b * cs.x + a * cs.y;
+        const float2 cq = cmul(csq[i], csr[bq][i]);
+        const float2 ck = cmul(csb[w][i], csr[l32][i]);
+        float a = fq[u][e], b = fq[u + NU / 2][e];
+        fq[u][e] = a * cq.x - b * cq.y;
+        fq[u + NU / 2][e] = b * cq.x + a * cq.y;
+        a = fk[u][e];
+        b = fk[u + NU / 2][e];
+        fk[u][e] = a * ck.x - b * ck.y;
+        fk[u + NU / 2][e] = b * ck.x + a * ck.y;
       }
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) qf[u] = QK::pack(f[u]);
+    for (int u = 0; u < NU; ++u) {
+      qf[u] = QK::pack(fq[u]);
+      kf[u] = QK::pack(fk[u]);
+    }
+  }
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[u], s);
+
+  float m_run = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+    const bool ok = (kk < len) & ((x0 + kk - tailbase) <= bq);
+    s[i] = ok ? s[i] * sc : -INFINITY;
+    m_run = fmaxf(m_run, s[i]);
+  }
+  m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
+  const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+  float l_run = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pr = __builtin_amdgcn_exp2f(s[i] - mu);
+    s[i] = pr;
+    l_run += pr;
   }
 
+  // ---- V^T block of this wave in LDS, then O^T = V^T P^T
+  unsigned char* Vw = ubuf + w * D * VROW;
+#pragma unroll
+  for (int jv = 0; jv < NVI; ++jv) {
+    const int it = lane + 64 * jv;
+    if (it < 8 * DCH) store_vt<T, E, SWM>(Vw, VROW, E * (it % DCH), it / DCH, rv[jv]);
+  }
+  __syncthreads();
   f32x16 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
-
-  for (int k = 0; k < kVerifyBlocksPerWave; ++k) {
-    const int j = (split * kVerifyWaves + w) * kVerifyBlocksPerWave + k;
-    int x0 = 0, len = 0;
-    int64_t pos0 = 0;
-    if (j < p.nblk) {
-      if (j < nbp) {
-        x0 = 32 * j;
-        len = min(32, p.P - x0);
-        pos0 = p.pos_base + x0;
-      } else if (j - nbp < nslot * nbs) {
-        const int jj = j - nbp, vs = jj / nbs, st = 32 * (jj % nbs);
-        x0 = p.P + vs * p.T + st;
-        len = min(32, p.T - st);
-        pos0 = slot_pos(p, vs / p.F, vs % p.F) + st;
-      } else {
-        const int st = 32 * (j - nbp - nslot * nbs);
-        x0 = p.W + st;
-        len = min(32, p.n_tail + p.B - st);
-        pos0 = p.pos_base + p.W + st;
-      }
+#pragma unroll
+  for (int c = 0; c < CPB; ++c) {
+    float pv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) pv[e] = s[E * c + e];
+    const u32x4 bop = PV::pack(pv);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int dr = 32 * d + l32;
+      o[d] = PV::mma(ld16(Vw + dr * VROW + (((2 * c + h) ^ (vswz(dr) & SWM)) << 4)), bop, o[d]);
     }
-    if (lane < H2) csb[w][lane] = cs_angle(static_cast<double>(pos0) * p.inv_freq[lane]);
-    __syncthreads();
-
-    // K rows: lane l32 holds key x0 + l32; rotate in registers.
-    u32x4 kf[NU];
-    {
-      const int x = x0 + l32;
-      const bool kv = l32 < len;
-      const bool from_blk = x >= tailbase;
-      const T* src = from_blk ? kb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                              : kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-      float f[NU][E];
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (kv) {
-          const u32x4 raw = ld16(src + 2 * E * u + E * h);
-          if (from_blk) st16(kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 2 * E * u + E * h, raw);
-          In::unpack(raw, f[u]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) f[u][e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NU / 2; ++u) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = 2 * E * u + E * h + e;
-          const float2 cs = cmul(csb[w][i], cs_r[l32][i]);
-          const float a = f[u][e], b = f[u + NU / 2][e];
-          f[u][e] = a * cs.x - b * cs.y;
-          f[u + NU / 2][e] = b * cs.x + a * cs.y;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < NU; ++u) kf[u] = QK::pack(f[u]);
-    }
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[u], s);
-
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
-      const bool ok = kk < len && (x0 + kk - tailbase) <= bq;
-      const float x = ok ? s[i] * sc : -INFINITY;
-      s[i] = x;
-      mloc = fmaxf(mloc, x);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pr = __builtin_amdgcn_exp2f(s[i] - mu);
-      s[i] = pr;
-      lsum += pr;
-    }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
-
-    // V rows -> this wave's LDS V^T block (keys permuted for bf16), copying block rows.
-    {
-      constexpr int DV = D / 8;
-      const int kg = lane >> 3, dg = lane & 7;
-      T vals[4][DV];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int key = 4 * kg + jj;
-        const int x = x0 + key;
-        if (key < len) {
-          const bool from_blk = x >= tailbase;
-          const T* src = (from_blk ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                                   : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D) + dg * DV;
-#pragma unroll
-          for (int c = 0; c < DV * static_cast<int>(sizeof(T)) / 16; ++c) {
-            const u32x4 raw = ld16(src + c * 16 / sizeof(T));
-            *reinterpret_cast<u32x4*>(&vals[jj][c * 16 / sizeof(T)]) = raw;
-            if (from_blk) st16(vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D + dg * DV + c * 16 / sizeof(T), raw);
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d < DV; ++d) vals[jj][d] = static_cast<T>(0.f);
-        }
-      }
-      int pbase;
-      if constexpr (E == 8) {
-        const int a = kg & 3;
-        pbase = (kg >> 2) * 16 + (a & 1) * 8 + (a >> 1) * 4;
-      } else {
-        pbase = 4 * kg;
-      }
-      T* vw = vst + w * D * VS;
-#pragma unroll
-      for (int d = 0; d < DV; ++d) {
-        T* dst = vw + (dg * DV + d) * VS + pbase;
-        if constexpr (E == 8) {
-          bf16 t4[4] = {vals[0][d], vals[1][d], vals[2][d], vals[3][d]};
-          *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(t4);
-        } else {
-          f32x4 t4 = {vals[0][d], vals[1][d], vals[2][d], vals[3][d]};
-          *reinterpret_cast<f32x4*>(dst) = t4;
-        }
-      }
-    }
-    __syncthreads();
-    {
-      const T* vw = vst + w * D * VS;
-#pragma unroll
-      for (int c = 0; c < CPB; ++c) {
-        float pv[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) pv[e] = s[E * c + e];
-        const u32x4 bop = PV::pack(pv);
-#pragma unroll
-        for (int d = 0; d < ND; ++d) o[d] = PV::mma(ld16(vw + (32 * d + l32) * VS + 2 * E * c + E * h), bop, o[d]);
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();   // V^T tiles are dead: the space is reused for the merge
 
-  // Merge the four waves (rows are shared, key ranges differ).
+  // ---- merge the four waves (same rows, different keys)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (lane < 32) {
     red_m[w][l32] = m_run;
@@ -684,6 +934,7 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
   for (int ww = 0; ww < 4; ++ww)
     if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
   const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  float* obuf = reinterpret_cast<float*>(ubuf);
   float* ob = obuf + (w & 1) * 32 * OS;
   if (w < 2) {
 #pragma unroll
@@ -720,9 +971,11 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 }
 
 // Verify merge: fixed-order log-sum-exp combination of the n_split partials of each kv head.
-// Grid = Hkv * 4 workgroups; thread = (row in an 8-row group, 4 consecutive d).
+// Grid = Hkv * 4 workgroups; thread = (row in an 8-row group, 4 consecutive d).  Partials are
+// read eight at a time so that their loads are in flight together.
 __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
+  constexpr int BATCH = 8;
   const int kvh = blockIdx.x >> 2, rg = blockIdx.x & 3;
   const int r = rg * 8 + (threadIdx.x >> 5);
   const int d0 = 4 * (threadIdx.x & 31);
@@ -733,21 +986,34 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
   const float* base = part + static_cast<size_t>(kvh) * p.n_split * pw;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = f32x4{};
-  for (int s = 0; s < p.n_split; ++s) {
-    const float* ps = base + s * pw;
-    const float m = ps[32 * p.D + r];
-    if (m == -INFINITY) continue;
-    const float l = ps[32 * p.D + 32 + r];
-    const f32x4 ov = *reinterpret_cast<const f32x4*>(ps + r * p.D + d0);
-    if (m > M) {
-      const float c = __builtin_amdgcn_exp2f(M - m);
-      acc *= c;
-      L *= c;
-      M = m;
+  for (int s0 = 0; s0 < p.n_split; s0 += BATCH) {
+    float mm[BATCH], ll[BATCH];
+    f32x4 ov[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      mm[j] = -INFINITY;
+      ll[j] = 0.f;
+      ov[j] = f32x4{};
+      if (s0 + j < p.n_split) {
+        const float* ps = base + (s0 + j) * pw;
+        mm[j] = ps[32 * p.D + r];
+        ll[j] = ps[32 * p.D + 32 + r];
+        ov[j] = *reinterpret_cast<const f32x4*>(ps + r * p.D + d0);
+      }
     }
-    const float wgt = __builtin_amdgcn_exp2f(m - M);
-    acc += wgt * ov;
-    L += wgt * l;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (mm[j] == -INFINITY) continue;
+      if (mm[j] > M) {
+        const float c = __builtin_amdgcn_exp2f(M - mm[j]);
+        acc *= c;
+        L *= c;
+        M = mm[j];
+      }
+      const float wgt = __builtin_amdgcn_exp2f(mm[j] - M);
+      acc += wgt * ov[j];
+      L += wgt * ll[j];
+    }
   }
   const f32x4 res = acc * (1.f / L);
   const int64_t oidx = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + hh) * p.D + d0;
@@ -760,11 +1026,18 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
 }
 
 template <typename T, int D>
-int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out,
+int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                     hipStream_t st) {
+  using QKT = typename Path<T>::QKT;
+  constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
+  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
+  QKT* krot = static_cast<QKT*>(ws);
+  hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3((p.W + 127) / 128, p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const T*>(kc), krot, aligned);
+  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
-  hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(256), 0, st, p,
-                     static_cast<const T*>(q), static_cast<const T*>(kc), static_cast<const T*>(vc), out);
+  hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
+                     static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 
@@ -795,14 +1068,14 @@ int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* k
 }
 
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc, void* out,
-                  void* stream) {
+                  void* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_bf16) {
-    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, st)
-                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, st);
+    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, ws, st)
+                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, ws, st);
   }
-  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, st)
-                    : launch_stream_t<float, 64>(p, q, kc, vc, out, st);
+  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st)
+                    : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st);
 }
 
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb, void* kc,

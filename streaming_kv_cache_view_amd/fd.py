@@ -50,7 +50,8 @@ def lib() -> ctypes.CDLL:
         L.fd_key_position.argtypes, L.fd_key_position.restype = [G, i64, i64, ctypes.POINTER(i64)], ctypes.c_int
         L.fd_kv_insert_frame.argtypes = [G, vp, vp, vp, vp, i64, vp]
         L.fd_kv_insert_frame.restype = ctypes.c_int
-        L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp]
+        L.fd_stream_workspace_bytes.argtypes, L.fd_stream_workspace_bytes.restype = [G], sz
+        L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn.restype = ctypes.c_int
         L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
         L.fd_verify_attn.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
@@ -60,8 +61,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_stream_attn",
-           "fd_verify_workspace_bytes", "fd_verify_attn", "fd_status_str")
+EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_stream_workspace_bytes",
+           "fd_stream_attn", "fd_verify_workspace_bytes", "fd_verify_attn", "fd_status_str")
 
 
 def make_geom(g, out_dtype: str = "f32") -> FdGeom:
@@ -112,11 +113,21 @@ def kv_insert_frame(g, k_cache, v_cache, k_new, v_new, frame_idx: int, stream=No
         int(frame_idx), _stream(stream)))
 
 
-def stream_attn(g, q_new, k_cache, v_cache, newest_frame: int, out, out_dtype: str = "f32", stream=None):
-    """out [V*T][Hq][D] = streaming-prefill attention of the new frame's queries q_new [V*T][Hq][D]."""
+def stream_workspace_bytes(g) -> int:
+    return lib().fd_stream_workspace_bytes(ctypes.byref(make_geom(g)))
+
+
+def stream_attn(g, q_new, k_cache, v_cache, newest_frame: int, out, ws, ws_bytes: int | None = None,
+                out_dtype: str = "f32", stream=None):
+    """out [V*T][Hq][D] = streaming-prefill attention of the new frame's queries q_new [V*T][Hq][D].
+
+    ws: device workspace of at least stream_workspace_bytes(g) bytes (rotated window keys).
+    """
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
     _check("fd_stream_attn", lib().fd_stream_attn(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_new), _ptr(k_cache), _ptr(v_cache),
-        int(newest_frame), _ptr(out), _stream(stream)))
+        int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def verify_workspace_bytes(g, blk_len: int) -> int:

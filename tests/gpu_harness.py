@@ -59,7 +59,8 @@ def stream_out(w, layer, kc, vc, t, out_dtype="f32", q=None):
     g = w.geom
     out = torch.empty((g.n_new, g.n_q_heads, g.head_dim),
                       dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=DEV)
-    fd.stream_attn(g, q if q is not None else q_new(w, layer, t), kc, vc, t, out, out_dtype=out_dtype)
+    ws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=DEV)
+    fd.stream_attn(g, q if q is not None else q_new(w, layer, t), kc, vc, t, out, ws, out_dtype=out_dtype)
     return out
 
 

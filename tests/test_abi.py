@@ -95,7 +95,8 @@ def test_geometry_errors(kw, code):
     L = fd.lib()
     g = _g(**kw)
     assert L.fd_cache_rows(ctypes.byref(g)) == -1
-    assert L.fd_stream_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 5, FAKE, None) == code
+    assert L.fd_stream_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 5, FAKE, FAKE, 1 << 40, None) == code
+    assert L.fd_stream_workspace_bytes(ctypes.byref(g)) == 0
     assert L.fd_kv_insert_frame(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, 0, None) == code
     assert L.fd_verify_workspace_bytes(ctypes.byref(g), 8) == 0
 
@@ -104,11 +105,16 @@ def test_call_errors():
     L = fd.lib()
     g = _g()
     gp = ctypes.byref(g)
-    assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, None) == -1
-    assert L.fd_stream_attn(gp, None, FAKE, FAKE, 5, FAKE, None) == -1
-    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, None, None) == -1
-    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 2, FAKE, None) == -4        # window not full
-    assert L.fd_stream_attn(gp, MISALIGNED, FAKE, FAKE, 5, FAKE, None) == -5
+    sws = L.fd_stream_workspace_bytes(gp)
+    assert sws == g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
+    assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
+    assert L.fd_stream_attn(gp, None, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
+    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, None, FAKE, sws, None) == -1
+    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 2, FAKE, FAKE, sws, None) == -4     # window not full
+    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, None, sws, None) == -7     # no workspace
+    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws - 1, None) == -7
+    assert L.fd_stream_attn(gp, MISALIGNED, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -5
+    assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, MISALIGNED, sws, None) == -5
     assert L.fd_kv_insert_frame(gp, FAKE, None, FAKE, FAKE, 0, None) == -1
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, FAKE, -1, None) == -4
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, MISALIGNED, 0, None) == -5
