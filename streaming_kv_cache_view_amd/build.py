@@ -32,6 +32,9 @@ def command(out: str = LIB, extra=()) -> list[str]:
         # MFMA accumulators in ordinary VGPRs: the softmax reads S and rescales O with VALU
         # instructions, which cannot address AGPRs; this avoids per-tile AGPR<->VGPR copies
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # device code never produces or tests NaN: lets fmaxf lower to a bare v_max / v_max3
+        # (no canonicalising max per operand); host argument checks are unaffected
+        "-Xarch_device", "-fno-honor-nans",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -2,11 +2,13 @@
 //
 //  insert_kernel       bit copy of the new frame's pre-RoPE K/V into ring slot t mod F
 //                      (FlashDrive technical summary, Methodology 1, "Token Layout").
-//  stream_attn_kernel  attention of the new frame's tokens over the view-major window:
-//                      K tiles are staged HBM -> registers -> LDS with RoPE applied in
-//                      registers at each key's current (shifted) position (Methodology 1,
-//                      "Positional Encoding"); the streaming mask is generated from the
-//                      view / slot / token indices, never loaded.
+//  rope_window_kernel  once per call: every window key rotated at its current (shifted)
+//                      position (Methodology 1, "Positional Encoding") into a caller
+//                      workspace, in the QK^T operand format; the cache stays unrotated.
+//  stream_pp_kernel    (bf16) attention of the new frame's tokens over the view-major window,
+//                      two wave groups in MFMA / softmax ping-pong; the streaming mask is
+//                      generated from the view / slot / token indices, never loaded.
+//  stream_attn_kernel  (fp32) the same attention, both groups in the same phase.
 //  verify_split_kernel + verify_merge_kernel
 //                      speculative-verify attention of a short draft block over the whole
 //                      window + reasoning tail (README technique list, "Speculative
@@ -26,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fd_internal.h"
 
@@ -155,6 +159,27 @@ __device__ inline u32x2 ds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): the wave's 64
+// chunks land contiguously at lds_block (wave-uniform), lane i at +16i.
+__device__ inline void g2lds16(const void* g, void* lds_block) {
+  typedef __attribute__((address_space(1))) const void gvoid;
+  typedef __attribute__((address_space(3))) void lvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)(g), (lvoid*)(lds_block), 16, 0, 0);
+}
+// Workgroup barrier without the release/acquire fences of __syncthreads (which make the
+// compiler wait for every outstanding memory operation, loads meant to stay in flight across
+// the barrier included).  Callers
+// order what crosses it with explicit waits; the empty asm keeps the compiler from moving
+// memory operations across it.
+__device__ inline void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
+constexpr int kWaitVm0 = 0x0F70;
+
 
 // N contiguous stored elements of T (N * sizeof(T) a multiple of 16) -> floats.
 template <typename T, int N>
@@ -717,6 +742,449 @@ __global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const
 }
 
 // ---------------------------------------------------------------------------------------
+// Streaming-prefill attention for bf16 inputs: two wave groups in ping-pong.
+//
+// Same work split as the kernel above (workgroup = 128 query rows of one kv head, two groups
+// of four waves taking alternate key tiles, one LDS merge at the end), but the two groups run
+// half a tile out of phase.  Wave w and wave w+4 share a SIMD; at every half-step one of
+// them is in its MFMA phase (PV of tile k-1, then QK^T of tile k: 2x16 MFMAs for D = 128,
+// operands from LDS) while the other is in its VALU phase (mask, row max, exp2, row sum,
+// P -> bf16 of tile k, then staging of the group's next tile).  A workgroup barrier separates
+// the half-steps, so the two phases of one SIMD's waves overlap instead of contending.
+//
+// Tiles move HBM/L2 -> LDS by direct loads (global_load_lds, no registers); a group's LDS
+// ring holds two tiles.  The barrier between half-steps is a bare s_barrier: each wave orders
+// what crosses it with explicit waits (its tile loads) or by consuming its LDS reads.
+//
+// Softmax bookkeeping.  Q is scaled by log2(e)/sqrt(D) before the fp16 rounding, so QK^T is
+// already in log2 units.  The QK^T accumulator starts at -m_ref (the row's reference max),
+// so the MFMA output is the exponent itself; m_ref is raised (and O, l rescaled) only when a
+// tile's maximum exceeds it by more than kTau, so exp2 arguments stay <= kTau.
+// ---------------------------------------------------------------------------------------
+
+// max / sum of a value over the two lane halves (lane l and lane l ^ 32)
+__device__ inline float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const bf16* __restrict__ q,
+                                                        const _Float16* __restrict__ krot,
+                                                        const bf16* __restrict__ vc, void* __restrict__ out) {
+  using QK = F16Ops;
+  using PV = BF16Ops;
+  constexpr int E = 8;                           // 16-bit elements per 16-byte chunk
+  constexpr int TK = 64;                         // keys per tile
+  constexpr int NKB = TK / 32;                   // 32-key MFMA blocks per tile
+  constexpr int H2 = D / 2;
+  constexpr int CH = H2 / E;                     // chunks per half row (Q staging)
+  constexpr int NU = D / 16;                     // k-steps of QK^T
+  constexpr int RPP = 256 / CH;                  // Q staging rows per pass
+  constexpr int QS = D + E;                      // Q staging row stride (elements, padded)
+  constexpr int KROWB = D * 2;                   // K tile row (bytes; chunks XOR-swizzled)
+  constexpr int KCH = D * 2 / 16;                // 16-byte chunks per K row
+  constexpr int VROWB = D * 2;
+  constexpr int VCH = VROWB / 16;
+  constexpr int NKL = TK * KCH / 256;            // direct K loads per thread and tile
+  constexpr int NVL = TK * VCH / 256;            // direct V loads per thread and tile
+  constexpr int KSLOT = TK * KROWB;
+  constexpr int SLOT = KSLOT + TK * VROWB;
+  constexpr int QBYTES = 128 * QS * 2;
+  constexpr int MBYTES = 4 * 32 * (D + 4) * 4;
+  constexpr int B1 = 4 * SLOT > QBYTES + 16 * H2 * 8 ? 4 * SLOT : QBYTES + 16 * H2 * 8;
+  constexpr int BUFB = B1 > MBYTES ? B1 : MBYTES;
+  constexpr int ND = D / 32;
+  constexpr int NC = TK / 16;                    // PV k-chunks per tile
+  constexpr int NMF = NC * ND;                   // PV MFMAs per tile (== QK MFMAs per tile)
+  constexpr float kTau = 8.f;
+  static_assert(NMF == NKB * NU, "PV and QK^T phases must pair one to one");
+  static_assert(NKL >= 1 && NVL >= 1 && (TK * KCH) % 256 == 0 && (TK * VCH) % 256 == 0, "staging map");
+
+  __shared__ float2 csq[4][H2];
+  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ __attribute__((aligned(16))) unsigned char buf[BUFB];
+  float2 (*csA)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES);
+  float2 (*csB)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES + 8 * H2 * 8);
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = tid >> 6;
+  const int grp = w >> 2, wr = w & 3, gt = tid & 255;
+  // wave-uniform values in scalar registers (the index arithmetic of staging and masking)
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  int bid = blockIdx.x;
+  const int kvh = bid % p.Hkv;
+  bid /= p.Hkv;
+  const int hsub = bid % p.n_hsub;
+  bid /= p.n_hsub;
+  const int qb = bid % p.nqb;
+  const int v = p.V - 1 - bid / p.nqb;
+  const int tok0 = qb * 32 * p.TBW;
+  const int head = kvh * p.G + hsub * p.HPW + (wr % p.HPW);
+  const int my_tok = tok0 + 32 * (wr / p.HPW) + l32;
+  const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
+
+  // ---- tile sequence: prefix, full frames of views 0..v (newest slot of view v last), diagonal
+  const int tps = (p.T + TK - 1) / TK;
+  const int hasP = p.P > 0 ? 1 : 0;
+  const int nfull = v * p.F + p.F - 1;
+  const int tok_end = tok0 + 32 * p.TBW;
+  const int ndiag = (min(p.T, tok_end) + TK - 1) / TK;
+  const int ntiles = hasP * ((p.P + TK - 1) / TK) + nfull * tps + ndiag;
+  struct Cursor {
+    int e, k, nk, seglen, row0;
+    bool diag;
+  };
+  auto enter = [&](Cursor& c, int e) {
+    c.e = e;
+    c.k = 0;
+    if (e < hasP) {
+      c.row0 = 0;
+      c.seglen = p.P;
+      c.nk = (p.P + TK - 1) / TK;
+      c.diag = false;
+      return;
+    }
+    e -= hasP;
+    int u, s;
+    if (e < nfull) {
+      if (e < v * p.F) {
+        u = e / p.F;
+        s = e - u * p.F;
+      } else {
+        u = v;
+        const int j = e - v * p.F;
+        s = j < p.s_new ? j : j + 1;
+      }
+      c.nk = tps;
+      c.diag = false;
+    } else {
+      u = v;
+      s = p.s_new;
+      c.nk = ndiag;
+      c.diag = true;
+    }
+    c.row0 = p.P + (u * p.F + s) * p.T;
+    c.seglen = p.T;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.k == c.nk) enter(c, c.e + 1);
+  };
+  auto advance2 = [&](Cursor& c) {   // a group takes every other tile
+    advance(c);
+    advance(c);
+  };
+
+  // ---- staging of one tile by the group's 256 threads, straight from HBM/L2 into LDS
+  // (global_load_lds, 16 bytes per lane; each instruction fills 1 KB of LDS linearly, lane i
+  // at +16i, so the swizzles are applied by choosing which global chunk a lane fetches).
+  // LDS has 64 four-byte banks (256 bytes per bank row).  K row r keeps chunk c at position
+  // c ^ kswz(r): the 16 rows read by a QK^T operand load (one chunk each) land in 16 distinct
+  // bank groups.  V row `key` keeps chunk c at c ^ vswz(key): the 32 lanes of a transposing
+  // read (4 keys x 4 chunks x 2 halves) land in 32 distinct bank pairs.  Rows past the tile's
+  // end are clamped to its last row: in bounds, and those keys are masked.
+  constexpr int KPR = 16 / KCH, VPR = 16 / VCH;  // rows per bank row
+  auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
+  auto vswz = [](uint32_t key) { return 4 * ((key / VPR) & (VCH / 4 - 1)); };
+  auto slot_of = [&](int j) { return 2 * grp + (j & 1); };
+  // Tile j+1 is staged at the start of VALU phase j, into the slot of tile j-1 (its K was read
+  // in MFMA phase j-1, its V in MFMA phase j), one half-step ahead of its use.
+  auto stage_k = [&](const Cursor& c, int j) {
+    unsigned char* Kb = buf + uni(slot_of(j) * SLOT);
+    const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
+    const int wrs = uni(wr);
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(krot + (static_cast<int64_t>(kvh) * p.W + row0) * D);
+    uint32_t ln = lane;
+    asm volatile("" : "+v"(ln));   // recompute the lane terms here rather than keep them live
+    const uint32_t lr = static_cast<uint32_t>(lastr);
+#pragma unroll
+    for (int m = 0; m < NKL; ++m) {
+      const uint32_t blk = wrs * NKL + m, r = blk * (64 / KCH) + ln / KCH;
+      const uint32_t cg = (ln % KCH) ^ kswz(r);
+      g2lds16(kb + (min(r, lr) * (D * 2) + cg * 16), Kb + blk * 1024);
+    }
+  };
+  auto stage_v = [&](const Cursor& c, int j) {
+    unsigned char* Vb = buf + uni(slot_of(j) * SLOT) + KSLOT;
+    const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
+    const int wrs = uni(wr);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D);
+    uint32_t ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t lr = static_cast<uint32_t>(lastr);
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) {
+      const uint32_t blk = wrs * NVL + m, r = blk * (64 / VCH) + ln / VCH;
+      const uint32_t cg = (ln % VCH) ^ vswz(r);
+      g2lds16(vb + (min(r, lr) * (D * 2) + cg * 16), Vb + blk * 1024);
+    }
+  };
+
+  // ---- prologue: rotated, scaled queries (through LDS into operand registers)
+  Cursor cl;   // the group's next tile to stage
+  enter(cl, 0);
+  if (grp == 1) advance(cl);
+  Cursor cs = cl;   // the group's tile whose softmax is next
+  const int ngt = (ntiles - grp + 1) / 2;
+  for (int e = tid; e < 16 * H2; e += 512) {
+    const int tb = e / (8 * H2), a = (e / H2) % 8, i = e % H2;
+    const float2 v2 = cs_angle((tb == 0 ? 8.0 * a : static_cast<double>(a)) * p.inv_freq[i]);
+    if (tb == 0) csA[a][i] = v2;
+    else csB[a][i] = v2;
+  }
+  for (int e = tid; e < 4 * H2; e += 512) {
+    const int ww = e / H2, i = e % H2;
+    csq[ww][i] = cs_angle(static_cast<double>(qpos0 + tok0 + 32 * (ww / p.HPW)) * p.inv_freq[i]);
+  }
+  __syncthreads();
+  {
+    const float sc = p.sm_scale_log2;
+    _Float16* Ql = reinterpret_cast<_Float16*>(buf);
+    const int kc_ = gt % CH, kr0 = gt / CH;
+#pragma unroll
+    for (int ps = 0; ps < (64 + RPP - 1) / RPP; ++ps) {
+      const int rq = kr0 + ps * RPP;
+      if (RPP > 64 && rq >= 64) continue;
+      const int row = 64 * grp + rq;
+      const int ww = row >> 5, r = row & 31;
+      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+      const int tk = tok0 + 32 * (ww / p.HPW) + r;
+      float x1[E], x2[E];
+      if (tk < p.T) {
+        const bf16* src = q + (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
+        BF16Ops::unpack(ld16(src + E * kc_), x1);
+        BF16Ops::unpack(ld16(src + H2 + E * kc_), x2);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x1[e] = x2[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = E * kc_ + e;
+        const float2 c2 = cmul(csq[ww][i], cmul(csA[r >> 3][i], csB[r & 7][i]));
+        const float a = x1[e], b = x2[e];
+        x1[e] = (a * c2.x - b * c2.y) * sc;
+        x2[e] = (b * c2.x + a * c2.y) * sc;
+      }
+      st16(Ql + row * QS + E * kc_, QK::pack(x1));
+      st16(Ql + row * QS + H2 + E * kc_, QK::pack(x2));
+    }
+  }
+  __syncthreads();
+  u32x4 qf[NU];
+  {
+    const _Float16* Ql = reinterpret_cast<const _Float16*>(buf);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) qf[u] = ld16(Ql + (32 * wr + l32) * QS + 2 * E * u + E * h);
+  }
+  __syncthreads();
+  if (ngt > 0) {
+    stage_k(cl, 0);
+    stage_v(cl, 0);
+    advance2(cl);
+  }
+
+  // lane constants of the operand reads
+  int krd[NU];                                           // QK A operand: row l32, chunk 2u+h
+#pragma unroll
+  for (int u = 0; u < NU; ++u) krd[u] = l32 * KROWB + (((2 * u + h) ^ kswz(l32)) << 4);
+  const int key0 = 4 * h + ((lane & 15) >> 2);           // PV A operand: keys 16c+key0 (+8)
+  int voff[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int cb2 = (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    voff[d] = key0 * VROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+  }
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+  f32x16 s[NKB];
+  u32x4 pb[NC];
+  float m_ref = 0.f, l_run = 0.f;   // S accumulators start at -m_ref; P = exp2(S)
+  f32x16 negm = f32x16{};
+  bool fresh = true;                // no key has contributed to this row yet
+
+  // MFMA phase k: PV of tile k-1 (P in pb) and QK^T of tile k, one of each per step.  The
+  // operand reads of step t+2 are issued before the MFMAs of step t (the schedule is pinned
+  // with sched_group_barrier: the MFMA pipe would otherwise wait on every LDS read).
+  auto mfma_phase = [&](auto pv_t, auto qk_t, int k) {
+    constexpr bool DO_PV = decltype(pv_t)::value, DO_QK = decltype(qk_t)::value;
+    constexpr int RD = (DO_PV ? 2 : 0) + (DO_QK ? 1 : 0);   // LDS reads per step
+    constexpr int MF = (DO_PV ? 1 : 0) + (DO_QK ? 1 : 0);   // MFMAs per step
+    constexpr int LEAD = 2;
+    const unsigned char* Kb = buf + uni(slot_of(k) * SLOT);
+    const unsigned char* Vb = buf + uni(slot_of(k + 1) * SLOT) + KSLOT;   // slot of tile k-1
+    u32x4 va[NMF], ka[NMF];
+    auto read = [&](int t) {
+      if constexpr (DO_PV) {
+        const int cc = t / ND, d = t % ND;
+        const u32x2 lo = ds_read_tr16(Vb + voff[d] + 16 * cc * VROWB);
+        const u32x2 hi = ds_read_tr16(Vb + voff[d] + (16 * cc + 8) * VROWB);
+        va[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+      if constexpr (DO_QK) {
+        const int kb = t / NU, u = t % NU;
+        ka[t] = ld16(Kb + krd[u] + kb * 32 * KROWB);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < LEAD; ++t) read(t);
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) {
+      if (t + LEAD < NMF) read(t + LEAD);
+      if constexpr (DO_PV) {
+        const int cc = t / ND, d = t % ND;
+        o[d] = PV::mma(va[t], pb[cc], o[d]);
+      }
+      if constexpr (DO_QK) {
+        const int kb = t / NU, u = t % NU;
+        s[kb] = QK::mma(ka[t], qf[u], u == 0 ? negm : s[kb]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, LEAD * RD, 0);
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) {
+      if (t + LEAD < NMF) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    }
+  };
+
+  // VALU phase: softmax of the tile at cursor c (S in s[], relative to m_ref) -> pb, l_run.
+  auto softmax = [&](const Cursor& c) {
+    const int ktok0 = uni(c.k * TK), len = uni(min(TK, c.seglen - ktok0));
+    const bool diag = uni(c.diag ? 1 : 0) != 0;
+    if (diag || len < TK) {   // generated mask: tile end, causal newest slot
+      // key kk = 32kb + 8(i/4) + 4h + i%4 is visible iff kk < lim
+      const int lim = (diag ? min(len, my_tok - ktok0 + 1) : len) - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) < lim) ? s[kb][i] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    }
+    mx = xhalf_max(mx);
+    const bool need = fresh || mx > kTau;
+    if (__ballot(need) != 0) {   // first keys of a row, or a row max grew by more than 2^kTau
+      const float delta = (need && mx != -INFINITY) ? mx : 0.f;
+      const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(-delta);   // O, l are 0 if fresh
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] -= delta;
+      m_ref += delta;
+      fresh = fresh && mx == -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(s[kb][i]);
+        s[kb][i] = pr;
+        lsum += pr;
+      }
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      float pv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) pv[e] = s[cc / 2][E * (cc % 2) + e];
+      pb[cc] = PV::pack(pv);
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile 0 has landed
+  wg_barrier();
+  // ---- half-steps: group g is in its MFMA phase k at step 2k + g, in its VALU phase k at
+  // step 2k + 1 + g (softmax of tile k, then staging of tile k+1 and loads of tile k+2).
+  const int ng0 = (ntiles + 1) / 2, ng1 = ntiles / 2;
+  const int nsteps = max(2 * ng0 + 1, 2 * ng1 + 2);
+  for (int st = 0; st < nsteps; ++st) {
+    const int qs = st - grp;
+    if (qs >= 0) {
+      const int k = qs >> 1;
+      if ((qs & 1) == 0) {
+   // K of tile k+1 into the slot K of k-1 has left
+        const bool pv = k >= 1 && k <= ngt, qk = k < ngt;
+        if (pv && qk) mfma_phase(std::true_type{}, std::true_type{}, k);
+        else if (qk) mfma_phase(std::false_type{}, std::true_type{}, k);
+        else if (pv) mfma_phase(std::true_type{}, std::false_type{}, k);
+      } else if (k < ngt) {
+        if (k + 1 < ngt) {   // V of tile k+1 into the slot V of k-1 has left
+          stage_k(cl, k + 1);
+          stage_v(cl, k + 1);
+          advance2(cl);
+        }
+        softmax(cs);
+        advance2(cs);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile k+1 has landed
+      }
+    }
+    wg_barrier();
+  }
+
+  __syncthreads();
+  // ---- merge the two groups (same rows, disjoint key tiles), then O / l
+  const float m_eff = fresh ? -INFINITY : m_ref;
+  const float l_half = xhalf_sum(l_run);
+  float* mb = reinterpret_cast<float*>(buf) + wr * 32 * (D + 4);
+  if (grp == 1) {
+    if (lane < 32) {
+      red_m[wr][l32] = m_eff;
+      red_l[wr][l32] = l_half;
+    }
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig)
+        *reinterpret_cast<f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h) =
+            f32x4{o[d][4 * ig], o[d][4 * ig + 1], o[d][4 * ig + 2], o[d][4 * ig + 3]};
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = red_m[wr][l32], l1 = red_l[wr][l32];
+    const float M = fmaxf(m_eff, m1);
+    const float a0 = (m_eff == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_eff - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    const float inv = 1.f / (a0 * l_half + a1 * l1);
+    if (my_tok < p.T) {
+      const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int d0 = 32 * d + 8 * ig + 4 * h;
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
+          const f32x4 r = {(o[d][4 * ig] * a0 + ov[0] * a1) * inv, (o[d][4 * ig + 1] * a0 + ov[1] * a1) * inv,
+                           (o[d][4 * ig + 2] * a0 + ov[2] * a1) * inv, (o[d][4 * ig + 3] * a0 + ov[3] * a1) * inv};
+          if (p.out_bf16) {
+            bf16 b4[4] = {static_cast<bf16>(r[0]), static_cast<bf16>(r[1]), static_cast<bf16>(r[2]), static_cast<bf16>(r[3])};
+            *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + obase + d0) = *reinterpret_cast<const u32x2*>(b4);
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + d0) = r;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Verify, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block token b), one
 // 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W), reasoning rows
 // [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk and copied into
@@ -1036,8 +1504,13 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                      static_cast<const T*>(kc), krot, aligned);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
-  hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
-                     static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
+  if constexpr (std::is_same<T, bf16>::value) {
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
+                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
+  } else {
+    hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
+                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
+  }
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 
