@@ -89,9 +89,10 @@ def verify_pairs(g, n_tail, blk) -> int:
     return blk * (g.window + n_tail) + blk * (blk + 1) // 2
 
 
-def cpu_baseline(layers_sample: int = 3):
-    """The fp64 oracle (as it stands) on a bounded sample: config-3 streaming layers + config-4 verifies."""
-    import numpy as np
+def cpu_baseline(min_seconds: float = 12.0, max_layers: int = 36):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: config-3
+    streaming-prefill layers, one after another, until min_seconds have elapsed (or all
+    max_layers are done).  Returns its algorithmic TFLOP/s (same FLOP count as the GPU)."""
     import oracle.fd_oracle as fd_oracle
     from streaming_kv_cache_view_amd import synth
     try:
@@ -100,20 +101,21 @@ def cpu_baseline(layers_sample: int = 3):
     except Exception:
         blas_threads = 1
     cores = len(os.sched_getaffinity(0))
-    w3, w4 = synth.CONFIGS[3], synth.CONFIGS[4]
+    w3 = synth.CONFIGS[3]
     g = w3.geom
-    flops = 0
+    flops, layers = 0, 0
     t0 = time.perf_counter()
-    for layer in range(layers_sample):
-        for _t, _out in fd_oracle.run_stream_workload(w3, layer, [w3.first_t], synth):
+    while layers < max_layers and time.perf_counter() - t0 < min_seconds:
+        for _t, _out in fd_oracle.run_stream_workload(w3, layers, [w3.first_t], synth):
             flops += 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
+        layers += 1
     t_stream = time.perf_counter() - t0
     return {
         "value": flops / t_stream / 1e12,
         "unit": "TFLOP/s",
-        "cores": min(cores, blas_threads) if blas_threads > 1 else 1,
+        "cores": min(cores, blas_threads),
         "kind": "oracle",
-        "sample": f"fp64 oracle streaming prefill of config 3, {layers_sample} of 36 layers "
+        "sample": f"fp64 oracle streaming prefill of config 3, layers 0..{layers - 1} of 36 "
                   f"(window build + full re-rotation + explicit mask), {t_stream:.1f} s; "
                   f"host cores visible {cores}, BLAS threads {blas_threads}",
     }
@@ -126,7 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle sample length (whole config-3 layers until this many seconds)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -262,7 +265,7 @@ def main():
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_layers)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
