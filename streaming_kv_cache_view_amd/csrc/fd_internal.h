@@ -11,8 +11,9 @@ namespace fd {
 constexpr int kMaxHalf = 64;      // D/2 for D = 128
 constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
 constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
-constexpr int kVerifyBlocksPerWave = 1;
-constexpr int kVerifyWaves = 4;
+constexpr int kVerifyWaves = 4;             // waves per verify workgroup
+constexpr int kVerifyBlocksPerWave = 1;     // fp32 path
+constexpr int kVerifyBlocksPerWaveDma = 2;  // bf16 path
 
 // Everything a kernel needs about one call, passed by value as a kernel argument.
 struct KParams {
@@ -33,6 +34,7 @@ struct KParams {
   int64_t t;          // newest frame
   float sm_scale_log2;  // log2(e) / sqrt(D)
   float pad1;
+  double log2_theta;    // log2(rope_theta): frequencies computed in-kernel without a memory load
   double inv_freq[kMaxHalf];  // theta^(-2i/D), fp64
 };
 
@@ -41,7 +43,8 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
   return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock) + ceil_div(tail_rows, kVerifyBlock);
 }
-inline int verify_splits(int nblk) { return ceil_div(nblk, kVerifyWaves * kVerifyBlocksPerWave); }
+// splits per kv head: each workgroup covers kVerifyWaves * blocks_per_wave key blocks
+inline int verify_splits(int nblk, int blocks_per_wave) { return ceil_div(nblk, kVerifyWaves * blocks_per_wave); }
 // fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
 constexpr size_t kVerifyWsHeader = 256;

@@ -1438,44 +1438,346 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Verify for bf16 inputs, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block
+// token b), one 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W),
+// reasoning rows [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk
+// and copied into the cache here).  They are cut into 32-key blocks inside segments of
+// contiguous positions; wave w of split s takes blocks 8s + 2w and 8s + 2w + 1.
+//
+// The kernel is a single pass over HBM: every K and V byte of the workgroup's eight blocks
+// (128 KB for D = 128) is requested at once, straight into LDS (global_load_lds), before
+// the rotation tables are built; only then are keys rotated (LDS -> registers, at their
+// current positions), QK^T / softmax / PV run per block, and the four waves merge into one
+// (m, l, O) partial per (kv head, split).
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
+                                                         const bf16* __restrict__ kb,
+                                                         const bf16* __restrict__ vb, bf16* __restrict__ kc,
+                                                         bf16* __restrict__ vc, float* __restrict__ part) {
+  using QK = F16Ops;
+  using PV = BF16Ops;
+  constexpr int E = 8;
+  constexpr int H2 = D / 2;
+  constexpr int NU = D / 16;                     // QK^T k-steps (chunks 2u + h)
+  constexpr int ND = D / 32;
+  constexpr int ROWB = D * 2;                    // K / V row bytes
+  constexpr int KCH = ROWB / 16;                 // 16-byte chunks per row
+  constexpr int BLKB = 32 * ROWB;                // one 32-key block of K (or V)
+  constexpr int NIB = BLKB / 1024;               // direct loads per block and matrix
+  constexpr int NBW = kVerifyBlocksPerWaveDma;   // blocks per wave
+  constexpr int RS = H2 + 2;                     // padded offset-table row (float2)
+  constexpr int OS = D + 4;
+  constexpr int KVB = 4 * NBW * BLKB;            // K (or V) bytes of the workgroup
+  static_assert(2 * 32 * OS * 4 <= KVB, "merge buffer aliases the K tiles");
+  constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
+  auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
+  auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
+
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[KVB];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[KVB];
+  __shared__ __attribute__((aligned(16))) float2 csr[32][RS];   // cos/sin(r f_i), r < 32
+  __shared__ float2 csq[H2];                     // cos/sin(first block position * f_i)
+  __shared__ float2 csb[4][NBW][H2];             // cos/sin(key block base * f_i)
+  __shared__ float red_m[4][32], red_l[4][32];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int kvh = blockIdx.x % p.Hkv, split = blockIdx.x / p.Hkv;
+  const int hh = l32 / p.B, bq = l32 % p.B;
+  const bool qvalid = hh < p.G;
+  const int head = kvh * p.G + (qvalid ? hh : 0);
+  const int tailbase = p.W + p.n_tail;   // cache row of block token 0
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+
+  // ---- this thread's rotation frequency theta^(-2i/D), computed (a load of the table would
+  // queue behind the K/V loads below and hold back the rotation tables until they land)
+  const double fi = exp2(-(2.0 * (tid % H2) / D) * p.log2_theta);
+
+  // ---- this wave's key blocks
+  const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
+  int x0[NBW], len[NBW];
+  int64_t pos0[NBW];
+#pragma unroll
+  for (int lb = 0; lb < NBW; ++lb) {
+    const int j = split * 4 * NBW + NBW * w + lb;
+    x0[lb] = 0;
+    len[lb] = 0;
+    pos0[lb] = 0;
+    if (j < p.nblk) {
+      if (j < nbp) {
+        x0[lb] = 32 * j;
+        len[lb] = min(32, p.P - x0[lb]);
+        pos0[lb] = p.pos_base + x0[lb];
+      } else if (j - nbp < nslot * nbs) {
+        const int jj = j - nbp, vs = jj / nbs, st = 32 * (jj % nbs);
+        x0[lb] = p.P + vs * p.T + st;
+        len[lb] = min(32, p.T - st);
+        pos0[lb] = slot_pos(p, vs / p.F, vs % p.F) + st;
+      } else {
+        const int st = 32 * (j - nbp - nslot * nbs);
+        x0[lb] = p.W + st;
+        len[lb] = min(32, p.n_tail + p.B - st);
+        pos0[lb] = p.pos_base + p.W + st;
+      }
+    }
+    x0[lb] = uni(x0[lb]);
+    len[lb] = uni(len[lb]);
+  }
+
+  // ---- queries (registers) and every K / V byte of the workgroup (LDS), all in flight
+  u32x4 qraw[NU];
+  {
+    const bf16* qsrc = qb + (static_cast<int64_t>(bq) * p.Hq + head) * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) qraw[u] = ld16(qsrc + 2 * E * u + E * h);   // invalid rows: zeroed below
+  }
+#pragma unroll
+  for (int lb = 0; lb < NBW; ++lb) {
+    if (len[lb] <= 0) continue;
+    unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
+    unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
+    const uint32_t lr = static_cast<uint32_t>(len[lb] - 1);
+#pragma unroll
+    for (int m = 0; m < NIB; ++m) {
+      const uint32_t pos = m * 64 + lane, r = min(pos / KCH, lr), c = pos % KCH;
+      const int x = x0[lb] + static_cast<int>(r);
+      const bf16* krow = x >= tailbase ? kb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
+                                       : kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+      const bf16* vrow = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
+                                       : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+      g2lds16(krow + 8 * (c ^ kswz(pos / KCH)), Kt + m * 1024);
+      g2lds16(vrow + 8 * (c ^ vswz(pos / KCH)), Vt + m * 1024);
+    }
+  }
+
+  // ---- rotation tables, computed in registers while the loads are in flight (an LDS store
+  // here would wait for the direct loads, which also write LDS); stored once they have landed
+  constexpr int NR = 32 * H2 / 256;             // csr entries per thread: rows tid/H2 + k*(256/H2)
+  float2 tr_[NR], tq = make_float2(1.f, 0.f), tb[NBW];
+#pragma unroll
+  for (int k2 = 0; k2 < NR; ++k2) tr_[k2] = cs_angle(static_cast<double>(tid / H2 + k2 * (256 / H2)) * fi);
+  if (tid < H2) tq = cs_angle(static_cast<double>(p.pos_base + tailbase) * fi);
+#pragma unroll
+  for (int lb = 0; lb < NBW; ++lb) tb[lb] = lane < H2 ? cs_angle(static_cast<double>(pos0[lb]) * fi) : tq;
+  __builtin_amdgcn_sched_barrier(0);      // keep the table math ahead of the wait
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's K / V have landed
+#pragma unroll
+  for (int k2 = 0; k2 < NR; ++k2) csr[tid / H2 + k2 * (256 / H2)][tid % H2] = tr_[k2];
+  if (tid < H2) csq[tid] = tq;
+  if (lane < H2) {
+#pragma unroll
+    for (int lb = 0; lb < NBW; ++lb) csb[w][lb][lane] = tb[lb];
+  }
+  __syncthreads();
+
+  // ---- block rows: into the cache (their K / V came from k_blk / v_blk)
+#pragma unroll
+  for (int lb = 0; lb < NBW; ++lb) {
+    if (len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
+    const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
+    const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
+    for (int e = lane; e < 32 * KCH; e += 64) {
+      const int r = e / KCH, c = e % KCH, x = x0[lb] + r;
+      if (r < len[lb] && x >= tailbase) {
+        const int64_t dst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 8 * c;
+        st16(kc + dst, ld16(Kt + r * ROWB + ((c ^ kswz(r)) << 4)));
+        st16(vc + dst, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
+      }
+    }
+  }
+
+  // ---- queries rotated at their positions, scaled into log2 units, rounded to fp16
+  u32x4 qf[NU];
+  {
+    float fq[NU][E];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[u], fq[u]);
+    const float qs = qvalid ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
+#pragma unroll
+    for (int u = 0; u < NU / 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = 2 * E * u + E * h + e;
+        const float2 cq = cmul(csq[i], csr[bq][i]);
+        const float a = fq[u][e], b = fq[u + NU / 2][e];
+        fq[u][e] = (a * cq.x - b * cq.y) * qs;
+        fq[u + NU / 2][e] = (b * cq.x + a * cq.y) * qs;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) qf[u] = QK::pack(fq[u]);
+  }
+
+  // lane constants of the PV operand reads (V^T through transposing reads)
+  const int key0 = 4 * h + ((lane & 15) >> 2);
+  int voff[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int cb2 = (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    voff[d] = key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+  }
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+  for (int lb = 0; lb < NBW; ++lb) {
+    if (len[lb] <= 0) continue;
+    const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
+    const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
+    // K row l32 (both halves of every RoPE pair), rotated at its position, fp16
+    u32x4 kf[NU];
+    {
+      float fk[2][E];
+#pragma unroll
+      for (int u = 0; u < NU / 2; ++u) {
+        BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4)), fk[0]);
+        BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * (u + NU / 2) + h) ^ kswz(l32)) << 4)), fk[1]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = 2 * E * u + E * h + e;
+          const float2 ck = cmul(csb[w][lb][i], csr[l32][i]);
+          const float a = fk[0][e], b = fk[1][e];
+          fk[0][e] = a * ck.x - b * ck.y;
+          fk[1][e] = b * ck.x + a * ck.y;
+        }
+        kf[u] = QK::pack(fk[0]);
+        kf[u + NU / 2] = QK::pack(fk[1]);
+      }
+    }
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[u], s);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+      const bool ok = (kk < len[lb]) & ((x0[lb] + kk - tailbase) <= bq);
+      s[i] = ok ? s[i] : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = __builtin_amdgcn_exp2f(s[i] - mu);
+      l_run += s[i];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float pv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) pv[e] = s[E * cc + e];
+      const u32x4 bop = PV::pack(pv);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const u32x2 lo = ds_read_tr16(Vt + voff[d] + 16 * cc * ROWB);
+        const u32x2 hi = ds_read_tr16(Vt + voff[d] + (16 * cc + 8) * ROWB);
+        o[d] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, bop, o[d]);
+      }
+    }
+  }
+  __syncthreads();   // K / V tiles are dead: the space is reused for the merge
+
+  // ---- merge the four waves (same rows, different keys) into one partial
+  const float l_tot = xhalf_sum(l_run);
+  if (lane < 32) {
+    red_m[w][l32] = m_run;
+    red_l[w][l32] = l_tot;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][l32]);
+  float L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww)
+    if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
+  const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  float* obuf = reinterpret_cast<float*>(kbuf);
+  float* ob = obuf + (w & 1) * 32 * OS;
+  if (w < 2) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const f32x4 r = {o[d][4 * ig] * scale, o[d][4 * ig + 1] * scale, o[d][4 * ig + 2] * scale, o[d][4 * ig + 3] * scale};
+        *reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h) = r;
+      }
+  }
+  __syncthreads();
+  if (w >= 2) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        f32x4* dst = reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h);
+        const f32x4 r = {o[d][4 * ig] * scale, o[d][4 * ig + 1] * scale, o[d][4 * ig + 2] * scale, o[d][4 * ig + 3] * scale};
+        *dst = *dst + r;
+      }
+  }
+  __syncthreads();
+  float* dstp = part + (static_cast<int64_t>(kvh) * p.n_split + split) * verify_partial_words(D);
+  for (int e = tid; e < 32 * D / 4; e += 256) {
+    const int r = e / (D / 4), c = e % (D / 4);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(obuf + 32 * OS + r * OS + 4 * c);
+    *reinterpret_cast<f32x4*>(dstp + r * D + 4 * c) = a + b;
+  }
+  if (w == 0 && lane < 32) {
+    dstp[32 * D + l32] = M;
+    dstp[32 * D + 32 + l32] = L;
+  }
+}
+
 // Verify merge: fixed-order log-sum-exp combination of the n_split partials of each kv head.
-// Grid = Hkv * 4 workgroups; thread = (row in an 8-row group, 4 consecutive d).  Partials are
-// read eight at a time so that their loads are in flight together.
+// One workgroup per (kv head, row); thread (split group sg, 4 consecutive d).  Each thread
+// folds splits sg, sg + SG, ... (all its loads in flight together), then the split groups
+// are folded in LDS in index order.
 __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
-  constexpr int BATCH = 8;
-  const int kvh = blockIdx.x >> 2, rg = blockIdx.x & 3;
-  const int r = rg * 8 + (threadIdx.x >> 5);
-  const int d0 = 4 * (threadIdx.x & 31);
-  if (d0 >= p.D) return;
+  constexpr int MAXF = 8;   // splits folded per thread per pass
+  const int kvh = blockIdx.x / 32, r = blockIdx.x % 32;
   const int hh = r / p.B, b = r % p.B;
   if (hh >= p.G) return;
+  const int cpr = p.D / 4;                    // 4-float chunks per row
+  const int sg = threadIdx.x / cpr, c = threadIdx.x % cpr;
+  const int SG = 256 / cpr;                   // split groups
   const size_t pw = verify_partial_words(p.D);
   const float* base = part + static_cast<size_t>(kvh) * p.n_split * pw;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = f32x4{};
-  for (int s0 = 0; s0 < p.n_split; s0 += BATCH) {
-    float mm[BATCH], ll[BATCH];
-    f32x4 ov[BATCH];
+  for (int s0 = sg; s0 < p.n_split; s0 += SG * MAXF) {
+    float mm[MAXF], ll[MAXF];
+    f32x4 ov[MAXF];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
+    for (int j = 0; j < MAXF; ++j) {
+      const int s = s0 + j * SG;
       mm[j] = -INFINITY;
       ll[j] = 0.f;
       ov[j] = f32x4{};
-      if (s0 + j < p.n_split) {
-        const float* ps = base + (s0 + j) * pw;
+      if (s < p.n_split) {
+        const float* ps = base + s * pw;
         mm[j] = ps[32 * p.D + r];
         ll[j] = ps[32 * p.D + 32 + r];
-        ov[j] = *reinterpret_cast<const f32x4*>(ps + r * p.D + d0);
+        ov[j] = *reinterpret_cast<const f32x4*>(ps + r * p.D + 4 * c);
       }
     }
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
+    for (int j = 0; j < MAXF; ++j) {
       if (mm[j] == -INFINITY) continue;
       if (mm[j] > M) {
-        const float c = __builtin_amdgcn_exp2f(M - mm[j]);
-        acc *= c;
-        L *= c;
+        const float f = __builtin_amdgcn_exp2f(M - mm[j]);
+        acc *= f;
+        L *= f;
         M = mm[j];
       }
       const float wgt = __builtin_amdgcn_exp2f(mm[j] - M);
@@ -1483,8 +1785,26 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
       L += wgt * ll[j];
     }
   }
-  const f32x4 res = acc * (1.f / L);
-  const int64_t oidx = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + hh) * p.D + d0;
+  __shared__ float sM[256], sL[256];
+  __shared__ f32x4 sA[256];
+  sM[threadIdx.x] = M;
+  sL[threadIdx.x] = L;
+  sA[threadIdx.x] = acc;
+  __syncthreads();
+  if (sg != 0) return;
+  float Mt = -INFINITY;
+  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, sM[g * cpr + c]);
+  float Lt = 0.f;
+  f32x4 At = f32x4{};
+  for (int g = 0; g < SG; ++g) {
+    const float mg = sM[g * cpr + c];
+    if (mg == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(mg - Mt);
+    Lt += f * sL[g * cpr + c];
+    At += f * sA[g * cpr + c];
+  }
+  const f32x4 res = At * (1.f / Lt);
+  const int64_t oidx = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
   if (p.out_bf16) {
     bf16 b4[4] = {static_cast<bf16>(res[0]), static_cast<bf16>(res[1]), static_cast<bf16>(res[2]), static_cast<bf16>(res[3])};
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + oidx) = *reinterpret_cast<const u32x2*>(b4);
@@ -1518,11 +1838,17 @@ template <typename T, int D>
 int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void* vb, void* kc, void* vc,
                     void* out, void* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
-  hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_split), dim3(256), 0, st, p,
-                     static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
-                     static_cast<T*>(kc), static_cast<T*>(vc), part);
+  if constexpr (std::is_same<T, bf16>::value) {
+    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_split), dim3(256), 0, st, p,
+                       static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
+                       static_cast<T*>(kc), static_cast<T*>(vc), part);
+  } else {
+    hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_split), dim3(256), 0, st, p,
+                       static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
+                       static_cast<T*>(kc), static_cast<T*>(vc), part);
+  }
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * 4), dim3(256), 0, st, p,
+  hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * 32), dim3(256), 0, st, p,
                      static_cast<const float*>(part), out);
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
