@@ -126,7 +126,7 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
   if ((g->n_q_heads / g->n_kv_heads) * blk_len > 32) return 0;
   const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame,
                                      g->tail_cap);
-  const int S = fd::verify_splits(nblk, fd::kVerifyBlocksPerWave);   // the larger of the two paths
+  const int S = fd::verify_splits(nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);   // the larger count
   return fd::kVerifyWsHeader +
          size_t(g->n_kv_heads) * S * fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
@@ -148,8 +148,9 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
   p.n_tail = n_tail;
   p.B = blk_len;
   p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, n_tail + blk_len);
-  p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16 ? fd::kVerifyBlocksPerWaveDma
-                                                                   : fd::kVerifyBlocksPerWave);
+  p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16
+                                            ? fd::kVerifyWavesDma * fd::kVerifyBlocksPerWaveDma
+                                            : fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
   return fd::launch_verify(p, g->in_dtype == FD_BF16, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws,
                            hip_stream);
 }

@@ -11,9 +11,10 @@ namespace fd {
 constexpr int kMaxHalf = 64;      // D/2 for D = 128
 constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
 constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
-constexpr int kVerifyWaves = 4;             // waves per verify workgroup
-constexpr int kVerifyBlocksPerWave = 1;     // fp32 path
-constexpr int kVerifyBlocksPerWaveDma = 2;  // bf16 path
+constexpr int kVerifyWaves = 4;             // waves per verify workgroup, fp32 path
+constexpr int kVerifyBlocksPerWave = 1;
+constexpr int kVerifyWavesDma = 8;          // bf16 path
+constexpr int kVerifyBlocksPerWaveDma = 1;
 
 // Everything a kernel needs about one call, passed by value as a kernel argument.
 struct KParams {
@@ -43,8 +44,8 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
   return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock) + ceil_div(tail_rows, kVerifyBlock);
 }
-// splits per kv head: each workgroup covers kVerifyWaves * blocks_per_wave key blocks
-inline int verify_splits(int nblk, int blocks_per_wave) { return ceil_div(nblk, kVerifyWaves * blocks_per_wave); }
+// splits per kv head: each workgroup covers blocks_per_wg key blocks
+inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, blocks_per_wg); }
 // fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
 constexpr size_t kVerifyWsHeader = 256;

@@ -65,6 +65,14 @@ __device__ inline float2 cs_angle(double a) {
 }
 
 // cos/sin of (base + offset) from cos/sin of base and of offset.
+// (cos, sin) of 2*pi*r for r in revolutions: the fraction of r is taken in fp64 (exact for
+// |r| < 2^31), then the hardware sin / cos units, which take revolutions (max error 1.3e-7
+// over [-0.5, 0.5], measured on gfx950).
+__device__ inline float2 cs_rev(double r) {
+  const float f = static_cast<float>(r - rint(r));
+  return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
 __device__ inline float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
 }
@@ -1443,16 +1451,16 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 // token b), one 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W),
 // reasoning rows [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk
 // and copied into the cache here).  They are cut into 32-key blocks inside segments of
-// contiguous positions; wave w of split s takes blocks 8s + 2w and 8s + 2w + 1.
+// contiguous positions; wave w of split s (eight waves, two per SIMD) takes block 8s + w.
 //
 // The kernel is a single pass over HBM: every K and V byte of the workgroup's eight blocks
-// (128 KB for D = 128) is requested at once, straight into LDS (global_load_lds), before
-// the rotation tables are built; only then are keys rotated (LDS -> registers, at their
-// current positions), QK^T / softmax / PV run per block, and the four waves merge into one
-// (m, l, O) partial per (kv head, split).
+// (128 KB for D = 128) is requested at once, straight into LDS (global_load_lds).  Each wave
+// proceeds as soon as its own block has landed: keys are rotated (LDS -> registers, at their
+// current positions; cos / sin per lane from the hardware units), QK^T / softmax / PV run,
+// and the eight waves fold into one (m, l, O) partial per (kv head, split), in a fixed order.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
+__global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
                                                          const bf16* __restrict__ kb,
                                                          const bf16* __restrict__ vb, bf16* __restrict__ kc,
                                                          bf16* __restrict__ vc, float* __restrict__ part) {
@@ -1466,21 +1474,20 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   constexpr int KCH = ROWB / 16;                 // 16-byte chunks per row
   constexpr int BLKB = 32 * ROWB;                // one 32-key block of K (or V)
   constexpr int NIB = BLKB / 1024;               // direct loads per block and matrix
+  constexpr int NW = kVerifyWavesDma;           // waves per workgroup
   constexpr int NBW = kVerifyBlocksPerWaveDma;   // blocks per wave
-  constexpr int RS = H2 + 2;                     // padded offset-table row (float2)
   constexpr int OS = D + 4;
-  constexpr int KVB = 4 * NBW * BLKB;            // K (or V) bytes of the workgroup
-  static_assert(2 * 32 * OS * 4 <= KVB, "merge buffer aliases the K tiles");
+  constexpr int KVB = NW * NBW * BLKB;           // K (or V) bytes of the workgroup
+  static_assert(4 * 32 * OS * 4 <= 2 * KVB, "merge slots alias the K / V tiles");
   constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
   auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
   auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
 
-  __shared__ __attribute__((aligned(16))) unsigned char kbuf[KVB];
-  __shared__ __attribute__((aligned(16))) unsigned char vbuf[KVB];
-  __shared__ __attribute__((aligned(16))) float2 csr[32][RS];   // cos/sin(r f_i), r < 32
-  __shared__ float2 csq[H2];                     // cos/sin(first block position * f_i)
-  __shared__ float2 csb[4][NBW][H2];             // cos/sin(key block base * f_i)
-  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ __attribute__((aligned(16))) unsigned char kvbuf[2 * KVB];   // K tiles, then V tiles
+  unsigned char* const kbuf = kvbuf;
+  unsigned char* const vbuf = kvbuf + KVB;
+  __shared__ double frev[H2];                    // theta^(-2i/D) / (2 pi): revolutions per position
+  __shared__ float red_m[NW][32], red_l[NW][32];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int kvh = blockIdx.x % p.Hkv, split = blockIdx.x / p.Hkv;
@@ -1490,9 +1497,17 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   const int tailbase = p.W + p.n_tail;   // cache row of block token 0
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
 
-  // ---- this thread's rotation frequency theta^(-2i/D), computed (a load of the table would
-  // queue behind the K/V loads below and hold back the rotation tables until they land)
-  const double fi = exp2(-(2.0 * (tid % H2) / D) * p.log2_theta);
+  // ---- rotation frequencies, in revolutions per position (computed: a table load from the
+  // kernel arguments would queue behind the K/V loads below)
+  if (tid < H2) frev[tid] = exp2(-(2.0 * tid / D) * p.log2_theta) * 0.15915494309189535;
+  __syncthreads();
+  // this lane's frequencies are 16u + 8h + e (u < NU/2, e < 8): four bases from the table
+  // (read before any direct load: LDS reads after them would wait for their completion) and
+  // the ratio rho = theta^(-2/D) between consecutive frequencies
+  double fbase[NU / 2];
+#pragma unroll
+  for (int u = 0; u < NU / 2; ++u) fbase[u] = frev[2 * E * u + E * h];
+  const double rho = exp2(-(2.0 / D) * p.log2_theta);
 
   // ---- this wave's key blocks
   const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
@@ -1500,7 +1515,7 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   int64_t pos0[NBW];
 #pragma unroll
   for (int lb = 0; lb < NBW; ++lb) {
-    const int j = split * 4 * NBW + NBW * w + lb;
+    const int j = split * NW * NBW + NBW * w + lb;
     x0[lb] = 0;
     len[lb] = 0;
     pos0[lb] = 0;
@@ -1532,44 +1547,67 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
 #pragma unroll
     for (int u = 0; u < NU; ++u) qraw[u] = ld16(qsrc + 2 * E * u + E * h);   // invalid rows: zeroed below
   }
-#pragma unroll
-  for (int lb = 0; lb < NBW; ++lb) {
-    if (len[lb] <= 0) continue;
-    unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
-    unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
-    const uint32_t lr = static_cast<uint32_t>(len[lb] - 1);
+  // direct loads of this wave's block, interleaved with the (cos, sin) of its key's 32 RoPE
+  // angles (they depend on positions only), so the wave computes while the memory pipe drains
+  static_assert(NBW == 1, "one key block per wave");
+  float2 kcs[NU / 2][E];
+  {
+    unsigned char* Kt = kbuf + w * BLKB;
+    unsigned char* Vt = vbuf + w * BLKB;
+    const uint32_t lr = static_cast<uint32_t>(max(len[0], 1) - 1);
+    const double kpos = static_cast<double>(pos0[0] + l32);
 #pragma unroll
     for (int m = 0; m < NIB; ++m) {
-      const uint32_t pos = m * 64 + lane, r = min(pos / KCH, lr), c = pos % KCH;
-      const int x = x0[lb] + static_cast<int>(r);
-      const bf16* krow = x >= tailbase ? kb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                                       : kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-      const bf16* vrow = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                                       : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-      g2lds16(krow + 8 * (c ^ kswz(pos / KCH)), Kt + m * 1024);
-      g2lds16(vrow + 8 * (c ^ vswz(pos / KCH)), Vt + m * 1024);
+      if (len[0] > 0) {
+        const uint32_t pos = m * 64 + lane, r = min(pos / KCH, lr), c = pos % KCH;
+        const int x = x0[0] + static_cast<int>(r);
+        const bf16* krow = x >= tailbase ? kb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
+                                         : kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+        const bf16* vrow = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
+                                         : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+        g2lds16(krow + 8 * (c ^ kswz(pos / KCH)), Kt + m * 1024);
+        g2lds16(vrow + 8 * (c ^ vswz(pos / KCH)), Vt + m * 1024);
+      }
+      if (m < NU / 2) {
+        double f = fbase[m];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kcs[m][e] = cs_rev(kpos * f);
+          asm volatile("" : "+v"(kcs[m][e].x), "+v"(kcs[m][e].y));   // computed here, not sunk
+          f *= rho;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // ---- rotation tables, computed in registers while the loads are in flight (an LDS store
-  // here would wait for the direct loads, which also write LDS); stored once they have landed
-  constexpr int NR = 32 * H2 / 256;             // csr entries per thread: rows tid/H2 + k*(256/H2)
-  float2 tr_[NR], tq = make_float2(1.f, 0.f), tb[NBW];
+  // ---- queries rotated at their positions, scaled into log2 units, rounded to fp16 (their
+  // loads were issued first, so this waits for them only, while the K / V loads land)
+  u32x4 qf[NU];
+  {
+    float fq[NU][E];
 #pragma unroll
-  for (int k2 = 0; k2 < NR; ++k2) tr_[k2] = cs_angle(static_cast<double>(tid / H2 + k2 * (256 / H2)) * fi);
-  if (tid < H2) tq = cs_angle(static_cast<double>(p.pos_base + tailbase) * fi);
+    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[u], fq[u]);
+    const float qs = qvalid ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
+    const double qpos = static_cast<double>(p.pos_base + tailbase + bq);
 #pragma unroll
-  for (int lb = 0; lb < NBW; ++lb) tb[lb] = lane < H2 ? cs_angle(static_cast<double>(pos0[lb]) * fi) : tq;
-  __builtin_amdgcn_sched_barrier(0);      // keep the table math ahead of the wait
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's K / V have landed
+    for (int u = 0; u < NU / 2; ++u) {
+      double f = fbase[u];
 #pragma unroll
-  for (int k2 = 0; k2 < NR; ++k2) csr[tid / H2 + k2 * (256 / H2)][tid % H2] = tr_[k2];
-  if (tid < H2) csq[tid] = tq;
-  if (lane < H2) {
+      for (int e = 0; e < E; ++e) {
+        const float2 cq = cs_rev(qpos * f);
+        f *= rho;
+        const float a = fq[u][e], b = fq[u + NU / 2][e];
+        fq[u][e] = (a * cq.x - b * cq.y) * qs;
+        fq[u + NU / 2][e] = (b * cq.x + a * cq.y) * qs;
+      }
+    }
 #pragma unroll
-    for (int lb = 0; lb < NBW; ++lb) csb[w][lb][lane] = tb[lb];
+    for (int u = 0; u < NU; ++u) qf[u] = QK::pack(fq[u]);
   }
-  __syncthreads();
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's K / V have landed (no other wave's
+                                          // LDS is read before the final merge)
 
   // ---- block rows: into the cache (their K / V came from k_blk / v_blk)
 #pragma unroll
@@ -1585,28 +1623,6 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
         st16(vc + dst, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
       }
     }
-  }
-
-  // ---- queries rotated at their positions, scaled into log2 units, rounded to fp16
-  u32x4 qf[NU];
-  {
-    float fq[NU][E];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[u], fq[u]);
-    const float qs = qvalid ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
-#pragma unroll
-    for (int u = 0; u < NU / 2; ++u) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = 2 * E * u + E * h + e;
-        const float2 cq = cmul(csq[i], csr[bq][i]);
-        const float a = fq[u][e], b = fq[u + NU / 2][e];
-        fq[u][e] = (a * cq.x - b * cq.y) * qs;
-        fq[u + NU / 2][e] = (b * cq.x + a * cq.y) * qs;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) qf[u] = QK::pack(fq[u]);
   }
 
   // lane constants of the PV operand reads (V^T through transposing reads)
@@ -1637,8 +1653,7 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
         BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * (u + NU / 2) + h) ^ kswz(l32)) << 4)), fk[1]);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const int i = 2 * E * u + E * h + e;
-          const float2 ck = cmul(csb[w][lb][i], csr[l32][i]);
+          const float2 ck = kcs[u][e];
           const float a = fk[0][e], b = fk[1][e];
           fk[0][e] = a * ck.x - b * ck.y;
           fk[1][e] = b * ck.x + a * ck.y;
@@ -1687,7 +1702,9 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   }
   __syncthreads();   // K / V tiles are dead: the space is reused for the merge
 
-  // ---- merge the four waves (same rows, different keys) into one partial
+  // ---- fold the eight waves (same rows, different keys) into one partial, in a fixed order:
+  // waves 0-3 write their rescaled O to four LDS slots, waves 4-7 add theirs, the four slots
+  // are summed in slot order.
   const float l_tot = xhalf_sum(l_run);
   if (lane < 32) {
     red_m[w][l32] = m_run;
@@ -1696,15 +1713,15 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red_m[ww][l32]);
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][l32]);
   float L = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww)
+  for (int ww = 0; ww < NW; ++ww)
     if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
   const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  float* obuf = reinterpret_cast<float*>(kbuf);
-  float* ob = obuf + (w & 1) * 32 * OS;
-  if (w < 2) {
+  float* obuf = reinterpret_cast<float*>(kvbuf);   // four slots of 32 x OS floats
+  float* ob = obuf + (w & 3) * 32 * OS;
+  if (w < 4) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -1714,7 +1731,7 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
       }
   }
   __syncthreads();
-  if (w >= 2) {
+  if (w >= 4) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -1726,11 +1743,12 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
   }
   __syncthreads();
   float* dstp = part + (static_cast<int64_t>(kvh) * p.n_split + split) * verify_partial_words(D);
-  for (int e = tid; e < 32 * D / 4; e += 256) {
+  for (int e = tid; e < 32 * D / 4; e += 64 * NW) {
     const int r = e / (D / 4), c = e % (D / 4);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(obuf + 32 * OS + r * OS + 4 * c);
-    *reinterpret_cast<f32x4*>(dstp + r * D + 4 * c) = a + b;
+    f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
+#pragma unroll
+    for (int sl = 1; sl < 4; ++sl) a = a + *reinterpret_cast<const f32x4*>(obuf + sl * 32 * OS + r * OS + 4 * c);
+    *reinterpret_cast<f32x4*>(dstp + r * D + 4 * c) = a;
   }
   if (w == 0 && lane < 32) {
     dstp[32 * D + l32] = M;
@@ -1739,13 +1757,14 @@ __global__ __launch_bounds__(256) void verify_dma_kernel(const KParams p, const 
 }
 
 // Verify merge: fixed-order log-sum-exp combination of the n_split partials of each kv head.
-// One workgroup per (kv head, row); thread (split group sg, 4 consecutive d).  Each thread
+// One workgroup per (kv head, row), kv head = blockIdx % Hkv as in the split kernel, so each
+// reads partials from its own XCD's L2; thread (split group sg, 4 consecutive d).  Each thread
 // folds splits sg, sg + SG, ... (all its loads in flight together), then the split groups
 // are folded in LDS in index order.
 __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
   constexpr int MAXF = 8;   // splits folded per thread per pass
-  const int kvh = blockIdx.x / 32, r = blockIdx.x % 32;
+  const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;   // kv head k on the XCD that wrote it
   const int hh = r / p.B, b = r % p.B;
   if (hh >= p.G) return;
   const int cpr = p.D / 4;                    // 4-float chunks per row
@@ -1839,7 +1858,7 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
                     void* out, void* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_split), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
                        static_cast<T*>(kc), static_cast<T*>(vc), part);
   } else {
