@@ -104,7 +104,11 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache, const voi
 size_t fd_stream_workspace_bytes(const fd_geom* g) {
   if (check_geom(g) != FD_OK) return 0;
   const size_t window = size_t(g->prefix_len) + size_t(g->n_views) * g->n_frames * g->tok_per_frame;
-  return size_t(g->n_kv_heads) * window * g->head_dim * (g->in_dtype == FD_BF16 ? 2 : 4);
+  const size_t krot = size_t(g->n_kv_heads) * window * g->head_dim * (g->in_dtype == FD_BF16 ? 2 : 4);
+  if (g->in_dtype != FD_BF16) return krot;
+  const fd::KParams p = make_params(g, g->n_frames - 1);
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
+  return fd::align256(krot) + fd::stream_partial_bytes(n_rb, p.V, p.D);
 }
 
 int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,

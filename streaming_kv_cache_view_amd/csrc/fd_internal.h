@@ -50,6 +50,18 @@ inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, bl
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
 constexpr size_t kVerifyWsHeader = 256;
 
+// Streaming kernel (bf16 path) work split.  A row block is the 128 query rows of one
+// (kv head, head subset, token block); its views' tile sequences are laid end to end (longest
+// view, shortest, second longest, ...) and cut into V equal chunks, one workgroup each.  A
+// view cut between chunks leaves one (m, l, O) partial per piece, merged by a second kernel;
+// the workspace holds, after the rotated keys, two partial slots per (row block, chunk): a
+// chunk's first job may continue a view, its last may be continued.
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
+inline size_t stream_partial_bytes(int n_rb, int V, int D) {
+  return size_t(n_rb) * V * 2 * stream_partial_words(D) * sizeof(float);
+}
+
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
                   int slot, void* stream);
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,

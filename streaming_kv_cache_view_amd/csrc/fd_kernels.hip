@@ -41,6 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -187,6 +188,23 @@ __device__ inline void wg_barrier() {
 }
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
+
+// s_waitcnt vmcnt(n), n < 64
+constexpr int wait_vm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
+// LDS address of a pointer into __shared__ memory
+__device__ inline uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const void lvoid;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lvoid*)(p)));
+}
+// The same 16-byte-per-lane global -> LDS load as g2lds16 (lane i lands at lds + 16i; gbase
+// and lds wave-uniform, voff the lane's byte offset from gbase), issued from inline assembly.
+// The compiler does not see it as an LDS write and so inserts no wait for it before later
+// LDS reads of other buffers: loads can stay in flight across whole compute phases.  The
+// caller makes the data visible with s_waitcnt vmcnt(n) (vector loads complete in issue
+// order) and a barrier, and keeps the target out of reach of LDS reads until then.
+__device__ inline void g2lds16_async(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
+}
 
 
 // N contiguous stored elements of T (N * sizeof(T) a multiple of 16) -> floats.
@@ -780,10 +798,136 @@ __device__ inline float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Output store of 4 consecutive elements (bf16 or fp32 output).
+__device__ inline void store_out4(void* out, int out_bf16, int64_t idx, const f32x4& r) {
+  if (out_bf16) {
+    bf16 b4[4] = {static_cast<bf16>(r[0]), static_cast<bf16>(r[1]), static_cast<bf16>(r[2]), static_cast<bf16>(r[3])};
+    *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + idx) = *reinterpret_cast<const u32x2*>(b4);
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = r;
+  }
+}
+
+// Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
+// HPW heads x TBW 32-token blocks of one kv head and head subset).  For each view v its tile
+// sequence has view_tiles(v) tiles; the row block's views are laid end to end in the order
+// V-1, 0, V-2, 1, ... (long and short alternate) and the ntot tiles are cut into V chunks,
+// chunk c = [bnd(c), bnd(c+1)).  Every view has at least one tile, so no chunk is empty.
+struct StreamSplit {
+  int nP, tps, ndiag, V, F, ntot;
+  __device__ StreamSplit(const KParams& p, int qb) {
+    constexpr int TK = kTileKeys;
+    nP = (p.P + TK - 1) / TK;
+    tps = (p.T + TK - 1) / TK;
+    ndiag = (min(p.T, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
+    V = p.V;
+    F = p.F;
+    ntot = 0;
+    for (int u = 0; u < V; ++u) ntot += view_tiles(u);
+  }
+  __device__ int view_tiles(int u) const { return nP + (u * F + F - 1) * tps + ndiag; }
+  __device__ int order(int oi) const { return (oi & 1) ? oi / 2 : V - 1 - oi / 2; }
+  __device__ int bnd(int c) const { return static_cast<int>((static_cast<int64_t>(c) * ntot) / V); }
+  // start of view v in the end-to-end order
+  __device__ int start(int v) const {
+    int pos = 0;
+    for (int oi = 0; oi < V; ++oi) {
+      const int u = order(oi);
+      if (u == v) break;
+      pos += view_tiles(u);
+    }
+    return pos;
+  }
+  // the chunk holding tile x of the end-to-end order
+  __device__ int chunk_of(int x) const {
+    int c = 0;
+    for (int i = 1; i < V; ++i)
+      if (bnd(i) <= x) c = i;
+    return c;
+  }
+};
+
+// Slot of the partial of a job of view v in chunk c: two per (row block, chunk), 0 for the
+// chunk's first job (which starts at bnd(c)), 1 for its last.
+template <int D>
+__device__ inline float* stream_slot(float* part, const KParams& p, int rbi, int c, int which) {
+  return part + (static_cast<int64_t>(rbi * p.V + c) * 2 + which) * stream_partial_words(D);
+}
+
+// Merge of the views whose tiles were split between chunks: two workgroups per (row block,
+// view), 64 rows each; views held whole by one chunk were written by the attention kernel.
+// For the pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
+// sum_i 2^(m_i - M) l_i with M = max_i m_i (the online-softmax merge of disjoint key sets),
+// taken in batches of up to 4 pieces whose loads are all in flight together.  A slot holds
+// O[128][D], then (m, l) pairs per row.  Thread tid takes row tid/8 of its half and an
+// eighth of the columns.
+template <int D>
+__global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
+                                                           void* __restrict__ out) {
+  constexpr int DQ = D / 8, MAXP = 4;
+  const int half = blockIdx.x & 1, rv = blockIdx.x >> 1;
+  const int rbi = rv / p.V, v = rv % p.V;
+  const int qb = rbi % p.nqb, hsub = (rbi / p.nqb) % p.n_hsub, kvh = rbi / (p.nqb * p.n_hsub);
+  const StreamSplit sp(p, qb);
+  const int sv = sp.start(v), nv = sp.view_tiles(v);
+  const int cf = sp.chunk_of(sv), cl = sp.chunk_of(sv + nv - 1);
+  if (cf == cl) return;
+  const int tid = threadIdx.x, row = 64 * half + (tid >> 3), d0 = (tid & 7) * DQ;
+  const int ww = row >> 5;
+  const int tok = qb * 32 * p.TBW + 32 * (ww / p.HPW) + (row & 31);
+  if (tok >= p.T) return;
+  const int which_cf = sv > sp.bnd(cf) ? 1 : 0;
+  float M = -INFINITY, L = 0.f;
+  float acc[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) acc[i] = 0.f;
+  for (int c0 = cf; c0 <= cl; c0 += MAXP) {
+    f32x2 ml[MAXP];
+    f32x4 x[MAXP][DQ / 4];
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+      const int c = c0 + j;
+      if (c <= cl) {
+        const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, c, c == cf ? which_cf : 0);
+        ml[j] = *reinterpret_cast<const f32x2*>(sl + 128 * D + 2 * row);
+#pragma unroll
+        for (int i = 0; i < DQ / 4; ++i) x[j][i] = *reinterpret_cast<const f32x4*>(sl + row * D + d0 + 4 * i);
+      } else {
+        ml[j] = f32x2{-INFINITY, 0.f};
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) Mn = fmaxf(Mn, ml[j][0]);
+    const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    L *= r;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) acc[i] *= r;
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+      if (ml[j][0] == -INFINITY) continue;
+      const float wgt = __builtin_amdgcn_exp2f(ml[j][0] - Mn);
+      L += wgt * ml[j][1];
+#pragma unroll
+      for (int i = 0; i < DQ / 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * i + e] += wgt * x[j][i][e];
+    }
+    M = Mn;
+  }
+  const float inv = 1.f / L;
+  const int head = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+  const int64_t obase = (static_cast<int64_t>(v * p.T + tok) * p.Hq + head) * D + d0;
+#pragma unroll
+  for (int i = 0; i < DQ; i += 4)
+    store_out4(out, p.out_bf16, obase + i, f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv});
+}
+
 template <int D>
 __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const bf16* __restrict__ q,
                                                         const _Float16* __restrict__ krot,
-                                                        const bf16* __restrict__ vc, void* __restrict__ out) {
+                                                        const bf16* __restrict__ vc, void* __restrict__ out,
+                                                        float* __restrict__ part) {
   using QK = F16Ops;
   using PV = BF16Ops;
   constexpr int E = 8;                           // 16-bit elements per 16-byte chunk
@@ -819,9 +963,7 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   float2 (*csA)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES);
   float2 (*csB)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES + 8 * H2 * 8);
 
-  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int w = tid >> 6;
-  const int grp = w >> 2, wr = w & 3, gt = tid & 255;
+  const int tid0 = threadIdx.x;
   // wave-uniform values in scalar registers (the index arithmetic of staging and masking)
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   int bid = blockIdx.x;
@@ -830,19 +972,53 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   const int hsub = bid % p.n_hsub;
   bid /= p.n_hsub;
   const int qb = bid % p.nqb;
-  const int v = p.V - 1 - bid / p.nqb;
+  const int chunk = bid / p.nqb;
+  const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;   // row block
   const int tok0 = qb * 32 * p.TBW;
+
+  // ---- tile sequence of view v: prefix, full frames of views 0..v (view v's newest slot
+  // excluded), then view v's newest frame (the diagonal, masked per token)
+  const StreamSplit sp(p, qb);
+  const int tps = sp.tps, nP = sp.nP, ndiag = sp.ndiag;
+  const int hasP = p.P > 0 ? 1 : 0;
+  // ---- this workgroup's chunk [c0, c1) of the row block's views laid end to end
+  const int c0 = sp.bnd(chunk), c1 = sp.bnd(chunk + 1);
+
+  // LDS swizzles of the K and V tiles (see the staging below)
+  constexpr int KPR = 16 / KCH, VPR = 16 / VCH;  // rows per bank row
+  auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
+  auto vswz = [](uint32_t key) { return 4 * ((key / VPR) & (VCH / 4 - 1)); };
+  int vstart = 0;   // start of view v in the end-to-end order
+  for (int oi = 0; oi < p.V; ++oi) {
+  const int v = sp.order(oi);
+  const int nv = sp.view_tiles(v);
+  const int sv = vstart;
+  vstart += nv;
+  const int ja = max(c0, sv) - sv, jb = min(c1, sv + nv) - sv;   // this job: tiles [ja, jb) of view v
+  if (ja >= jb) continue;
+  // Lane indices from an opaque copy of the thread index: nothing derived from them is
+  // hoisted out of this loop (it would stay live across every job's main loop).
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = tid >> 6;
+  const int grp = w >> 2, wr = w & 3, gt = tid & 255;
   const int head = kvh * p.G + hsub * p.HPW + (wr % p.HPW);
   const int my_tok = tok0 + 32 * (wr / p.HPW) + l32;
-  const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
+  // lane constants of the operand reads.  QK A operand: row l32, chunk (2u+h) ^ kswz(l32),
+  // at krd0 ^ 32u.  PV A operand: keys 16c+key0 (+8), columns 32d + 16((lane>>4)&1) +
+  // 4(lane&3) with the V swizzle, at voff0 ^ 64d.  (The swizzles XOR whole chunk indices, so
+  // the step in u or d is an XOR of the byte offset.)
+  const int krd0 = l32 * KROWB + ((h ^ kswz(l32)) << 4);
+  const int key0 = 4 * h + ((lane & 15) >> 2);
+  const int voff0 = [&] {
+    const int cb2 = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    return key0 * VROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+  }();
 
-  // ---- tile sequence: prefix, full frames of views 0..v (newest slot of view v last), diagonal
-  const int tps = (p.T + TK - 1) / TK;
-  const int hasP = p.P > 0 ? 1 : 0;
+  const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
   const int nfull = v * p.F + p.F - 1;
-  const int tok_end = tok0 + 32 * p.TBW;
-  const int ndiag = (min(p.T, tok_end) + TK - 1) / TK;
-  const int ntiles = hasP * ((p.P + TK - 1) / TK) + nfull * tps + ndiag;
+  const int ntiles = jb - ja;
   struct Cursor {
     int e, k, nk, seglen, row0;
     bool diag;
@@ -895,14 +1071,12 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   // bank groups.  V row `key` keeps chunk c at c ^ vswz(key): the 32 lanes of a transposing
   // read (4 keys x 4 chunks x 2 halves) land in 32 distinct bank pairs.  Rows past the tile's
   // end are clamped to its last row: in bounds, and those keys are masked.
-  constexpr int KPR = 16 / KCH, VPR = 16 / VCH;  // rows per bank row
-  auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
-  auto vswz = [](uint32_t key) { return 4 * ((key / VPR) & (VCH / 4 - 1)); };
   auto slot_of = [&](int j) { return 2 * grp + (j & 1); };
   // Tile j+1 is staged at the start of VALU phase j, into the slot of tile j-1 (its K was read
   // in MFMA phase j-1, its V in MFMA phase j), one half-step ahead of its use.
+  const uint32_t lds_buf = lds_addr(buf);
   auto stage_k = [&](const Cursor& c, int j) {
-    unsigned char* Kb = buf + uni(slot_of(j) * SLOT);
+    const uint32_t Kb = uni(lds_buf + slot_of(j) * SLOT);
     const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
     const int wrs = uni(wr);
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(krot + (static_cast<int64_t>(kvh) * p.W + row0) * D);
@@ -913,11 +1087,11 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
     for (int m = 0; m < NKL; ++m) {
       const uint32_t blk = wrs * NKL + m, r = blk * (64 / KCH) + ln / KCH;
       const uint32_t cg = (ln % KCH) ^ kswz(r);
-      g2lds16(kb + (min(r, lr) * (D * 2) + cg * 16), Kb + blk * 1024);
+      g2lds16_async(kb, min(r, lr) * (D * 2) + cg * 16, Kb + blk * 1024);
     }
   };
   auto stage_v = [&](const Cursor& c, int j) {
-    unsigned char* Vb = buf + uni(slot_of(j) * SLOT) + KSLOT;
+    const uint32_t Vb = uni(lds_buf + slot_of(j) * SLOT + KSLOT);
     const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
     const int wrs = uni(wr);
     const unsigned char* vb = reinterpret_cast<const unsigned char*>(vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D);
@@ -928,14 +1102,23 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
     for (int m = 0; m < NVL; ++m) {
       const uint32_t blk = wrs * NVL + m, r = blk * (64 / VCH) + ln / VCH;
       const uint32_t cg = (ln % VCH) ^ vswz(r);
-      g2lds16(vb + (min(r, lr) * (D * 2) + cg * 16), Vb + blk * 1024);
+      g2lds16_async(vb, min(r, lr) * (D * 2) + cg * 16, Vb + blk * 1024);
     }
   };
 
   // ---- prologue: rotated, scaled queries (through LDS into operand registers)
-  Cursor cl;   // the group's next tile to stage
-  enter(cl, 0);
-  if (grp == 1) advance(cl);
+  Cursor cl;   // the group's next tile to stage: first tile ja + grp (if any)
+  {
+    const int t = ja + grp;
+    if (t < nP) {
+      enter(cl, 0);
+      cl.k = t;
+    } else {
+      const int f = min((t - nP) / tps, nfull);
+      enter(cl, hasP + f);
+      cl.k = t - nP - f * tps;
+    }
+  }
   Cursor cs = cl;   // the group's tile whose softmax is next
   const int ngt = (ntiles - grp + 1) / 2;
   for (int e = tid; e < 16 * H2; e += 512) {
@@ -996,18 +1179,6 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
     advance2(cl);
   }
 
-  // lane constants of the operand reads
-  int krd[NU];                                           // QK A operand: row l32, chunk 2u+h
-#pragma unroll
-  for (int u = 0; u < NU; ++u) krd[u] = l32 * KROWB + (((2 * u + h) ^ kswz(l32)) << 4);
-  const int key0 = 4 * h + ((lane & 15) >> 2);           // PV A operand: keys 16c+key0 (+8)
-  int voff[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int cb2 = (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    voff[d] = key0 * VROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
-  }
-
   f32x16 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = f32x16{};
@@ -1031,13 +1202,14 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
     auto read = [&](int t) {
       if constexpr (DO_PV) {
         const int cc = t / ND, d = t % ND;
-        const u32x2 lo = ds_read_tr16(Vb + voff[d] + 16 * cc * VROWB);
-        const u32x2 hi = ds_read_tr16(Vb + voff[d] + (16 * cc + 8) * VROWB);
+        const int vo = voff0 ^ (64 * d);
+        const u32x2 lo = ds_read_tr16(Vb + vo + 16 * cc * VROWB);
+        const u32x2 hi = ds_read_tr16(Vb + vo + (16 * cc + 8) * VROWB);
         va[t] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
       if constexpr (DO_QK) {
         const int kb = t / NU, u = t % NU;
-        ka[t] = ld16(Kb + krd[u] + kb * 32 * KROWB);
+        ka[t] = ld16(Kb + (krd0 ^ (32 * u)) + kb * 32 * KROWB);
       }
     };
 #pragma unroll
@@ -1164,32 +1336,48 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
             f32x4{o[d][4 * ig], o[d][4 * ig + 1], o[d][4 * ig + 2], o[d][4 * ig + 3]};
   }
   __syncthreads();
+  const bool whole = ja == 0 && jb == nv;
   if (grp == 0) {
     const float m1 = red_m[wr][l32], l1 = red_l[wr][l32];
     const float M = fmaxf(m_eff, m1);
     const float a0 = (m_eff == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_eff - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    const float inv = 1.f / (a0 * l_half + a1 * l1);
-    if (my_tok < p.T) {
-      const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+    const float lsum = a0 * l_half + a1 * l1;
+    if (whole) {
+      const float inv = 1.f / lsum;
+      if (my_tok < p.T) {
+        const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+#pragma unroll
+          for (int ig = 0; ig < 4; ++ig) {
+            const int d0 = 32 * d + 8 * ig + 4 * h;
+            const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
+            const f32x4 r = {(o[d][4 * ig] * a0 + ov[0] * a1) * inv, (o[d][4 * ig + 1] * a0 + ov[1] * a1) * inv,
+                             (o[d][4 * ig + 2] * a0 + ov[2] * a1) * inv, (o[d][4 * ig + 3] * a0 + ov[3] * a1) * inv};
+            store_out4(out, p.out_bf16, obase + d0, r);
+          }
+        }
+      }
+    } else {   // this job's piece of view v: unnormalised O, row max M, row sum l
+      float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
+      const int row = 32 * wr + l32;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
 #pragma unroll
         for (int ig = 0; ig < 4; ++ig) {
           const int d0 = 32 * d + 8 * ig + 4 * h;
           const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
-          const f32x4 r = {(o[d][4 * ig] * a0 + ov[0] * a1) * inv, (o[d][4 * ig + 1] * a0 + ov[1] * a1) * inv,
-                           (o[d][4 * ig + 2] * a0 + ov[2] * a1) * inv, (o[d][4 * ig + 3] * a0 + ov[3] * a1) * inv};
-          if (p.out_bf16) {
-            bf16 b4[4] = {static_cast<bf16>(r[0]), static_cast<bf16>(r[1]), static_cast<bf16>(r[2]), static_cast<bf16>(r[3])};
-            *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + obase + d0) = *reinterpret_cast<const u32x2*>(b4);
-          } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + d0) = r;
-          }
+          *reinterpret_cast<f32x4*>(slot + row * D + d0) =
+              f32x4{o[d][4 * ig] * a0 + ov[0] * a1, o[d][4 * ig + 1] * a0 + ov[1] * a1,
+                    o[d][4 * ig + 2] * a0 + ov[2] * a1, o[d][4 * ig + 3] * a0 + ov[3] * a1};
         }
       }
+      if (h == 0) *reinterpret_cast<f32x2*>(slot + 128 * D + 2 * row) = f32x2{M, lsum};
     }
   }
+  __syncthreads();   // LDS is reused by the next job
+  }   // jobs
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1839,13 +2027,18 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
   const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
   QKT* krot = static_cast<QKT*>(ws);
+  // bf16 path: the partial slots of split views after the rotated keys
+  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                         align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3((p.W + 127) / 128, p.Hkv), dim3(256), 0, st, p,
                      static_cast<const T*>(kc), krot, aligned);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
-                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
+                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+    hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, p, part, out);
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
