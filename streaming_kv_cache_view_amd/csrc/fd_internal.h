@@ -54,10 +54,12 @@ constexpr size_t kVerifyWsHeader = 256;
 // (kv head, head subset, token block); its views' tile sequences are laid end to end (longest
 // view, shortest, second longest, ...) and cut into V equal chunks, one workgroup each.  A
 // view cut between chunks leaves one (m, l, O) partial per piece, merged by a second kernel;
-// the workspace holds, after the rotated keys, two partial slots per (row block, chunk): a
-// chunk's first job may continue a view, its last may be continued.
+// the workspace holds, after the rotated keys and queries, two partial slots per (row block,
+// chunk): a chunk's first job may continue a view, its last may be continued.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
+// rotated, scaled queries (fp16, [V*T][Hq][D]) after the rotated keys
+inline size_t stream_qrot_bytes(int V, int T, int Hq, int D) { return align256(size_t(V) * T * Hq * D * 2); }
 inline size_t stream_partial_bytes(int n_rb, int V, int D) {
   return size_t(n_rb) * V * 2 * stream_partial_words(D) * sizeof(float);
 }

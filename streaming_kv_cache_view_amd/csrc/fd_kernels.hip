@@ -327,6 +327,10 @@ struct TileInfo {
 // When P and T are multiples of RPP no block straddles two segments, so the rotation of
 // row base + r is cs(base) (per block) times cs(r) (per thread); otherwise each element's
 // angle is reduced on its own.
+// For bf16 inputs the workgroups past the first nkb also rotate the new frames' queries
+// (rows (token, query head of the kv head)) at their positions, scale them by
+// log2(e)/sqrt(D) and store them as fp16 in the input's [V*T][Hq][D] order: the attention
+// kernel loads its QK^T operands straight from there.
 // ---------------------------------------------------------------------------------------
 __device__ inline int64_t row_pos(const KParams& p, int x) {
   if (x < p.P) return p.pos_base + x;
@@ -338,7 +342,8 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
                                                           typename Path<T>::QKT* __restrict__ krot,
-                                                          int aligned) {
+                                                          int aligned, int nkb, const T* __restrict__ q,
+                                                          typename Path<T>::QKT* __restrict__ qrot) {
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
   using QKT = typename Path<T>::QKT;
@@ -352,6 +357,35 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   __shared__ float2 csb[NB][H2];
   const int tid = threadIdx.x, kvh = blockIdx.y, row_base = blockIdx.x * ROWS;
   const int rr = tid / CH, c = tid % CH;
+  if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token tg, head kvh*G + hh)
+    const int G = p.G, NQ = p.V * p.T * G, qr0 = (blockIdx.x - nkb) * ROWS;
+    const float sc = p.sm_scale_log2;
+    double frev[E];   // frequencies in revolutions per position
+#pragma unroll
+    for (int e = 0; e < E; ++e) frev[e] = p.inv_freq[E * c + e] * 0.15915494309189535;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int r = qr0 + b * RPP + rr;
+      if (r >= NQ || (ROWS < RPP && rr >= ROWS)) continue;
+      const int tg = r / G, hh = r - tg * G;
+      const int v = tg / p.T, i = tg - v * p.T;
+      const double pos = static_cast<double>(p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + i);
+      const int64_t off = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hh) * D;
+      float x1[E], x2[E];
+      In::unpack(ld16(q + off + E * c), x1);
+      In::unpack(ld16(q + off + H2 + E * c), x2);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float2 cs = cs_rev(pos * frev[e]);
+        const float a = x1[e], bb = x2[e];
+        x1[e] = (a * cs.x - bb * cs.y) * sc;
+        x2[e] = (bb * cs.x + a * cs.y) * sc;
+      }
+      st16(qrot + off + E * c, QK::pack(x1));
+      st16(qrot + off + H2 + E * c, QK::pack(x2));
+    }
+    return;
+  }
   if (tid < H2) sfreq[tid] = p.inv_freq[tid];
   for (int e = tid; e < NB * H2; e += 256) {
     const int b = e / H2, i = e % H2, x0 = row_base + b * RPP;
@@ -924,7 +958,7 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
 }
 
 template <int D>
-__global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const bf16* __restrict__ q,
+__global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
                                                         const _Float16* __restrict__ krot,
                                                         const bf16* __restrict__ vc, void* __restrict__ out,
                                                         float* __restrict__ part) {
@@ -934,10 +968,7 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   constexpr int TK = 64;                         // keys per tile
   constexpr int NKB = TK / 32;                   // 32-key MFMA blocks per tile
   constexpr int H2 = D / 2;
-  constexpr int CH = H2 / E;                     // chunks per half row (Q staging)
   constexpr int NU = D / 16;                     // k-steps of QK^T
-  constexpr int RPP = 256 / CH;                  // Q staging rows per pass
-  constexpr int QS = D + E;                      // Q staging row stride (elements, padded)
   constexpr int KROWB = D * 2;                   // K tile row (bytes; chunks XOR-swizzled)
   constexpr int KCH = D * 2 / 16;                // 16-byte chunks per K row
   constexpr int VROWB = D * 2;
@@ -946,10 +977,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   constexpr int NVL = TK * VCH / 256;            // direct V loads per thread and tile
   constexpr int KSLOT = TK * KROWB;
   constexpr int SLOT = KSLOT + TK * VROWB;
-  constexpr int QBYTES = 128 * QS * 2;
   constexpr int MBYTES = 4 * 32 * (D + 4) * 4;
-  constexpr int B1 = 4 * SLOT > QBYTES + 16 * H2 * 8 ? 4 * SLOT : QBYTES + 16 * H2 * 8;
-  constexpr int BUFB = B1 > MBYTES ? B1 : MBYTES;
+  constexpr int BUFB = 4 * SLOT > MBYTES ? 4 * SLOT : MBYTES;
   constexpr int ND = D / 32;
   constexpr int NC = TK / 16;                    // PV k-chunks per tile
   constexpr int NMF = NC * ND;                   // PV MFMAs per tile (== QK MFMAs per tile)
@@ -957,11 +986,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   static_assert(NMF == NKB * NU, "PV and QK^T phases must pair one to one");
   static_assert(NKL >= 1 && NVL >= 1 && (TK * KCH) % 256 == 0 && (TK * VCH) % 256 == 0, "staging map");
 
-  __shared__ float2 csq[4][H2];
   __shared__ float red_m[4][32], red_l[4][32];
   __shared__ __attribute__((aligned(16))) unsigned char buf[BUFB];
-  float2 (*csA)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES);
-  float2 (*csB)[H2] = reinterpret_cast<float2 (*)[H2]>(buf + QBYTES + 8 * H2 * 8);
 
   const int tid0 = threadIdx.x;
   // wave-uniform values in scalar registers (the index arithmetic of staging and masking)
@@ -1071,7 +1097,7 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   // bank groups.  V row `key` keeps chunk c at c ^ vswz(key): the 32 lanes of a transposing
   // read (4 keys x 4 chunks x 2 halves) land in 32 distinct bank pairs.  Rows past the tile's
   // end are clamped to its last row: in bounds, and those keys are masked.
-  auto slot_of = [&](int j) { return 2 * grp + (j & 1); };
+  auto slot_of = [&](int j) { return grp + 2 * (j & 1); };   // tile 0 of either group in slots 0, 1
   // Tile j+1 is staged at the start of VALU phase j, into the slot of tile j-1 (its K was read
   // in MFMA phase j-1, its V in MFMA phase j), one half-step ahead of its use.
   const uint32_t lds_buf = lds_addr(buf);
@@ -1121,62 +1147,19 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   }
   Cursor cs = cl;   // the group's tile whose softmax is next
   const int ngt = (ntiles - grp + 1) / 2;
-  for (int e = tid; e < 16 * H2; e += 512) {
-    const int tb = e / (8 * H2), a = (e / H2) % 8, i = e % H2;
-    const float2 v2 = cs_angle((tb == 0 ? 8.0 * a : static_cast<double>(a)) * p.inv_freq[i]);
-    if (tb == 0) csA[a][i] = v2;
-    else csB[a][i] = v2;
-  }
-  for (int e = tid; e < 4 * H2; e += 512) {
-    const int ww = e / H2, i = e % H2;
-    csq[ww][i] = cs_angle(static_cast<double>(qpos0 + tok0 + 32 * (ww / p.HPW)) * p.inv_freq[i]);
-  }
-  __syncthreads();
-  {
-    const float sc = p.sm_scale_log2;
-    _Float16* Ql = reinterpret_cast<_Float16*>(buf);
-    const int kc_ = gt % CH, kr0 = gt / CH;
-#pragma unroll
-    for (int ps = 0; ps < (64 + RPP - 1) / RPP; ++ps) {
-      const int rq = kr0 + ps * RPP;
-      if (RPP > 64 && rq >= 64) continue;
-      const int row = 64 * grp + rq;
-      const int ww = row >> 5, r = row & 31;
-      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-      const int tk = tok0 + 32 * (ww / p.HPW) + r;
-      float x1[E], x2[E];
-      if (tk < p.T) {
-        const bf16* src = q + (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
-        BF16Ops::unpack(ld16(src + E * kc_), x1);
-        BF16Ops::unpack(ld16(src + H2 + E * kc_), x2);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) x1[e] = x2[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = E * kc_ + e;
-        const float2 c2 = cmul(csq[ww][i], cmul(csA[r >> 3][i], csB[r & 7][i]));
-        const float a = x1[e], b = x2[e];
-        x1[e] = (a * c2.x - b * c2.y) * sc;
-        x2[e] = (b * c2.x + a * c2.y) * sc;
-      }
-      st16(Ql + row * QS + E * kc_, QK::pack(x1));
-      st16(Ql + row * QS + H2 + E * kc_, QK::pack(x2));
-    }
-  }
-  __syncthreads();
-  u32x4 qf[NU];
-  {
-    const _Float16* Ql = reinterpret_cast<const _Float16*>(buf);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) qf[u] = ld16(Ql + (32 * wr + l32) * QS + 2 * E * u + E * h);
-  }
-  __syncthreads();
-  if (ngt > 0) {
+  if (ngt > 0) {   // tile 0 lands while the query operands load
     stage_k(cl, 0);
     stage_v(cl, 0);
     advance2(cl);
+  }
+  // QK^T B operand: the lane's query row (rotated and scaled by the rotation pass), d in
+  // [16u + 8h, 16u + 8h + 8)
+  u32x4 qf[NU];
+  {
+    const bool valid = my_tok < p.T;
+    const _Float16* src = qrot + (static_cast<int64_t>(v * p.T + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) qf[u] = valid ? ld16(src + 2 * E * u) : u32x4{0u, 0u, 0u, 0u};
   }
 
   f32x16 o[ND];
@@ -1337,46 +1320,60 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const b
   }
   __syncthreads();
   const bool whole = ja == 0 && jb == nv;
-  if (grp == 0) {
+  if (grp == 0) {   // combined rows, in place in LDS (normalised if the job covers the view)
     const float m1 = red_m[wr][l32], l1 = red_l[wr][l32];
     const float M = fmaxf(m_eff, m1);
     const float a0 = (m_eff == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_eff - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
     const float lsum = a0 * l_half + a1 * l1;
-    if (whole) {
-      const float inv = 1.f / lsum;
-      if (my_tok < p.T) {
-        const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
+    const float inv = whole ? 1.f / lsum : 1.f;
+    const float f0 = a0 * inv, f1 = a1 * inv;
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
+    for (int d = 0; d < ND; ++d) {
 #pragma unroll
-          for (int ig = 0; ig < 4; ++ig) {
-            const int d0 = 32 * d + 8 * ig + 4 * h;
-            const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
-            const f32x4 r = {(o[d][4 * ig] * a0 + ov[0] * a1) * inv, (o[d][4 * ig + 1] * a0 + ov[1] * a1) * inv,
-                             (o[d][4 * ig + 2] * a0 + ov[2] * a1) * inv, (o[d][4 * ig + 3] * a0 + ov[3] * a1) * inv};
-            store_out4(out, p.out_bf16, obase + d0, r);
-          }
-        }
+      for (int ig = 0; ig < 4; ++ig) {
+        f32x4* cell = reinterpret_cast<f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h);
+        const f32x4 ov = *cell;
+        *cell = f32x4{o[d][4 * ig] * f0 + ov[0] * f1, o[d][4 * ig + 1] * f0 + ov[1] * f1,
+                      o[d][4 * ig + 2] * f0 + ov[2] * f1, o[d][4 * ig + 3] * f0 + ov[3] * f1};
       }
-    } else {   // this job's piece of view v: unnormalised O, row max M, row sum l
-      float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
-      const int row = 32 * wr + l32;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const int d0 = 32 * d + 8 * ig + 4 * h;
-          const f32x4 ov = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + d0);
-          *reinterpret_cast<f32x4*>(slot + row * D + d0) =
-              f32x4{o[d][4 * ig] * a0 + ov[0] * a1, o[d][4 * ig + 1] * a0 + ov[1] * a1,
-                    o[d][4 * ig + 2] * a0 + ov[2] * a1, o[d][4 * ig + 3] * a0 + ov[3] * a1};
-        }
-      }
-      if (h == 0) *reinterpret_cast<f32x2*>(slot + 128 * D + 2 * row) = f32x2{M, lsum};
+    }
+    if (h == 0) {   // (each lane has read its own entries above)
+      red_m[wr][l32] = M;
+      red_l[wr][l32] = lsum;
     }
   }
-  __syncthreads();   // LDS is reused by the next job
+  __syncthreads();
+  // ---- rows out, 16 bytes per lane and whole rows per group of lanes.  Row r of the block
+  // is token tok0 + 32*((r/32)/HPW) + r%32 of query head kvh*G + hsub*HPW + (r/32)%HPW.
+  const float* rows = reinterpret_cast<const float*>(buf);
+  if (whole) {
+    const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
+    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
+      const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
+      if (tk >= p.T) continue;
+      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+      const int c = tid % TPR;
+      const float* src = rows + r * (D + 4);
+      const int64_t obase = (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
+      if (p.out_bf16) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src + 8 * c), hi = *reinterpret_cast<const f32x4*>(src + 8 * c + 4);
+        float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        st16(static_cast<bf16*>(out) + obase + 8 * c, BF16Ops::pack(x8));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + 4 * c) = *reinterpret_cast<const f32x4*>(src + 4 * c);
+      }
+    }
+  } else {   // this job's piece of view v: unnormalised O, then (row max M, row sum l)
+    float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
+    constexpr int TPR = D / 4;
+    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
+      const int c = tid % TPR;
+      *reinterpret_cast<f32x4*>(slot + r * D + 4 * c) = *reinterpret_cast<const f32x4*>(rows + r * (D + 4) + 4 * c);
+    }
+    if (tid < 128) *reinterpret_cast<f32x2*>(slot + 128 * D + 2 * tid) = f32x2{red_m[tid >> 5][tid & 31], red_l[tid >> 5][tid & 31]};
+  }
+  wg_barrier();   // LDS is reused by the next job (this job's output stores drain meanwhile)
   }   // jobs
 }
 
@@ -2027,15 +2024,17 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
   const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
   QKT* krot = static_cast<QKT*>(ws);
-  // bf16 path: the partial slots of split views after the rotated keys
-  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
-                                         align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
-  hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3((p.W + 127) / 128, p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const T*>(kc), krot, aligned);
+  // bf16 path: rotated, scaled queries and the partial slots of split views after the keys
+  const bool b16 = std::is_same<T, bf16>::value;
+  QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D));
+  const int nkb = (p.W + 127) / 128, nqk = b16 ? (p.V * p.T * p.G + 127) / 128 : 0;
+  hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
     hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, p, part, out);
