@@ -9,8 +9,8 @@ the ring advancing one frame per step.  Inputs are synthetic, seeded, resident i
 
 Prints one JSON line.  `value` is the streaming-prefill attention throughput over the
 whole step (algorithmic FLOPs = 4*D*Hq*unmasked (q,k) pairs, divided by the step time);
-`roofline` is the streaming-prefill kernel alone (its launches timed with HIP events on
-the stream they run on); `roofline_verify` the verify call (split + merge kernels).
+`roofline` is the streaming-prefill call (its kernels timed together with HIP events on
+the stream they run on); `roofline_verify` the verify call (its two kernels).
 """
 from __future__ import annotations
 
@@ -243,7 +243,7 @@ def main():
             "parallelism": "1 GPU",
         },
         "roofline": {
-            "kernel": "fd_stream_attn (rope_window_kernel + stream_attn_kernel)",
+            "kernel": "fd_stream_attn (rope_window_kernel + stream_pp_kernel + stream_merge_kernel)",
             "bound": "mfma",
             "achieved": round(att_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -252,7 +252,7 @@ def main():
             "traffic": committed_traffic("stream_attn_config3_traffic.md"),
         },
         "roofline_verify": {
-            "kernel": "fd_verify_attn (verify_split_kernel + verify_merge_kernel)",
+            "kernel": "fd_verify_attn (verify_dma_kernel + verify_merge_kernel)",
             "bound": "hbm",
             "achieved": round(ver_gbs, 1),
             "peak": PEAK_HBM_GBS,

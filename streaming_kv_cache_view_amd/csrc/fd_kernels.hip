@@ -5,11 +5,14 @@
 //  rope_window_kernel  once per call: every window key rotated at its current (shifted)
 //                      position (Methodology 1, "Positional Encoding") into a caller
 //                      workspace, in the QK^T operand format; the cache stays unrotated.
+//                      For bf16 inputs it also rotates and scales the new frames' queries.
 //  stream_pp_kernel    (bf16) attention of the new frame's tokens over the view-major window,
 //                      two wave groups in MFMA / softmax ping-pong; the streaming mask is
-//                      generated from the view / slot / token indices, never loaded.
+//                      generated from the view / slot / token indices, never loaded.  The
+//                      views of a block of query rows are balanced across workgroups.
+//  stream_merge_kernel (bf16) fixed-order merge of the views split between workgroups.
 //  stream_attn_kernel  (fp32) the same attention, both groups in the same phase.
-//  verify_split_kernel + verify_merge_kernel
+//  verify_dma_kernel (bf16) / verify_split_kernel (fp32) + verify_merge_kernel
 //                      speculative-verify attention of a short draft block over the whole
 //                      window + reasoning tail (README technique list, "Speculative
 //                      reasoning"; Methodology 2): split-KV over all CUs, then a fixed-order
@@ -957,6 +960,22 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
     store_out4(out, p.out_bf16, obase + i, f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv});
 }
 
+// ---------------------------------------------------------------------------------------
+// Streaming-prefill attention for bf16 inputs over the rotated window.
+// Workgroup = 8 waves over the 128 query rows of one row block (HPW query heads x 32*TBW
+// tokens sharing one kv head); blockIdx.x = ((chunk*nqb + qb)*n_hsub + hsub)*Hkv + kvh, so
+// consecutive workgroups are dealt round-robin to the 8 XCDs and each XCD keeps one kv
+// head's K/V in its L2.  The workgroup runs the jobs of its chunk (StreamSplit): pieces of
+// views' key sequences, each with the view's queries (loaded from the rotation pass's
+// output) -- the prefix, the slots of views < v, the older slots of view v and last the
+// newest slot of view v, the only one needing a per-token (causal) mask.
+// Waves w and w+4 own the same 32 rows; wave group g = w/4 takes the job's tiles g, g+2, ...
+// Half-steps separated by a barrier: one group in its MFMA phase (PV of its tile k-1 and
+// QK^T of its tile k, operands read from LDS two MFMAs ahead), the other in its VALU phase
+// (softmax of its tile k and the global -> LDS loads of its tile k+1).  The two groups merge
+// (m, l, O) through LDS at the end of a job; a whole view is normalised and written, a
+// piece goes to its partial slot for stream_merge_kernel.
+// ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
                                                         const _Float16* __restrict__ krot,
