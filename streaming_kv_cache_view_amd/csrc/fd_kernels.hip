@@ -902,9 +902,19 @@ template <int D>
 __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
   constexpr int DQ = D / 8, MAXP = 4;
-  const int half = blockIdx.x & 1, rv = blockIdx.x >> 1;
-  const int rbi = rv / p.V, v = rv % p.V;
-  const int qb = rbi % p.nqb, hsub = (rbi / p.nqb) % p.n_hsub, kvh = rbi / (p.nqb * p.n_hsub);
+  // blockIdx.x = ((half*V + v)*(n_hsub*nqb) + hsub*nqb + qb)*Hkv + kvh: like the attention
+  // kernel's, consecutive workgroups go round-robin to the XCDs with the kv head fastest, so
+  // (for Hkv a multiple of 8) a row block's partials are merged on the XCD whose L2 they were
+  // written through
+  int bid = blockIdx.x;
+  const int kvh = bid % p.Hkv;
+  bid /= p.Hkv;
+  const int qb = bid % p.nqb;
+  bid /= p.nqb;
+  const int hsub = bid % p.n_hsub;
+  bid /= p.n_hsub;
+  const int v = bid % p.V, half = bid / p.V;
+  const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
   const StreamSplit sp(p, qb);
   const int sv = sp.start(v), nv = sp.view_tiles(v);
   const int cf = sp.chunk_of(sv), cl = sp.chunk_of(sv + nv - 1);
