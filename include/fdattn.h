@@ -120,8 +120,8 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
 
 /* Bytes of workspace fd_stream_attn needs: the window's keys rotated at their current
  * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); for bf16 inputs
- * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements) and fp32
- * partial results of views whose key range is split between workgroups (about 2*V*D*4*128
+ * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements), a
+ * table of the attention kernel's key tiles (8 bytes per 64-key tile) and fp32 partial results of views whose key range is split between workgroups (about 2*V*D*4*128
  * bytes per block of 128 query rows).  0 on invalid geometry.
  * The size depends on the geometry only, so one workspace serves every layer.            */
 size_t fd_stream_workspace_bytes(const fd_geom* g);

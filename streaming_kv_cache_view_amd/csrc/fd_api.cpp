@@ -108,7 +108,8 @@ size_t fd_stream_workspace_bytes(const fd_geom* g) {
   if (g->in_dtype != FD_BF16) return krot;
   const fd::KParams p = make_params(g, g->n_frames - 1);
   const int n_rb = p.Hkv * p.n_hsub * p.nqb;
-  return fd::align256(krot) + fd::stream_qrot_bytes(p.V, p.T, p.Hq, p.D) + fd::stream_partial_bytes(n_rb, p.V, p.D);
+  return fd::align256(krot) + fd::stream_qrot_bytes(p.V, p.T, p.Hq, p.D) + fd::stream_tiles_bytes(p.P, p.T, p.V, p.F) +
+         fd::stream_partial_bytes(n_rb, p.V, p.D);
 }
 
 int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,

@@ -60,6 +60,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
 // rotated, scaled queries (fp16, [V*T][Hq][D]) after the rotated keys
 inline size_t stream_qrot_bytes(int V, int T, int Hq, int D) { return align256(size_t(V) * T * Hq * D * 2); }
+// tile table of the attention kernel (int2 per tile of every view's key sequence, the
+// diagonal at full length), between the queries and the partials
+inline size_t stream_tiles_bytes(int P, int T, int V, int F) {
+  const size_t nP = (size_t(P) + 63) / 64, tps = (size_t(T) + 63) / 64;
+  size_t n = 0;
+  for (int v = 0; v < V; ++v) n += nP + (size_t(v) * F + F - 1) * tps + tps;
+  return align256(n * 8);
+}
 inline size_t stream_partial_bytes(int n_rb, int V, int D) {
   return size_t(n_rb) * V * 2 * stream_partial_words(D) * sizeof(float);
 }

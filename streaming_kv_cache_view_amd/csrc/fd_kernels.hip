@@ -208,6 +208,13 @@ __device__ inline uint32_t lds_addr(const void* p) {
 __device__ inline void g2lds16_async(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
+// The same with an instruction offset OFF, which the hardware adds to both addresses: the
+// lane's global byte gbase + voff + OFF lands at LDS lds + OFF + 16i.
+template <int OFF>
+__device__ inline void g2lds16_async_at(const void* gbase, uint32_t voff, uint32_t lds) {
+  static_assert(OFF >= 0 && OFF < 4096, "instruction offset field");
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFF), "{m0}"(lds) : "memory");
+}
 
 
 // N contiguous stored elements of T (N * sizeof(T) a multiple of 16) -> floats.
@@ -318,6 +325,60 @@ struct TileInfo {
   int64_t pos0;
 };
 
+// Tile table of the streaming kernel (bf16 path), written once per call by the rotation
+// pass.  View v's key sequence is its prefix tiles, the full frames of views 0..v (view v's
+// newest slot excluded, slots in index order), then view v's newest frame (the diagonal,
+// masked per token); a row block whose tokens end early uses a prefix of the diagonal.  Entry
+// (v, t) = {first key row, len | diag << 7 | (first key's token within its segment) << 8}:
+// key rows index the rotated window and the cache alike.
+struct StreamTiles {
+  int nP, tps, ndmax, V, F;
+  __device__ explicit StreamTiles(const KParams& p) {
+    constexpr int TK = kTileKeys;
+    nP = (p.P + TK - 1) / TK;
+    tps = (p.T + TK - 1) / TK;
+    ndmax = tps;
+    V = p.V;
+    F = p.F;
+  }
+  __device__ int view_len(int u) const { return nP + (u * F + F - 1) * tps + ndmax; }
+  __device__ int offset(int v) const {   // first entry of view v
+    int o = 0;
+    for (int u = 0; u < v; ++u) o += view_len(u);
+    return o;
+  }
+  __device__ int2 desc(const KParams& p, int v, int t) const {
+    constexpr int TK = kTileKeys;
+    int row0, seglen, k, diag = 0;
+    if (t < nP) {   // prefix
+      row0 = 0;
+      seglen = p.P;
+      k = t;
+    } else {
+      const int nfull = v * F + F - 1;
+      const int f = min((t - nP) / tps, nfull);
+      k = t - nP - f * tps;
+      int u, sl;
+      if (f == nfull) {   // view v's newest frame
+        u = v;
+        sl = p.s_new;
+        diag = 1;
+      } else if (f < v * F) {
+        u = f / F;
+        sl = f - u * F;
+      } else {
+        u = v;
+        const int j = f - v * F;
+        sl = j < p.s_new ? j : j + 1;
+      }
+      row0 = p.P + (u * F + sl) * p.T;
+      seglen = p.T;
+    }
+    const int len = min(TK, seglen - k * TK);
+    return make_int2(row0 + k * TK, len | (diag << 7) | ((k * TK) << 8));
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // Window rotation pass of the streaming-prefill call.  Every key of the window is rotated
 // once, in registers, at the position it holds in the current window (technical summary,
@@ -346,7 +407,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
                                                           typename Path<T>::QKT* __restrict__ krot,
                                                           int aligned, int nkb, const T* __restrict__ q,
-                                                          typename Path<T>::QKT* __restrict__ qrot) {
+                                                          typename Path<T>::QKT* __restrict__ qrot,
+                                                          int2* __restrict__ tiles) {
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
   using QKT = typename Path<T>::QKT;
@@ -360,6 +422,11 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   __shared__ float2 csb[NB][H2];
   const int tid = threadIdx.x, kvh = blockIdx.y, row_base = blockIdx.x * ROWS;
   const int rr = tid / CH, c = tid % CH;
+  if (tiles && blockIdx.x == 0 && blockIdx.y == 0) {   // the attention kernel's tile table
+    const StreamTiles tt(p);
+    for (int v = 0, o = 0; v < p.V; o += tt.view_len(v), ++v)
+      for (int t = tid; t < tt.view_len(v); t += 256) tiles[o + t] = tt.desc(p, v, t);
+  }
   if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token tg, head kvh*G + hh)
     const int G = p.G, NQ = p.V * p.T * G, qr0 = (blockIdx.x - nkb) * ROWS;
     const float sc = p.sm_scale_log2;
@@ -845,6 +912,40 @@ __device__ inline void store_out4(void* out, int out_bf16, int64_t idx, const f3
   }
 }
 
+// Staging map of the bf16 streaming kernel's 64-key K and V tiles (rows of D 16-bit
+// elements, KCH 16-byte chunks each).  Wave wr of a group fills rows [16wr, 16wr+16) with
+// NL = KCH/4 loads of 1 KB; load m of lane ln fetches tile row r = (wr*NL + m)*(64/KCH) +
+// ln/KCH, chunk (ln % KCH) ^ swz(r), and lands at LDS byte 1024*(wr*NL + m) + 16*ln, so LDS row
+// r holds chunk c at position c ^ swz(r).  K rows use kswz (the 16 rows of one QK^T operand
+// read fall in 16 distinct bank groups), V rows vswz (the 32 lanes of a transposing read fall
+// in 32 distinct bank pairs).  Between loads m and 0 the row moves by 1024 bytes in memory
+// and in LDS, and the chunk index by XOR 4m for K and not at all for V: a whole tile needs one
+// lane offset per wave (instruction offsets 1024m), which check() proves for every lane.
+template <int D>
+struct StageMap {
+  static constexpr int KCH = D * 2 / 16, RPI = 64 / KCH, NL = KCH / 4;
+  static constexpr int KPR = 16 / KCH, VPR = 16 / KCH;   // rows per 256-byte bank row
+  static constexpr uint32_t kswz(uint32_t r) { return (r / KPR) & (KCH - 1); }
+  static constexpr uint32_t vswz(uint32_t r) { return 4 * ((r / VPR) & (KCH / 4 - 1)); }
+  static constexpr uint32_t row(uint32_t wr, uint32_t m, uint32_t ln) { return (wr * NL + m) * RPI + ln / KCH; }
+  static constexpr uint32_t k_off(uint32_t wr, uint32_t m, uint32_t ln) {
+    return row(wr, m, ln) * (D * 2) + (((ln % KCH) ^ kswz(row(wr, m, ln))) << 4);
+  }
+  static constexpr uint32_t v_off(uint32_t wr, uint32_t m, uint32_t ln) {
+    return row(wr, m, ln) * (D * 2) + (((ln % KCH) ^ vswz(row(wr, m, ln))) << 4);
+  }
+  static constexpr bool check() {
+    for (uint32_t wr = 0; wr < 4; ++wr)
+      for (uint32_t ln = 0; ln < 64; ++ln)
+        for (uint32_t m = 0; m < NL; ++m) {
+          if (k_off(wr, m, ln) != (k_off(wr, 0, ln) ^ (64 * m)) + 1024 * m) return false;
+          if (v_off(wr, m, ln) != v_off(wr, 0, ln) + 1024 * m) return false;
+        }
+    return RPI * D * 2 == 1024 && NL * 256 == 64 * KCH;
+  }
+};
+static_assert(StageMap<128>::check() && StageMap<64>::check(), "whole-tile staging offsets");
+
 // Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
 // HPW heads x TBW 32-token blocks of one kv head and head subset).  For each view v its tile
 // sequence has view_tiles(v) tiles; the row block's views are laid end to end in the order
@@ -990,7 +1091,7 @@ template <int D>
 __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
                                                         const _Float16* __restrict__ krot,
                                                         const bf16* __restrict__ vc, void* __restrict__ out,
-                                                        float* __restrict__ part) {
+                                                        float* __restrict__ part, const int2* __restrict__ tiles) {
   using QK = F16Ops;
   using PV = BF16Ops;
   constexpr int E = 8;                           // 16-bit elements per 16-byte chunk
@@ -1031,18 +1132,15 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;   // row block
   const int tok0 = qb * 32 * p.TBW;
 
-  // ---- tile sequence of view v: prefix, full frames of views 0..v (view v's newest slot
-  // excluded), then view v's newest frame (the diagonal, masked per token)
+  // ---- tile sequence of view v: StreamTiles (its table, tiles); its length for this row block
   const StreamSplit sp(p, qb);
-  const int tps = sp.tps, nP = sp.nP, ndiag = sp.ndiag;
-  const int hasP = p.P > 0 ? 1 : 0;
+  const StreamTiles stt(p);
   // ---- this workgroup's chunk [c0, c1) of the row block's views laid end to end
   const int c0 = sp.bnd(chunk), c1 = sp.bnd(chunk + 1);
 
-  // LDS swizzles of the K and V tiles (see the staging below)
-  constexpr int KPR = 16 / KCH, VPR = 16 / VCH;  // rows per bank row
-  auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
-  auto vswz = [](uint32_t key) { return 4 * ((key / VPR) & (VCH / 4 - 1)); };
+  // LDS swizzles of the K and V tiles (StageMap)
+  auto kswz = [](uint32_t r) { return StageMap<D>::kswz(r); };
+  auto vswz = [](uint32_t key) { return StageMap<D>::vswz(key); };
   int vstart = 0;   // start of view v in the end-to-end order
   for (int oi = 0; oi < p.V; ++oi) {
   const int v = sp.order(oi);
@@ -1071,116 +1169,52 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
     return key0 * VROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
   }();
 
-  const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
-  const int nfull = v * p.F + p.F - 1;
   const int ntiles = jb - ja;
-  struct Cursor {
-    int e, k, nk, seglen, row0;
-    bool diag;
-  };
-  auto enter = [&](Cursor& c, int e) {
-    c.e = e;
-    c.k = 0;
-    if (e < hasP) {
-      c.row0 = 0;
-      c.seglen = p.P;
-      c.nk = (p.P + TK - 1) / TK;
-      c.diag = false;
-      return;
-    }
-    e -= hasP;
-    int u, s;
-    if (e < nfull) {
-      if (e < v * p.F) {
-        u = e / p.F;
-        s = e - u * p.F;
-      } else {
-        u = v;
-        const int j = e - v * p.F;
-        s = j < p.s_new ? j : j + 1;
-      }
-      c.nk = tps;
-      c.diag = false;
-    } else {
-      u = v;
-      s = p.s_new;
-      c.nk = ndiag;
-      c.diag = true;
-    }
-    c.row0 = p.P + (u * p.F + s) * p.T;
-    c.seglen = p.T;
-  };
-  auto advance = [&](Cursor& c) {
-    if (++c.k == c.nk) enter(c, c.e + 1);
-  };
-  auto advance2 = [&](Cursor& c) {   // a group takes every other tile
-    advance(c);
-    advance(c);
-  };
+  // The job's tiles t = 0 .. ntiles-1 (tile ja + t of view v): group g takes t = g, g+2, ...
+  // and keeps tile t in LDS slot t & 3.  Their table entries are read with scalar loads.
+  const int2* jt = tiles + (stt.offset(v) + ja);
 
   // ---- staging of one tile by the group's 256 threads, straight from HBM/L2 into LDS
   // (global_load_lds, 16 bytes per lane; each instruction fills 1 KB of LDS linearly, lane i
-  // at +16i, so the swizzles are applied by choosing which global chunk a lane fetches).
-  // LDS has 64 four-byte banks (256 bytes per bank row).  K row r keeps chunk c at position
-  // c ^ kswz(r): the 16 rows read by a QK^T operand load (one chunk each) land in 16 distinct
-  // bank groups.  V row `key` keeps chunk c at c ^ vswz(key): the 32 lanes of a transposing
-  // read (4 keys x 4 chunks x 2 halves) land in 32 distinct bank pairs.  Rows past the tile's
-  // end are clamped to its last row: in bounds, and those keys are masked.
-  auto slot_of = [&](int j) { return grp + 2 * (j & 1); };   // tile 0 of either group in slots 0, 1
-  // Tile j+1 is staged at the start of VALU phase j, into the slot of tile j-1 (its K was read
-  // in MFMA phase j-1, its V in MFMA phase j), one half-step ahead of its use.
+  // at +16i, so the swizzles are applied by choosing which global chunk a lane fetches; the
+  // map and its swizzles are StageMap's).  LDS has 64 four-byte banks (256 bytes per bank row).
   const uint32_t lds_buf = lds_addr(buf);
-  auto stage_k = [&](const Cursor& c, int j) {
-    const uint32_t Kb = uni(lds_buf + slot_of(j) * SLOT);
-    const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
+  using SM = StageMap<D>;
+  static_assert(SM::NL == NKL && SM::NL == NVL, "staging map");
+  auto stage = [&](int t) {
+    const int2 d = jt[t];
+    const int row0 = d.x, lastr = (d.y & 127) - 1;
+    const uint32_t Kb = lds_buf + (t & 3) * SLOT, Vb = Kb + KSLOT;
     const int wrs = uni(wr);
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(krot + (static_cast<int64_t>(kvh) * p.W + row0) * D);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D);
     uint32_t ln = lane;
     asm volatile("" : "+v"(ln));   // recompute the lane terms here rather than keep them live
+    if (lastr == TK - 1) {   // whole tile: one lane offset, instruction offsets 1024m
+      const uint32_t ko = SM::k_off(wrs, 0, ln), kl = uni(Kb + wrs * NKL * 1024);
+      g2lds16_async_at<0>(kb, ko, kl);
+      if constexpr (NKL > 1) g2lds16_async_at<1024>(kb, ko ^ 64, kl);
+      if constexpr (NKL > 2) g2lds16_async_at<2048>(kb, ko ^ 128, kl);
+      if constexpr (NKL > 3) g2lds16_async_at<3072>(kb, ko ^ 192, kl);
+      const uint32_t vo = SM::v_off(wrs, 0, ln), vl = uni(Vb + wrs * NVL * 1024);
+      g2lds16_async_at<0>(vb, vo, vl);
+      if constexpr (NVL > 1) g2lds16_async_at<1024>(vb, vo, vl);
+      if constexpr (NVL > 2) g2lds16_async_at<2048>(vb, vo, vl);
+      if constexpr (NVL > 3) g2lds16_async_at<3072>(vb, vo, vl);
+      return;
+    }
+    // Rows past the tile's end are clamped to its last row: in bounds, and those keys are masked.
     const uint32_t lr = static_cast<uint32_t>(lastr);
 #pragma unroll
     for (int m = 0; m < NKL; ++m) {
-      const uint32_t blk = wrs * NKL + m, r = blk * (64 / KCH) + ln / KCH;
-      const uint32_t cg = (ln % KCH) ^ kswz(r);
-      g2lds16_async(kb, min(r, lr) * (D * 2) + cg * 16, Kb + blk * 1024);
-    }
-  };
-  auto stage_v = [&](const Cursor& c, int j) {
-    const uint32_t Vb = uni(lds_buf + slot_of(j) * SLOT + KSLOT);
-    const int row0 = uni(c.row0 + c.k * TK), lastr = uni(min(TK, c.seglen - c.k * TK) - 1);
-    const int wrs = uni(wr);
-    const unsigned char* vb = reinterpret_cast<const unsigned char*>(vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D);
-    uint32_t ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint32_t lr = static_cast<uint32_t>(lastr);
-#pragma unroll
-    for (int m = 0; m < NVL; ++m) {
-      const uint32_t blk = wrs * NVL + m, r = blk * (64 / VCH) + ln / VCH;
-      const uint32_t cg = (ln % VCH) ^ vswz(r);
-      g2lds16_async(vb, min(r, lr) * (D * 2) + cg * 16, Vb + blk * 1024);
+      const uint32_t r = min(SM::row(wrs, m, ln), lr) * (D * 2);
+      g2lds16_async(kb, r + (SM::k_off(wrs, m, ln) & (D * 2 - 1)), Kb + (wrs * NKL + m) * 1024);
+      g2lds16_async(vb, r + (SM::v_off(wrs, m, ln) & (D * 2 - 1)), Vb + (wrs * NVL + m) * 1024);
     }
   };
 
-  // ---- prologue: rotated, scaled queries (through LDS into operand registers)
-  Cursor cl;   // the group's next tile to stage: first tile ja + grp (if any)
-  {
-    const int t = ja + grp;
-    if (t < nP) {
-      enter(cl, 0);
-      cl.k = t;
-    } else {
-      const int f = min((t - nP) / tps, nfull);
-      enter(cl, hasP + f);
-      cl.k = t - nP - f * tps;
-    }
-  }
-  Cursor cs = cl;   // the group's tile whose softmax is next
-  const int ngt = (ntiles - grp + 1) / 2;
-  if (ngt > 0) {   // tile 0 lands while the query operands load
-    stage_k(cl, 0);
-    stage_v(cl, 0);
-    advance2(cl);
-  }
+  // ---- prologue: tile t = grp of the job lands while the query operands load
+  if (grp < ntiles) stage(uni(grp));
   // QK^T B operand: the lane's query row (rotated and scaled by the rotation pass), d in
   // [16u + 8h, 16u + 8h + 8)
   u32x4 qf[NU];
@@ -1200,16 +1234,17 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   f32x16 negm = f32x16{};
   bool fresh = true;                // no key has contributed to this row yet
 
-  // MFMA phase k: PV of tile k-1 (P in pb) and QK^T of tile k, one of each per step.  The
-  // operand reads of step t+2 are issued before the MFMAs of step t (the schedule is pinned
-  // with sched_group_barrier: the MFMA pipe would otherwise wait on every LDS read).
-  auto mfma_phase = [&](auto pv_t, auto qk_t, int k) {
+  // MFMA phase at half-step st: PV of tile st-2 (P in pb) and QK^T of tile st, one of each
+  // per step.  The operand reads of step t+2 are issued before the MFMAs of step t (the
+  // schedule is pinned with sched_group_barrier: the MFMA pipe would otherwise wait on every
+  // LDS read).
+  auto mfma_phase = [&](auto pv_t, auto qk_t, int st) {
     constexpr bool DO_PV = decltype(pv_t)::value, DO_QK = decltype(qk_t)::value;
     constexpr int RD = (DO_PV ? 2 : 0) + (DO_QK ? 1 : 0);   // LDS reads per step
     constexpr int MF = (DO_PV ? 1 : 0) + (DO_QK ? 1 : 0);   // MFMAs per step
     constexpr int LEAD = 2;
-    const unsigned char* Kb = buf + uni(slot_of(k) * SLOT);
-    const unsigned char* Vb = buf + uni(slot_of(k + 1) * SLOT) + KSLOT;   // slot of tile k-1
+    const unsigned char* Kb = buf + (st & 3) * SLOT;
+    const unsigned char* Vb = buf + ((st + 2) & 3) * SLOT + KSLOT;   // slot of tile st-2
     u32x4 va[NMF], ka[NMF];
     auto read = [&](int t) {
       if constexpr (DO_PV) {
@@ -1246,10 +1281,11 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
     }
   };
 
-  // VALU phase: softmax of the tile at cursor c (S in s[], relative to m_ref) -> pb, l_run.
-  auto softmax = [&](const Cursor& c) {
-    const int ktok0 = uni(c.k * TK), len = uni(min(TK, c.seglen - ktok0));
-    const bool diag = uni(c.diag ? 1 : 0) != 0;
+  // VALU phase: softmax of a tile (S in s[], relative to m_ref; meta its table entry's
+  // second word) -> pb, l_run.
+  auto softmax = [&](int meta) {
+    const int ktok0 = meta >> 8, len = meta & 127;
+    const bool diag = (meta & 128) != 0;
     if (diag || len < TK) {   // generated mask: tile end, causal newest slot
       // key kk = 32kb + 8(i/4) + 4h + i%4 is visible iff kk < lim
       const int lim = (diag ? min(len, my_tok - ktok0 + 1) : len) - 4 * h;
@@ -1280,17 +1316,17 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 #pragma unroll
       for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
     }
-    float lsum = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: short dependency chains
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pr = __builtin_amdgcn_exp2f(s[kb][i]);
         s[kb][i] = pr;
-        lsum += pr;
+        ls[i & 3] += pr;
       }
     }
-    l_run += lsum;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       float pv[E];
@@ -1302,30 +1338,23 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile 0 has landed
   wg_barrier();
-  // ---- half-steps: group g is in its MFMA phase k at step 2k + g, in its VALU phase k at
-  // step 2k + 1 + g (softmax of tile k, then staging of tile k+1 and loads of tile k+2).
-  const int ng0 = (ntiles + 1) / 2, ng1 = ntiles / 2;
-  const int nsteps = max(2 * ng0 + 1, 2 * ng1 + 2);
-  for (int st = 0; st < nsteps; ++st) {
-    const int qs = st - grp;
-    if (qs >= 0) {
-      const int k = qs >> 1;
-      if ((qs & 1) == 0) {
-   // K of tile k+1 into the slot K of k-1 has left
-        const bool pv = k >= 1 && k <= ngt, qk = k < ngt;
-        if (pv && qk) mfma_phase(std::true_type{}, std::true_type{}, k);
-        else if (qk) mfma_phase(std::false_type{}, std::true_type{}, k);
-        else if (pv) mfma_phase(std::true_type{}, std::false_type{}, k);
-      } else if (k < ngt) {
-        if (k + 1 < ngt) {   // V of tile k+1 into the slot V of k-1 has left
-          stage_k(cl, k + 1);
-          stage_v(cl, k + 1);
-          advance2(cl);
-        }
-        softmax(cs);
-        advance2(cs);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile k+1 has landed
-      }
+  // ---- half-steps st = 0 .. ntiles+1: the group of tile st (st & 1) is in its MFMA phase
+  // (QK^T of tile st, PV of tile st-2), the other group in its VALU phase (softmax of tile
+  // st-1, then staging of tile st+1 into the slot of tile st-3, whose K was read in MFMA
+  // phase st-3 and V in MFMA phase st-1).  Tile indices depend on st only.
+  for (int st = 0; st < ntiles + 2; ++st) {
+    int stv = st;
+    asm volatile("" : "+v"(stv));
+    if (((st - grp) & 1) == 0) {
+      const bool pv = stv >= 2 && stv - 2 < ntiles, qk = stv < ntiles;
+      if (pv && qk) mfma_phase(std::true_type{}, std::true_type{}, st);
+      else if (qk) mfma_phase(std::false_type{}, std::true_type{}, st);
+      else if (pv) mfma_phase(std::true_type{}, std::false_type{}, st);
+    } else if (stv >= 1 && stv - 1 < ntiles) {
+      const int meta = jt[st - 1].y;
+      if (stv + 1 < ntiles) stage(st + 1);
+      softmax(meta);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile st+1 has landed
     }
     wg_barrier();
   }
@@ -2053,18 +2082,22 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
   const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
   QKT* krot = static_cast<QKT*>(ws);
-  // bf16 path: rotated, scaled queries and the partial slots of split views after the keys
+  // bf16 path: rotated, scaled queries, the tile table and the partial slots of split views
+  // after the keys
   const bool b16 = std::is_same<T, bf16>::value;
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D));
+  int2* tiles = b16 ? reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D))
+                    : nullptr;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D) +
+                                         stream_tiles_bytes(p.P, p.T, p.V, p.F));
   const int nkb = (p.W + 127) / 128, nqk = b16 ? (p.V * p.T * p.G + 127) / 128 : 0;
   hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot);
+                     static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
-                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part);
+                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
     hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, p, part, out);
   } else {
