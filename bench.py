@@ -212,6 +212,31 @@ def main():
     mean = lambda a: sum(a) / len(a)
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
+    # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
+    # kernel argument depending on the newest frame only through it
+    F = g.n_frames
+    graphs = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(F):
+            gr = torch.cuda.CUDAGraph()
+            frame[0] = g.n_frames + i
+            with torch.cuda.graph(gr, stream=side):
+                step()
+            graphs[(g.n_frames + i) % F] = gr
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(F):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        graphs[i % F].replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    graph_ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
     esz = 2
     flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
     vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
@@ -263,6 +288,9 @@ def main():
         "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
                         "verify_attn": round(ver_us, 2)},
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
+        "graph": {"ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
+                  "graphs": F, "launches_per_step": L * 6,
+                  "note": "the same step replayed from one HIP graph per ring phase (t mod F)"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

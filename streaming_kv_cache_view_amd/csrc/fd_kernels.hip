@@ -204,16 +204,18 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // The compiler does not see it as an LDS write and so inserts no wait for it before later
 // LDS reads of other buffers: loads can stay in flight across whole compute phases.  The
 // caller makes the data visible with s_waitcnt vmcnt(n) (vector loads complete in issue
-// order) and a barrier, and keeps the target out of reach of LDS reads until then.
+// order) and a barrier, and keeps the target out of reach of LDS reads until then.  Each
+// load is preceded by one wait state after the write of M0 (the compiler does not see that
+// the assembly reads M0).
 __device__ inline void g2lds16_async(const void* gbase, uint32_t voff, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
 // The same with an instruction offset OFF, which the hardware adds to both addresses: the
 // lane's global byte gbase + voff + OFF lands at LDS lds + OFF + 16i.
 template <int OFF>
 __device__ inline void g2lds16_async_at(const void* gbase, uint32_t voff, uint32_t lds) {
   static_assert(OFF >= 0 && OFF < 4096, "instruction offset field");
-  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFF), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2" : : "v"(voff), "s"(gbase), "i"(OFF), "{m0}"(lds) : "memory");
 }
 
 

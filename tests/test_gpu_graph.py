@@ -1,0 +1,125 @@
+"""The per-window loop captured in HIP graphs.
+
+A window step is, per layer: insert the new frame of every view, streaming-prefill attention
+of the new frames, and an 8-token verify.  Every kernel argument depends on the newest frame
+index t only through t mod F (ring slot and ages), so F graphs, one per ring phase, replay any
+stream.  The library allocates nothing and synchronises nothing inside a call, so the calls
+capture as they are.  These tests replay the graphs over a rolling sequence of windows, with
+the program's own eager work and synchronisations between replays, and compare every replay
+bit for bit with the same calls launched eagerly on an identical copy of the caches.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from streaming_kv_cache_view_amd import fd, synth
+
+try:
+    from . import gpu_harness as H
+except ImportError:
+    import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fd.lib()
+
+
+class Window:
+    """Static device buffers of one window step over `layers` layers (a graph reads and
+    writes these same buffers on every replay)."""
+
+    def __init__(self, g, layers, n_tail, blk, gen):
+        rnd = lambda *s: torch.randn(*s, generator=gen, device=H.DEV).to(torch.bfloat16)
+        self.g, self.L, self.n_tail, self.blk = g, layers, n_tail, blk
+        self.kc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(layers)]
+        self.vc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(layers)]
+        self.kn = [torch.empty(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim, dtype=torch.bfloat16,
+                               device=H.DEV) for _ in range(layers)]
+        self.vn = [torch.empty_like(x) for x in self.kn]
+        self.qn = [torch.empty(g.n_new, g.n_q_heads, g.head_dim, dtype=torch.bfloat16, device=H.DEV)
+                   for _ in range(layers)]
+        self.qb = [torch.empty(blk, g.n_q_heads, g.head_dim, dtype=torch.bfloat16, device=H.DEV)
+                   for _ in range(layers)]
+        self.kb = [torch.empty(blk, g.n_kv_heads, g.head_dim, dtype=torch.bfloat16, device=H.DEV)
+                   for _ in range(layers)]
+        self.vb = [torch.empty_like(x) for x in self.kb]
+        self.out = [torch.empty(g.n_new, g.n_q_heads, g.head_dim, device=H.DEV) for _ in range(layers)]
+        self.vout = [torch.empty(blk, g.n_q_heads, g.head_dim, device=H.DEV) for _ in range(layers)]
+        self.sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+        self.vws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=H.DEV)
+
+    def clone_caches_from(self, other):
+        for a, b in zip(self.kc + self.vc, other.kc + other.vc):
+            a.copy_(b)
+
+    def load_inputs(self, src):
+        """Copy one window's frame, query and block inputs (lists per layer) into the buffers."""
+        for name in ("kn", "vn", "qn", "qb", "kb", "vb"):
+            for dst, x in zip(getattr(self, name), src[name]):
+                dst.copy_(x)
+
+    def step(self, t):
+        g = self.g
+        for l in range(self.L):
+            fd.kv_insert_frame(g, self.kc[l], self.vc[l], self.kn[l], self.vn[l], t)
+            fd.stream_attn(g, self.qn[l], self.kc[l], self.vc[l], t, self.out[l], self.sws)
+            fd.verify_attn(g, self.qb[l], self.kb[l], self.vb[l], self.kc[l], self.vc[l], t, self.n_tail,
+                           self.blk, self.vout[l], self.vws)
+
+
+def window_inputs(g, layers, blk, gen):
+    rnd = lambda *s: torch.randn(*s, generator=gen, device=H.DEV).to(torch.bfloat16)
+    return {
+        "kn": [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(layers)],
+        "vn": [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(layers)],
+        "qn": [rnd(g.n_new, g.n_q_heads, g.head_dim) for _ in range(layers)],
+        "qb": [rnd(blk, g.n_q_heads, g.head_dim) for _ in range(layers)],
+        "kb": [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(layers)],
+        "vb": [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(layers)],
+    }
+
+
+@pytest.mark.parametrize("cid,layers", [(3, 3), (5, 2)])
+def test_graph_rolling_windows_match_eager(cid, layers):
+    w = synth.CONFIGS[cid]
+    g = w.geom
+    F, blk, n_tail = g.n_frames, 8, min(200, g.tail_cap - 8)
+    gen = torch.Generator(device=H.DEV)
+    gen.manual_seed(20 + cid)
+    eager = Window(g, layers, n_tail, blk, gen)
+    graphed = Window(g, layers, n_tail, blk, gen)
+    graphed.clone_caches_from(eager)
+    t0 = F   # window full
+    # one graph per ring phase, captured on a side stream (capture does not run the kernels)
+    graphs = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for t in range(t0, t0 + F):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                graphed.step(t)
+            graphs[t % F] = gr
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    n_windows = 2 * F + 1
+    for i in range(n_windows):
+        t = t0 + i
+        src = window_inputs(g, layers, blk, gen)
+        eager.load_inputs(src)
+        eager.step(t)
+        graphed.load_inputs(src)
+        graphs[t % F].replay()
+        torch.cuda.synchronize()
+        for l in range(layers):
+            assert torch.equal(eager.out[l], graphed.out[l]), (cid, t, l, "stream")
+            assert torch.equal(eager.vout[l], graphed.vout[l]), (cid, t, l, "verify")
+        H.say(f"  cfg {cid} window t={t} (graph phase {t % F}): stream and verify outputs bit-identical")
+    for a, b in zip(eager.kc + eager.vc, graphed.kc + graphed.vc):
+        assert torch.equal(a, b)
