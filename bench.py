@@ -212,6 +212,26 @@ def main():
     mean = lambda a: sum(a) / len(a)
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
+    # verify with 16-token draft blocks (64 query rows per kv head)
+    b16 = 16
+    qb16 = [rnd(b16, g.n_q_heads, g.head_dim) for _ in range(L)]
+    kb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    vb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
+    vout16 = [torch.empty(b16, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
+    ws16 = torch.empty(fd.verify_workspace_bytes(g, b16), dtype=torch.uint8, device=dev)
+    t16 = frame[0]
+    v16_ms = []
+    for rep_i in range(1 + max(1, args.steps // 4)):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+        ev[0].record()
+        for l in range(L):
+            fd.verify_attn(g, qb16[l], kb16[l], vb16[l], kc[l], vc[l], t16, n_tail, b16, vout16[l], ws16)
+            ev[l + 1].record()
+        torch.cuda.synchronize()
+        if rep_i > 0:   # the first sweep is a warm-up
+            v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
+    v16_us = sum(v16_ms) / len(v16_ms) * 1e3
+
     # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
     # kernel argument depending on the newest frame only through it
     F = g.n_frames
@@ -241,6 +261,8 @@ def main():
     flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
     vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
                     + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+    v16bytes_layer = ((g.window + n_tail + b16) * g.n_kv_heads * g.head_dim * esz * 2
+                      + b16 * g.n_q_heads * g.head_dim * esz + b16 * g.n_q_heads * g.head_dim * 4)
     ibytes_layer = 2 * 2 * g.n_views * g.tok_per_frame * g.n_kv_heads * g.head_dim * esz
     value = flops_layer * L / (ms_per_step * 1e-3) / 1e12
     att_tflops = flops_layer / (att_us * 1e-6) / 1e12
@@ -288,6 +310,10 @@ def main():
         "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
                         "verify_attn": round(ver_us, 2)},
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
+        "verify_block16": {"us_per_call": round(v16_us, 2),
+                           "gbs": round(v16bytes_layer / (v16_us * 1e-6) / 1e9, 1),
+                           "frac": round(v16bytes_layer / (v16_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                           "note": "16-token draft block, 64 query rows per kv head"},
         "graph": {"ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
                   "graphs": F, "launches_per_step": L * 6,
                   "note": "the same step replayed from one HIP graph per ring phase (t mod F)"},

@@ -121,8 +121,9 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
 /* Bytes of workspace fd_stream_attn needs: the window's keys rotated at their current
  * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); for bf16 inputs
  * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements), a
- * table of the attention kernel's key tiles (8 bytes per 64-key tile) and fp32 partial results of views whose key range is split between workgroups (about 2*V*D*4*128
- * bytes per block of 128 query rows).  0 on invalid geometry.
+ * table of the attention kernel's key tiles (8 bytes per 64-key tile) and fp32 partial
+ * results of views whose key range is split between workgroups (about 2*V*D*4*128 bytes per
+ * block of 128 query rows).  0 on invalid geometry.
  * The size depends on the geometry only, so one workspace serves every layer.            */
 size_t fd_stream_workspace_bytes(const fd_geom* g);
 
@@ -146,7 +147,8 @@ int fd_stream_attn(const fd_geom* g, const void* q_new,
                    void* hip_stream);
 
 /* Bytes of workspace fd_verify_attn needs for blocks of up to blk_len tokens
- * (any n_tail with n_tail + blk_len <= tail_cap); 0 on invalid arguments.          */
+ * (any n_tail with n_tail + blk_len <= tail_cap): fp32 (m, l, O) partials per (kv head,
+ * 32-row block of query rows, key split); 0 on invalid arguments.                  */
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len);
 
 /* Speculative-verify attention of a draft block of blk_len tokens (README technique
@@ -161,8 +163,9 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len);
  *   ws     : device workspace of ws_bytes >= fd_verify_workspace_bytes(g, blk_len);
  *            scratch for split-KV partial results, no initial contents required.
  *            Calls that share one workspace must not overlap.
- *   Requires (Hq/Hkv) * blk_len <= 32, 1 <= blk_len, n_tail >= 0,
- *   n_tail + blk_len <= tail_cap, newest_frame >= F-1.                              */
+ *   Requires 1 <= blk_len <= 32, (Hq/Hkv) * blk_len <= 128 (the query rows of one kv
+ *   head, in up to four 32-row blocks), n_tail >= 0, n_tail + blk_len <= tail_cap,
+ *   newest_frame >= F-1.                                                            */
 int fd_verify_attn(const fd_geom* g, const void* q_blk,
                    const void* k_blk, const void* v_blk,
                    void* k_cache, void* v_cache, int64_t newest_frame,

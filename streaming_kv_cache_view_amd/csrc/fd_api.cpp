@@ -128,12 +128,13 @@ int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, con
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
   if (check_geom(g) != FD_OK) return 0;
   if (blk_len < 1 || blk_len > g->tail_cap) return 0;
-  if ((g->n_q_heads / g->n_kv_heads) * blk_len > 32) return 0;
+  const int G = g->n_q_heads / g->n_kv_heads;
+  if (blk_len > 32 || fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return 0;
   const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame,
                                      g->tail_cap);
   const int S = fd::verify_splits(nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);   // the larger count
-  return fd::kVerifyWsHeader +
-         size_t(g->n_kv_heads) * S * fd::verify_partial_words(g->head_dim) * sizeof(float);
+  return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * fd::verify_row_blocks(G, blk_len) * S *
+                                   fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
 
 int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,
@@ -144,7 +145,8 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
   if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !out) return FD_ERR_NULL;
   if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
   if (n_tail < 0 || blk_len < 1 || int64_t(n_tail) + blk_len > g->tail_cap) return FD_ERR_TAIL;
-  if ((g->n_q_heads / g->n_kv_heads) * blk_len > 32) return FD_ERR_TAIL;
+  if (blk_len > 32 || fd::verify_row_blocks(g->n_q_heads / g->n_kv_heads, blk_len) > fd::kVerifyMaxRowBlocks)
+    return FD_ERR_TAIL;
   if (!ws || ws_bytes < fd_verify_workspace_bytes(g, blk_len)) return FD_ERR_WORKSPACE;
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
@@ -152,6 +154,7 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
   fd::KParams p = make_params(g, newest_frame);
   p.n_tail = n_tail;
   p.B = blk_len;
+  p.n_rb = fd::verify_row_blocks(p.G, blk_len);
   p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, n_tail + blk_len);
   p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16
                                             ? fd::kVerifyWavesDma * fd::kVerifyBlocksPerWaveDma

@@ -30,7 +30,7 @@ struct KParams {
   int32_t nqb;        // ceil(T / (32*TBW))
   // verify
   int32_t n_tail, B, nblk, n_split;
-  int32_t pad0;
+  int32_t n_rb;       // 32-row blocks of the G*B verify query rows
   int64_t pos_base;
   int64_t t;          // newest frame
   float sm_scale_log2;  // log2(e) / sqrt(D)
@@ -48,6 +48,9 @@ inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
 inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, blocks_per_wg); }
 // fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
+// 32-row blocks of the G*B query rows of one kv head (at most kVerifyMaxRowBlocks)
+constexpr int kVerifyMaxRowBlocks = 4;
+inline int verify_row_blocks(int G, int B) { return ceil_div(G * B, 32); }
 constexpr size_t kVerifyWsHeader = 256;
 
 // Streaming kernel (bf16 path) work split.  A row block is the 128 query rows of one

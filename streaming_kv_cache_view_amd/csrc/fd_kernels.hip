@@ -1438,8 +1438,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 }
 
 // ---------------------------------------------------------------------------------------
-// Verify, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block token b), one
-// 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W), reasoning rows
+// Verify, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block token b), in
+// 32-row MFMA blocks, one workgroup per (kv head, row block, split).  Keys are numbered by cache row x: window rows [0, W), reasoning rows
 // [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk and copied into
 // the cache here).  They are cut into 32-key blocks inside segments of contiguous
 // positions; wave w of split s takes block (s*4 + w): its K rows are loaded straight into
@@ -1480,8 +1480,10 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
   __shared__ __attribute__((aligned(16))) unsigned char ubuf[UB];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int kvh = blockIdx.x % p.Hkv, split = blockIdx.x / p.Hkv;
-  const int hh = l32 / p.B, bq = l32 % p.B;
+  // blockIdx.x = (split * n_rb + rb) * Hkv + kvh: the row blocks of one split run side by
+  // side on one XCD and read the same K / V
+  const int kvh = blockIdx.x % p.Hkv, rb = (blockIdx.x / p.Hkv) % p.n_rb, split = blockIdx.x / (p.Hkv * p.n_rb);
+  const int qr = 32 * rb + l32, hh = qr / p.B, bq = qr % p.B;   // query row qr = hh*B + b
   const bool qvalid = hh < p.G;
   const int head = kvh * p.G + hh;
   const int tailbase = p.W + p.n_tail;  // cache row of block token 0
@@ -1538,11 +1540,11 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
         const T* src = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
                                      : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
         rv[jv][jj] = ld16(src + E * dc);
-        if (x >= tailbase) st16(vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D + E * dc, rv[jv][jj]);
+        if (x >= tailbase && rb == 0) st16(vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D + E * dc, rv[jv][jj]);
       }
     }
   }
-  if (kvalid && k_from_blk) {
+  if (kvalid && k_from_blk && rb == 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) st16(kc + (static_cast<int64_t>(kvh) * p.S_cap + xk) * D + 2 * E * u + E * h, kraw[u]);
   }
@@ -1678,7 +1680,7 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
       }
   }
   __syncthreads();
-  float* dstp = part + (static_cast<int64_t>(kvh) * p.n_split + split) * verify_partial_words(D);
+  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + split) * verify_partial_words(D);
   for (int e = tid; e < 32 * D / 4; e += 256) {
     const int r = e / (D / 4), c = e % (D / 4);
     const f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
@@ -1693,7 +1695,7 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 
 // ---------------------------------------------------------------------------------------
 // Verify for bf16 inputs, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block
-// token b), one 32-row MFMA block.  Keys are numbered by cache row x: window rows [0, W),
+// token b), in 32-row MFMA blocks, one workgroup per (kv head, row block, split).  Keys are numbered by cache row x: window rows [0, W),
 // reasoning rows [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk
 // and copied into the cache here).  They are cut into 32-key blocks inside segments of
 // contiguous positions; wave w of split s (eight waves, two per SIMD) takes block 8s + w.
@@ -1735,8 +1737,10 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   __shared__ float red_m[NW][32], red_l[NW][32];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int kvh = blockIdx.x % p.Hkv, split = blockIdx.x / p.Hkv;
-  const int hh = l32 / p.B, bq = l32 % p.B;
+  // blockIdx.x = (split * n_rb + rb) * Hkv + kvh: the row blocks of one split run side by
+  // side on one XCD and read the same K / V
+  const int kvh = blockIdx.x % p.Hkv, rb = (blockIdx.x / p.Hkv) % p.n_rb, split = blockIdx.x / (p.Hkv * p.n_rb);
+  const int qr = 32 * rb + l32, hh = qr / p.B, bq = qr % p.B;   // query row qr = hh*B + b
   const bool qvalid = hh < p.G;
   const int head = kvh * p.G + (qvalid ? hh : 0);
   const int tailbase = p.W + p.n_tail;   // cache row of block token 0
@@ -1857,7 +1861,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   // ---- block rows: into the cache (their K / V came from k_blk / v_blk)
 #pragma unroll
   for (int lb = 0; lb < NBW; ++lb) {
-    if (len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
+    if (rb != 0 || len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
     const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
     const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
     for (int e = lane; e < 32 * KCH; e += 64) {
@@ -1987,7 +1991,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
       }
   }
   __syncthreads();
-  float* dstp = part + (static_cast<int64_t>(kvh) * p.n_split + split) * verify_partial_words(D);
+  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + split) * verify_partial_words(D);
   for (int e = tid; e < 32 * D / 4; e += 64 * NW) {
     const int r = e / (D / 4), c = e % (D / 4);
     f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
@@ -2010,13 +2014,14 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
                                                            void* __restrict__ out) {
   constexpr int MAXF = 8;   // splits folded per thread per pass
   const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;   // kv head k on the XCD that wrote it
+  const int rr = r % 32;                                        // row within row block r / 32
   const int hh = r / p.B, b = r % p.B;
   if (hh >= p.G) return;
   const int cpr = p.D / 4;                    // 4-float chunks per row
   const int sg = threadIdx.x / cpr, c = threadIdx.x % cpr;
   const int SG = 256 / cpr;                   // split groups
   const size_t pw = verify_partial_words(p.D);
-  const float* base = part + static_cast<size_t>(kvh) * p.n_split * pw;
+  const float* base = part + (static_cast<size_t>(kvh) * p.n_rb + r / 32) * p.n_split * pw;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = f32x4{};
   for (int s0 = sg; s0 < p.n_split; s0 += SG * MAXF) {
@@ -2030,9 +2035,9 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
       ov[j] = f32x4{};
       if (s < p.n_split) {
         const float* ps = base + s * pw;
-        mm[j] = ps[32 * p.D + r];
-        ll[j] = ps[32 * p.D + 32 + r];
-        ov[j] = *reinterpret_cast<const f32x4*>(ps + r * p.D + 4 * c);
+        mm[j] = ps[32 * p.D + rr];
+        ll[j] = ps[32 * p.D + 32 + rr];
+        ov[j] = *reinterpret_cast<const f32x4*>(ps + rr * p.D + 4 * c);
       }
     }
 #pragma unroll
@@ -2114,16 +2119,16 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
                     void* out, void* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
+    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
                        static_cast<T*>(kc), static_cast<T*>(vc), part);
   } else {
-    hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_split), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(256), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
                        static_cast<T*>(kc), static_cast<T*>(vc), part);
   }
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * 32), dim3(256), 0, st, p,
+  hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
                      static_cast<const float*>(part), out);
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }

@@ -130,12 +130,17 @@ def test_call_errors():
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, FAKE, -1, None) == -4
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, MISALIGNED, 0, None) == -5
     ws = L.fd_verify_workspace_bytes(gp, 8)
-    assert ws > 0 and L.fd_verify_workspace_bytes(gp, 17) == 0                 # G*B = 34 > 32
+    ws17 = L.fd_verify_workspace_bytes(gp, 17)                                 # G*B = 34: two row blocks
+    assert ws > 0 and ws17 > ws and L.fd_verify_workspace_bytes(gp, 33) == 0   # B > 32 (and > tail_cap)
+    g8 = _g(n_q_heads=16)                                                      # G = 8
+    assert L.fd_verify_workspace_bytes(ctypes.byref(g8), 16) > 0               # 128 query rows
+    assert L.fd_verify_workspace_bytes(ctypes.byref(g8), 17) == 0              # 136 > 128
     args = [FAKE, FAKE, FAKE, FAKE, FAKE]
     assert L.fd_verify_attn(gp, *args, 5, -1, 8, FAKE, FAKE, ws, None) == -6
     assert L.fd_verify_attn(gp, *args, 5, 30, 8, FAKE, FAKE, ws, None) == -6   # n_tail + B > tail_cap
     assert L.fd_verify_attn(gp, *args, 5, 0, 0, FAKE, FAKE, ws, None) == -6
-    assert L.fd_verify_attn(gp, *args, 5, 0, 17, FAKE, FAKE, ws, None) == -6   # G*B > 32
+    assert L.fd_verify_attn(gp, *args, 5, 0, 17, FAKE, FAKE, ws, None) == -7   # two row blocks: more workspace
+    assert L.fd_verify_attn(ctypes.byref(g8), *args, 5, 0, 17, FAKE, FAKE, ws17, None) == -6   # G*B > 128
     assert L.fd_verify_attn(gp, *args, 5, 0, 8, FAKE, None, ws, None) == -7
     assert L.fd_verify_attn(gp, *args, 5, 0, 8, FAKE, FAKE, ws - 1, None) == -7
     assert L.fd_verify_attn(gp, *args, 2, 0, 8, FAKE, FAKE, ws, None) == -4
@@ -153,3 +158,5 @@ def test_workspace_size_covers_largest_block():
             + -(-g.tail_cap // 32))
     splits = -(-nblk // 4)
     assert ws >= g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4
+    # 16-token blocks: G*16 = 64 query rows per kv head, two 32-row blocks
+    assert fd.verify_workspace_bytes(g, 16) >= 2 * g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4

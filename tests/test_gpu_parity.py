@@ -243,6 +243,19 @@ def test_verify_config4_layers():
         check_verify(w, layer, w.first_t, w.n_tail, w.blk_len)
 
 
+# Larger draft blocks: G*B query rows per kv head in several 32-row blocks (G = 4: B = 16 is
+# 64 rows, B = 12 is 48 rows with a partial second block; config 1 has G = 2).
+@pytest.mark.parametrize("cid,n_tail,blk_len", [(2, 40, 16), (2, 3, 12), (1, 8, 24), (1, 0, 16)])
+def test_verify_block_rows(cid, n_tail, blk_len):
+    check_verify(synth.CONFIGS[cid], 0, 5 if cid == 2 else 4, n_tail, blk_len)
+
+
+def test_verify_config4_block16():
+    w = synth.CONFIGS[4]
+    check_verify(w, 0, w.first_t, w.n_tail, 16)
+    check_verify(w, 7, w.first_t, w.n_tail, 16, out_dtype="bf16")
+
+
 @pytest.mark.parametrize("w", EXTRA[:4], ids=lambda w: w.name)
 def test_verify_edge_geometries(w):
     g = w.geom
