@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle sample length (whole config-3 layers until this many seconds)")
+    ap.add_argument("--core-only", action="store_true",
+                    help="only the window step and its per-call timing (no block-16 verify, no graph "
+                         "replay): the per-kernel averages of a profiled run then cover one call type each")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -212,55 +215,59 @@ def main():
     mean = lambda a: sum(a) / len(a)
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
-    # verify with 16-token draft blocks (64 query rows per kv head)
-    b16 = 16
-    qb16 = [rnd(b16, g.n_q_heads, g.head_dim) for _ in range(L)]
-    kb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
-    vb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
-    vout16 = [torch.empty(b16, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
-    ws16 = torch.empty(fd.verify_workspace_bytes(g, b16), dtype=torch.uint8, device=dev)
-    t16 = frame[0]
-    v16_ms = []
-    for rep_i in range(1 + max(1, args.steps // 4)):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
-        ev[0].record()
-        for l in range(L):
-            fd.verify_attn(g, qb16[l], kb16[l], vb16[l], kc[l], vc[l], t16, n_tail, b16, vout16[l], ws16)
-            ev[l + 1].record()
-        torch.cuda.synchronize()
-        if rep_i > 0:   # the first sweep is a warm-up
-            v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
-    v16_us = sum(v16_ms) / len(v16_ms) * 1e3
-
-    # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
-    # kernel argument depending on the newest frame only through it
+    v16_us = graph_ms_per_step = None
     F = g.n_frames
-    graphs = {}
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    if not args.core_only:
+        # verify with 16-token draft blocks (64 query rows per kv head)
+        b16 = 16
+        qb16 = [rnd(b16, g.n_q_heads, g.head_dim) for _ in range(L)]
+        kb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
+        vb16 = [rnd(b16, g.n_kv_heads, g.head_dim) for _ in range(L)]
+        vout16 = [torch.empty(b16, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
+        ws16 = torch.empty(fd.verify_workspace_bytes(g, b16), dtype=torch.uint8, device=dev)
+        t16 = frame[0]
+        v16_ms = []
+        for rep_i in range(1 + max(1, args.steps // 4)):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+            ev[0].record()
+            for l in range(L):
+                fd.verify_attn(g, qb16[l], kb16[l], vb16[l], kc[l], vc[l], t16, n_tail, b16, vout16[l], ws16)
+                ev[l + 1].record()
+            torch.cuda.synchronize()
+            if rep_i > 0:   # the first sweep is a warm-up
+                v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
+        v16_us = sum(v16_ms) / len(v16_ms) * 1e3
+
+        # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
+        # kernel argument depending on the newest frame only through it
+        F = g.n_frames
+        graphs = {}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(F):
+                gr = torch.cuda.CUDAGraph()
+                frame[0] = g.n_frames + i
+                with torch.cuda.graph(gr, stream=side):
+                    step()
+                graphs[(g.n_frames + i) % F] = gr
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
         for i in range(F):
-            gr = torch.cuda.CUDAGraph()
-            frame[0] = g.n_frames + i
-            with torch.cuda.graph(gr, stream=side):
-                step()
-            graphs[(g.n_frames + i) % F] = gr
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    for i in range(F):
-        graphs[i].replay()
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        graphs[i % F].replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    graph_ms_per_step = t_start.elapsed_time(t_end) / args.steps
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(args.steps):
+            graphs[i % F].replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        graph_ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
     esz = 2
     flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
     vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
                     + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+    b16 = 16
     v16bytes_layer = ((g.window + n_tail + b16) * g.n_kv_heads * g.head_dim * esz * 2
                       + b16 * g.n_q_heads * g.head_dim * esz + b16 * g.n_q_heads * g.head_dim * 4)
     ibytes_layer = 2 * 2 * g.n_views * g.tok_per_frame * g.n_kv_heads * g.head_dim * esz
@@ -310,13 +317,15 @@ def main():
         "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
                         "verify_attn": round(ver_us, 2)},
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
-        "verify_block16": {"us_per_call": round(v16_us, 2),
-                           "gbs": round(v16bytes_layer / (v16_us * 1e-6) / 1e9, 1),
-                           "frac": round(v16bytes_layer / (v16_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                           "note": "16-token draft block, 64 query rows per kv head"},
-        "graph": {"ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
-                  "graphs": F, "launches_per_step": L * 6,
-                  "note": "the same step replayed from one HIP graph per ring phase (t mod F)"},
+        "verify_block16": None if v16_us is None else {
+            "us_per_call": round(v16_us, 2),
+            "gbs": round(v16bytes_layer / (v16_us * 1e-6) / 1e9, 1),
+            "frac": round(v16bytes_layer / (v16_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "16-token draft block, 64 query rows per kv head"},
+        "graph": None if graph_ms_per_step is None else {
+            "ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
+            "graphs": F, "launches_per_step": L * 6,
+            "note": "the same step replayed from one HIP graph per ring phase (t mod F)"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
