@@ -156,6 +156,21 @@ def oracle_stream(geom, window: StreamWindow, q_new) -> np.ndarray:
                   geom.rope_theta)
 
 
+def oracle_full_window(geom, window: StreamWindow, q_window) -> np.ndarray:
+    """Non-streaming (cold-start) prefill: every token of the window is a query.
+
+    The first window of a stream has no previous window to reuse, so all of it is
+    prefilled (README technique list, "Streaming inference": the streaming path prefills
+    the newest frame only, reusing the rest); the same mask applies, key position <= query
+    position over the logical view-major order.  q_window: [N][Hq][D] in logical order
+    (prefix, then view 0 oldest..newest, view 1, ...).  Returns fp64 [N][Hq][D].
+    """
+    assert window.full()
+    k, v = window.kv()
+    pos = window_positions(geom, k.shape[0])
+    return attend(q_window, k, v, pos, pos, geom.rope_theta)
+
+
 def oracle_verify(geom, window: StreamWindow, k_tail, v_tail, q_blk, k_blk, v_blk) -> np.ndarray:
     """Verify attention: block queries over window ++ reasoning tail ++ block (causal).
 

@@ -185,6 +185,31 @@ def pin_streaming_equals_full_recompute():
         assert err <= 1e-12, (w.name, err)
 
 
+def pin_full_window_is_sdpa_causal():
+    """Cold-start prefill == torch SDPA (is_causal) over the whole window, every row; and its
+    newest-frame rows are the streaming output.  The window and its queries are built
+    straight from frame ids (no deque), the positions are 0..N-1 + pos_base."""
+    for w in (synth.CONFIGS[1], TINY, TINY_G4):
+        g, t = w.geom, w.first_t
+        k, v, q = _full_window_direct(w, t)
+        got = fd_oracle.oracle_full_window(g, _window_at(w, t), q)
+        pos = g.pos_base + np.arange(k.shape[0])
+        full = _sdpa(fd_oracle.rope(q, pos, g.rope_theta), fd_oracle.rope(k, pos, g.rope_theta),
+                     v, causal=True)
+        assert np.max(np.abs(got - full)) <= 1e-12, w.name
+        rows = []
+        for vi in range(g.n_views):
+            start = g.prefix_len + (vi * g.n_frames + g.n_frames - 1) * g.tok_per_frame
+            rows.extend(range(start, start + g.tok_per_frame))
+        assert np.max(np.abs(got[rows] - _stream(w, t))) <= 1e-12, w.name
+        # the prefix rows only see the prefix: causal attention over the prefix alone
+        P = g.prefix_len
+        if P:
+            pre = _sdpa(fd_oracle.rope(q[:P], pos[:P], g.rope_theta), fd_oracle.rope(k[:P], pos[:P], g.rope_theta),
+                        v[:P], causal=True)
+            assert np.max(np.abs(got[:P] - pre)) <= 1e-12, w.name
+
+
 def pin_single_view_is_plain_causal():
     """With one view the streaming mask is plain causal attention; queries are the last T tokens."""
     w = Workload(103, "one view", Geometry(1, 3, 6, 4, 2, 1, 8, 8, 50.0, dtype=synth.F32),
@@ -311,6 +336,7 @@ ALL_PINS = [
     pin_shift_invariance,
     pin_sdpa_special_case,
     pin_streaming_equals_full_recompute,
+    pin_full_window_is_sdpa_causal,
     pin_single_view_is_plain_causal,
     pin_closed_forms,
     pin_mask_leak,
