@@ -215,7 +215,7 @@ def main():
     mean = lambda a: sum(a) / len(a)
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
-    v16_us = graph_ms_per_step = None
+    v16_us = graph_ms_per_step = prefill_us = None
     F = g.n_frames
     if not args.core_only:
         # verify with 16-token draft blocks (64 query rows per kv head)
@@ -237,6 +237,23 @@ def main():
             if rep_i > 0:   # the first sweep is a warm-up
                 v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
         v16_us = sum(v16_ms) / len(v16_ms) * 1e3
+
+        # cold-start (non-streaming) prefill: every window row a query, same mask
+        pws = torch.empty(fd.prefill_workspace_bytes(g), dtype=torch.uint8, device=dev)
+        qw = [rnd(g.window, g.n_q_heads, g.head_dim) for _ in range(L)]
+        ow = [torch.empty(g.window, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
+        pf_ms = []
+        for rep_i in range(2):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+            ev[0].record()
+            for l in range(L):
+                fd.prefill_attn(g, qw[l], kc[l], vc[l], t16, ow[l], pws)
+                ev[l + 1].record()
+            torch.cuda.synchronize()
+            if rep_i > 0:
+                pf_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
+        prefill_us = sum(pf_ms) / len(pf_ms) * 1e3
+        del qw, ow, pws
 
         # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
         # kernel argument depending on the newest frame only through it
@@ -267,6 +284,7 @@ def main():
     flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
     vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
                     + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+    flops_prefill = 4 * g.head_dim * g.n_q_heads * (g.window * (g.window + 1) // 2)
     b16 = 16
     v16bytes_layer = ((g.window + n_tail + b16) * g.n_kv_heads * g.head_dim * esz * 2
                       + b16 * g.n_q_heads * g.head_dim * esz + b16 * g.n_q_heads * g.head_dim * 4)
@@ -322,6 +340,13 @@ def main():
             "gbs": round(v16bytes_layer / (v16_us * 1e-6) / 1e9, 1),
             "frac": round(v16bytes_layer / (v16_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "note": "16-token draft block, 64 query rows per kv head"},
+        "prefill": None if prefill_us is None else {
+            "us_per_call": round(prefill_us, 2),
+            "achieved_tflops": round(flops_prefill / (prefill_us * 1e-6) / 1e12, 2),
+            "frac": round(flops_prefill / (prefill_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "stream_over_prefill_time": round(att_us / prefill_us, 4),
+            "stream_over_prefill_flops": round(flops_layer / flops_prefill, 4),
+            "note": "cold-start prefill of all 4,608 window rows (fd_prefill_attn) beside the streaming call"},
         "graph": None if graph_ms_per_step is None else {
             "ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
             "graphs": F, "launches_per_step": L * 6,

@@ -146,6 +146,33 @@ int fd_stream_attn(const fd_geom* g, const void* q_new,
                    int64_t newest_frame, void* out, void* ws, size_t ws_bytes,
                    void* hip_stream);
 
+/* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every
+ * window row's queries rotated (fp16), the key-tile table and fp32 partial results of
+ * frames whose key range is split between workgroups.  0 on invalid geometry or fp32
+ * inputs.  The size depends on the geometry only.                                   */
+size_t fd_prefill_workspace_bytes(const fd_geom* g);
+
+/* Non-streaming (cold-start) prefill: every token of the window is a query, under the same
+ * mask (README technique list, "Streaming inference": streaming prefills the newest frame
+ * only and reuses the rest; the first window of a stream has nothing to reuse.  Technical
+ * Summary, Methodology 1, "Token Layout").
+ *   q_win  : [W][Hq][D] bf16, pre-RoPE, in cache-row order: row x is the token held in cache
+ *            row x (rows [0, P) the prefix; row P + (v*F + s)*T + i token i of the frame in
+ *            view v's ring slot s), at the position fd_key_position gives for that row.
+ *   k_cache, v_cache : as for fd_stream_attn (window at newest_frame).
+ *   out    : [W][Hq][D] out_dtype, cache-row order.
+ *   ws     : device workspace of ws_bytes >= fd_prefill_workspace_bytes(g); no initial
+ *            contents required; calls that share one workspace must not overlap.
+ *   The token in row x sees every key at a position <= its own: prefix tokens the prefix
+ *   up to themselves; a token of view v's frame of age j the prefix, every frame of views
+ *   < v, view v's frames older than j and its own frame up to itself.  For the newest
+ *   frames this is fd_stream_attn's output.  bf16 inputs only (FD_ERR_DTYPE otherwise);
+ *   newest_frame >= F-1.                                                              */
+int fd_prefill_attn(const fd_geom* g, const void* q_win,
+                    const void* k_cache, const void* v_cache,
+                    int64_t newest_frame, void* out, void* ws, size_t ws_bytes,
+                    void* hip_stream);
+
 /* Bytes of workspace fd_verify_attn needs for blocks of up to blk_len tokens
  * (any n_tail with n_tail + blk_len <= tail_cap): fp32 (m, l, O) partials per (kv head,
  * 32-row block of query rows, key split); 0 on invalid arguments.                  */

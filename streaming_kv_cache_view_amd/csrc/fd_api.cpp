@@ -50,6 +50,10 @@ fd::KParams make_params(const fd_geom* g, int64_t t) {
   p.TBW = 4 / p.HPW;
   p.n_hsub = p.G / p.HPW;
   p.nqb = fd::ceil_div(p.T, 32 * p.TBW);
+  p.qmode = 0;   // streaming: one segment per view (its newest frame)
+  p.seg0 = 0;
+  p.nseg = p.V;
+  p.qtok = p.T;
   p.pos_base = g->pos_base;
   p.t = t;
   p.sm_scale_log2 = float(1.4426950408889634 / std::sqrt(double(p.D)));
@@ -108,8 +112,32 @@ size_t fd_stream_workspace_bytes(const fd_geom* g) {
   if (g->in_dtype != FD_BF16) return krot;
   const fd::KParams p = make_params(g, g->n_frames - 1);
   const int n_rb = p.Hkv * p.n_hsub * p.nqb;
-  return fd::align256(krot) + fd::stream_qrot_bytes(p.V, p.T, p.Hq, p.D) + fd::stream_tiles_bytes(p.P, p.T, p.V, p.F) +
-         fd::stream_partial_bytes(n_rb, p.V, p.D);
+  return fd::align256(krot) + fd::stream_qrot_bytes(p.V * p.T, p.Hq, p.D) +
+         fd::stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + fd::stream_partial_bytes(n_rb, p.V, p.D);
+}
+
+size_t fd_prefill_workspace_bytes(const fd_geom* g) {
+  if (check_geom(g) != FD_OK || g->in_dtype != FD_BF16) return 0;
+  const fd::KParams p = make_params(g, g->n_frames - 1);
+  const size_t krot = size_t(p.Hkv) * p.W * p.D * 2;
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;   // the frame segments' row blocks (the prefix's need no partials)
+  return fd::align256(krot) + fd::stream_qrot_bytes(p.W, p.Hq, p.D) +
+         fd::stream_tiles_bytes(1, p.P, p.T, p.V, p.F) + fd::stream_partial_bytes(n_rb, p.V * p.F, p.D);
+}
+
+int fd_prefill_attn(const fd_geom* g, const void* q_win, const void* k_cache, const void* v_cache,
+                    int64_t newest_frame, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (g->in_dtype != FD_BF16) return FD_ERR_DTYPE;
+  if (!q_win || !k_cache || !v_cache || !out) return FD_ERR_NULL;
+  if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
+  if (!ws || ws_bytes < fd_prefill_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  if (!aligned16(q_win) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
+    return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, newest_frame);
+  p.qmode = 1;
+  return fd::launch_prefill(p, q_win, k_cache, v_cache, out, ws, hip_stream);
 }
 
 int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,

@@ -27,7 +27,15 @@ struct KParams {
   int32_t HPW;        // query heads per workgroup (min(G, 4))
   int32_t TBW;        // 32-token query blocks per workgroup (4 / HPW)
   int32_t n_hsub;     // G / HPW
-  int32_t nqb;        // ceil(T / (32*TBW))
+  int32_t nqb;        // ceil(qtok / (32*TBW))
+  // query segments of the bf16 attention kernel: a segment is the query tokens of one frame
+  // (or of the prefix), with one key-tile sequence
+  int32_t qmode;      // 0 streaming: segment v = view v's newest frame (queries [V*T][Hq][D]);
+                      // 1 full window: segment v*F + j = view v's frame of age j, segment V*F =
+                      //   the prefix (queries [W][Hq][D] in cache-row order)
+  int32_t seg0;       // first segment of this launch
+  int32_t nseg;       // segments (and chunks) per row block of this launch
+  int32_t qtok;       // query tokens per segment of this launch (T, or P for the prefix)
   // verify
   int32_t n_tail, B, nblk, n_split;
   int32_t n_rb;       // 32-row blocks of the G*B verify query rows
@@ -61,24 +69,33 @@ constexpr size_t kVerifyWsHeader = 256;
 // chunk): a chunk's first job may continue a view, its last may be continued.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
-// rotated, scaled queries (fp16, [V*T][Hq][D]) after the rotated keys
-inline size_t stream_qrot_bytes(int V, int T, int Hq, int D) { return align256(size_t(V) * T * Hq * D * 2); }
-// tile table of the attention kernel (int2 per tile of every view's key sequence, the
-// diagonal at full length), between the queries and the partials
-inline size_t stream_tiles_bytes(int P, int T, int V, int F) {
+// rotated, scaled queries (fp16, [rows][Hq][D]) after the rotated keys: rows = V*T (streaming)
+// or W (full window)
+inline size_t stream_qrot_bytes(int rows, int Hq, int D) { return align256(size_t(rows) * Hq * D * 2); }
+// tile table of the attention kernel: an int2 per tile of every segment's key sequence (the
+// diagonal at full length), between the queries and the partials.  Segment of frame age j of
+// view v: prefix, the v*F + j earlier frames, the diagonal; the prefix segment: its tiles.
+inline size_t stream_tiles_bytes(int qmode, int P, int T, int V, int F) {
   const size_t nP = (size_t(P) + 63) / 64, tps = (size_t(T) + 63) / 64;
   size_t n = 0;
-  for (int v = 0; v < V; ++v) n += nP + (size_t(v) * F + F - 1) * tps + tps;
+  if (qmode == 0) {
+    for (int v = 0; v < V; ++v) n += nP + (size_t(v) * F + F - 1) * tps + tps;
+  } else {
+    for (int sg = 0; sg < V * F; ++sg) n += nP + size_t(sg) * tps + tps;
+    n += nP;
+  }
   return align256(n * 8);
 }
-inline size_t stream_partial_bytes(int n_rb, int V, int D) {
-  return size_t(n_rb) * V * 2 * stream_partial_words(D) * sizeof(float);
+inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
+  return size_t(n_rb) * nseg * 2 * stream_partial_words(D) * sizeof(float);
 }
 
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
                   int slot, void* stream);
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,
                   void* out, void* ws, void* stream);
+int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
+                   void* stream);
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb,
                   void* kc, void* vc, void* out, void* ws, void* stream);
 

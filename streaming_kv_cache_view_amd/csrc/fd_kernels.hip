@@ -328,13 +328,16 @@ struct TileInfo {
 };
 
 // Tile table of the streaming kernel (bf16 path), written once per call by the rotation
-// pass.  View v's key sequence is its prefix tiles, the full frames of views 0..v (view v's
-// newest slot excluded, slots in index order), then view v's newest frame (the diagonal,
-// masked per token); a row block whose tokens end early uses a prefix of the diagonal.  Entry
-// (v, t) = {first key row, len | diag << 7 | (first key's token within its segment) << 8}:
-// key rows index the rotated window and the cache alike.
+// pass, one key-tile sequence per query segment.  A segment is the queries of one frame: in a
+// streaming call view v's newest frame, in a full-window call every frame (view v, age j) and
+// the prefix.  Frame (v, j)'s sequence is the prefix tiles, every frame of views < v, view
+// v's frames older than j (in age order), then its own frame (the diagonal, masked per
+// token); the prefix segment's is the prefix tiles, masked per token.  A row block whose
+// tokens end early uses a prefix of the diagonal.  Entry (segment, t) = {first key row,
+// len | diag << 7 | (first key's token within its segment) << 8}: key rows index the
+// rotated window and the cache alike.
 struct StreamTiles {
-  int nP, tps, ndmax, V, F;
+  int nP, tps, ndmax, V, F, qmode;
   __device__ explicit StreamTiles(const KParams& p) {
     constexpr int TK = kTileKeys;
     nP = (p.P + TK - 1) / TK;
@@ -342,36 +345,70 @@ struct StreamTiles {
     ndmax = tps;
     V = p.V;
     F = p.F;
+    qmode = p.qmode;
   }
-  __device__ int view_len(int u) const { return nP + (u * F + F - 1) * tps + ndmax; }
-  __device__ int offset(int v) const {   // first entry of view v
+  // segment sg: the view v and frame age j of its queries (j < 0: the prefix segment)
+  __device__ void seg(int sg, int& v, int& j) const {
+    if (qmode == 0) {
+      v = sg;
+      j = F - 1;
+    } else if (sg < V * F) {
+      v = sg / F;
+      j = sg - v * F;
+    } else {
+      v = 0;
+      j = -1;
+    }
+  }
+  __device__ int segments() const { return qmode == 0 ? V : V * F + (nP > 0 ? 1 : 0); }
+  __device__ int view_len(int sg) const {
+    int v, j;
+    seg(sg, v, j);
+    return j < 0 ? nP : nP + (v * F + j) * tps + ndmax;
+  }
+  __device__ int offset(int sg) const {   // first entry of segment sg
     int o = 0;
-    for (int u = 0; u < v; ++u) o += view_len(u);
+    for (int u = 0; u < sg; ++u) o += view_len(u);
     return o;
   }
-  __device__ int2 desc(const KParams& p, int v, int t) const {
+  // ring slot of the frame of age a (age F-1 = the newest, in slot s_new)
+  __device__ static int slot_of_age(const KParams& p, int a) { return (p.s_new + 1 + a) % p.F; }
+  // first query row of segment sg: [V*T] rows (streaming) or cache-row order [W] (full window)
+  __device__ int qrow0(const KParams& p, int sg) const {
+    int v, j;
+    seg(sg, v, j);
+    if (qmode == 0) return v * p.T;
+    return j < 0 ? 0 : p.P + (v * F + slot_of_age(p, j)) * p.T;
+  }
+  __device__ int2 desc(const KParams& p, int sg, int t) const {
     constexpr int TK = kTileKeys;
+    int v, j;
+    seg(sg, v, j);
     int row0, seglen, k, diag = 0;
-    if (t < nP) {   // prefix
+    if (j < 0) {   // the prefix segment: prefix tiles, causal among prefix tokens
+      row0 = 0;
+      seglen = p.P;
+      k = t;
+      diag = 1;
+    } else if (t < nP) {   // prefix
       row0 = 0;
       seglen = p.P;
       k = t;
     } else {
-      const int nfull = v * F + F - 1;
+      const int nfull = v * F + j;   // every frame of views < v, then view v's older frames
       const int f = min((t - nP) / tps, nfull);
       k = t - nP - f * tps;
       int u, sl;
-      if (f == nfull) {   // view v's newest frame
+      if (f == nfull) {   // the queries' own frame: the diagonal
         u = v;
-        sl = p.s_new;
+        sl = slot_of_age(p, j);
         diag = 1;
       } else if (f < v * F) {
         u = f / F;
         sl = f - u * F;
       } else {
         u = v;
-        const int j = f - v * F;
-        sl = j < p.s_new ? j : j + 1;
+        sl = slot_of_age(p, f - v * F);   // age f - v*F < j
       }
       row0 = p.P + (u * F + sl) * p.T;
       seglen = p.T;
@@ -426,11 +463,12 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   const int rr = tid / CH, c = tid % CH;
   if (tiles && blockIdx.x == 0 && blockIdx.y == 0) {   // the attention kernel's tile table
     const StreamTiles tt(p);
-    for (int v = 0, o = 0; v < p.V; o += tt.view_len(v), ++v)
-      for (int t = tid; t < tt.view_len(v); t += 256) tiles[o + t] = tt.desc(p, v, t);
+    for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
+      for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
   }
   if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token tg, head kvh*G + hh)
-    const int G = p.G, NQ = p.V * p.T * G, qr0 = (blockIdx.x - nkb) * ROWS;
+    // streaming: the newest frames' rows [V*T]; full window: every window row [W]
+    const int G = p.G, NQ = (p.qmode == 0 ? p.V * p.T : p.W) * G, qr0 = (blockIdx.x - nkb) * ROWS;
     const float sc = p.sm_scale_log2;
     double frev[E];   // frequencies in revolutions per position
 #pragma unroll
@@ -441,7 +479,8 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       if (r >= NQ || (ROWS < RPP && rr >= ROWS)) continue;
       const int tg = r / G, hh = r - tg * G;
       const int v = tg / p.T, i = tg - v * p.T;
-      const double pos = static_cast<double>(p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + i);
+      const double pos = static_cast<double>(
+          p.qmode == 0 ? p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + i : row_pos(p, tg));
       const int64_t off = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hh) * D;
       float x1[E], x2[E];
       In::unpack(ld16(q + off + E * c), x1);
@@ -949,23 +988,33 @@ struct StageMap {
 static_assert(StageMap<128>::check() && StageMap<64>::check(), "whole-tile staging offsets");
 
 // Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
-// HPW heads x TBW 32-token blocks of one kv head and head subset).  For each view v its tile
-// sequence has view_tiles(v) tiles; the row block's views are laid end to end in the order
-// V-1, 0, V-2, 1, ... (long and short alternate) and the ntot tiles are cut into V chunks,
-// chunk c = [bnd(c), bnd(c+1)).  Every view has at least one tile, so no chunk is empty.
+// HPW heads x TBW 32-token blocks of one kv head and head subset).  The launch covers nseg
+// query segments (StreamTiles; in a streaming call the views); for each the row block has a
+// tile sequence of view_tiles tiles.  They are laid end to end in the order nseg-1, 0,
+// nseg-2, 1, ... (long and short alternate) and the ntot tiles are cut into nseg chunks,
+// chunk c = [bnd(c), bnd(c+1)).  Every segment has at least one tile, so no chunk is empty.
 struct StreamSplit {
-  int nP, tps, ndiag, V, F, ntot;
+  int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf;
   __device__ StreamSplit(const KParams& p, int qb) {
     constexpr int TK = kTileKeys;
     nP = (p.P + TK - 1) / TK;
     tps = (p.T + TK - 1) / TK;
-    ndiag = (min(p.T, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
-    V = p.V;
+    ndiag = (min(p.qtok, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
+    V = p.nseg;   // segments of this launch: the "views" of a row block
     F = p.F;
+    seg0 = p.seg0;
+    qmode = p.qmode;
+    vf = p.V * p.F;
     ntot = 0;
     for (int u = 0; u < V; ++u) ntot += view_tiles(u);
   }
-  __device__ int view_tiles(int u) const { return nP + (u * F + F - 1) * tps + ndiag; }
+  // tiles of segment seg0 + u for this row block (StreamTiles: frame (v, j) of a full window
+  // is segment v*F + j, after v*F + j earlier frames)
+  __device__ int view_tiles(int u) const {
+    const int sg = seg0 + u;
+    if (qmode == 0) return nP + (sg * F + F - 1) * tps + ndiag;
+    return sg < vf ? nP + sg * tps + ndiag : ndiag;
+  }
   __device__ int order(int oi) const { return (oi & 1) ? oi / 2 : V - 1 - oi / 2; }
   __device__ int bnd(int c) const { return static_cast<int>((static_cast<int64_t>(c) * ntot) / V); }
   // start of view v in the end-to-end order
@@ -991,11 +1040,12 @@ struct StreamSplit {
 // chunk's first job (which starts at bnd(c)), 1 for its last.
 template <int D>
 __device__ inline float* stream_slot(float* part, const KParams& p, int rbi, int c, int which) {
-  return part + (static_cast<int64_t>(rbi * p.V + c) * 2 + which) * stream_partial_words(D);
+  return part + (static_cast<int64_t>(rbi * p.nseg + c) * 2 + which) * stream_partial_words(D);
 }
 
-// Merge of the views whose tiles were split between chunks: two workgroups per (row block,
-// view), 64 rows each; views held whole by one chunk were written by the attention kernel.
+// Merge of the segments (views) whose tiles were split between chunks: two workgroups per
+// (row block, segment), 64 rows each; segments held whole by one chunk were written by the
+// attention kernel.
 // For the pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
 // sum_i 2^(m_i - M) l_i with M = max_i m_i (the online-softmax merge of disjoint key sets),
 // taken in batches of up to 4 pieces whose loads are all in flight together.  A slot holds
@@ -1005,7 +1055,7 @@ template <int D>
 __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
   constexpr int DQ = D / 8, MAXP = 4;
-  // blockIdx.x = ((half*V + v)*(n_hsub*nqb) + hsub*nqb + qb)*Hkv + kvh: like the attention
+  // blockIdx.x = ((half*nseg + v)*(n_hsub*nqb) + hsub*nqb + qb)*Hkv + kvh: like the attention
   // kernel's, consecutive workgroups go round-robin to the XCDs with the kv head fastest, so
   // (for Hkv a multiple of 8) a row block's partials are merged on the XCD whose L2 they were
   // written through
@@ -1016,7 +1066,7 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
   bid /= p.nqb;
   const int hsub = bid % p.n_hsub;
   bid /= p.n_hsub;
-  const int v = bid % p.V, half = bid / p.V;
+  const int v = bid % p.nseg, half = bid / p.nseg;   // segment p.seg0 + v
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
   const StreamSplit sp(p, qb);
   const int sv = sp.start(v), nv = sp.view_tiles(v);
@@ -1025,7 +1075,7 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
   const int tid = threadIdx.x, row = 64 * half + (tid >> 3), d0 = (tid & 7) * DQ;
   const int ww = row >> 5;
   const int tok = qb * 32 * p.TBW + 32 * (ww / p.HPW) + (row & 31);
-  if (tok >= p.T) return;
+  if (tok >= p.qtok) return;
   const int which_cf = sv > sp.bnd(cf) ? 1 : 0;
   float M = -INFINITY, L = 0.f;
   float acc[DQ];
@@ -1067,7 +1117,7 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
   }
   const float inv = 1.f / L;
   const int head = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-  const int64_t obase = (static_cast<int64_t>(v * p.T + tok) * p.Hq + head) * D + d0;
+  const int64_t obase = (static_cast<int64_t>(StreamTiles(p).qrow0(p, p.seg0 + v) + tok) * p.Hq + head) * D + d0;
 #pragma unroll
   for (int i = 0; i < DQ; i += 4)
     store_out4(out, p.out_bf16, obase + i, f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv});
@@ -1137,15 +1187,15 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   // ---- tile sequence of view v: StreamTiles (its table, tiles); its length for this row block
   const StreamSplit sp(p, qb);
   const StreamTiles stt(p);
-  // ---- this workgroup's chunk [c0, c1) of the row block's views laid end to end
+  // ---- this workgroup's chunk [c0, c1) of the row block's segments laid end to end
   const int c0 = sp.bnd(chunk), c1 = sp.bnd(chunk + 1);
 
   // LDS swizzles of the K and V tiles (StageMap)
   auto kswz = [](uint32_t r) { return StageMap<D>::kswz(r); };
   auto vswz = [](uint32_t key) { return StageMap<D>::vswz(key); };
-  int vstart = 0;   // start of view v in the end-to-end order
-  for (int oi = 0; oi < p.V; ++oi) {
-  const int v = sp.order(oi);
+  int vstart = 0;   // start of segment v in the end-to-end order
+  for (int oi = 0; oi < p.nseg; ++oi) {
+  const int v = sp.order(oi);   // segment p.seg0 + v of this launch
   const int nv = sp.view_tiles(v);
   const int sv = vstart;
   vstart += nv;
@@ -1174,7 +1224,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   const int ntiles = jb - ja;
   // The job's tiles t = 0 .. ntiles-1 (tile ja + t of view v): group g takes t = g, g+2, ...
   // and keeps tile t in LDS slot t & 3.  Their table entries are read with scalar loads.
-  const int2* jt = tiles + (stt.offset(v) + ja);
+  const int2* jt = tiles + (stt.offset(p.seg0 + v) + ja);
+  const int qrow0 = stt.qrow0(p, p.seg0 + v);   // query / output row of the segment's token 0
 
   // ---- staging of one tile by the group's 256 threads, straight from HBM/L2 into LDS
   // (global_load_lds, 16 bytes per lane; each instruction fills 1 KB of LDS linearly, lane i
@@ -1221,8 +1272,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   // [16u + 8h, 16u + 8h + 8)
   u32x4 qf[NU];
   {
-    const bool valid = my_tok < p.T;
-    const _Float16* src = qrot + (static_cast<int64_t>(v * p.T + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
+    const bool valid = my_tok < p.qtok;
+    const _Float16* src = qrot + (static_cast<int64_t>(qrow0 + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
 #pragma unroll
     for (int u = 0; u < NU; ++u) qf[u] = valid ? ld16(src + 2 * E * u) : u32x4{0u, 0u, 0u, 0u};
   }
@@ -1411,11 +1462,11 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
     const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
     for (int r = tid / TPR; r < 128; r += 512 / TPR) {
       const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-      if (tk >= p.T) continue;
+      if (tk >= p.qtok) continue;
       const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
       const int c = tid % TPR;
       const float* src = rows + r * (D + 4);
-      const int64_t obase = (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
+      const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D;
       if (p.out_bf16) {
         const f32x4 lo = *reinterpret_cast<const f32x4*>(src + 8 * c), hi = *reinterpret_cast<const f32x4*>(src + 8 * c + 4);
         float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -2093,15 +2144,15 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   // after the keys
   const bool b16 = std::is_same<T, bf16>::value;
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
-  int2* tiles = b16 ? reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D))
+  int2* tiles = b16 ? reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D))
                     : nullptr;
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V, p.T, p.Hq, D) +
-                                         stream_tiles_bytes(p.P, p.T, p.V, p.F));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D) +
+                                         stream_tiles_bytes(0, p.P, p.T, p.V, p.F));
   const int nkb = (p.W + 127) / 128, nqk = b16 ? (p.V * p.T * p.G + 127) / 128 : 0;
   hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
                      static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-  const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;
+  const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles);
@@ -2110,6 +2161,48 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
+  }
+  return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+// Full-window (cold-start) prefill, bf16: one rotation pass for the window's keys and every
+// window row's queries, then the attention kernel over the V*F frame segments (and the merge
+// of the segments split between workgroups) and over the prefix segment (one chunk: no
+// split, no merge).
+template <int D>
+int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
+                     hipStream_t st) {
+  using QKT = _Float16;
+  constexpr int RPP = 256 / (D / 2 / Path<bf16>::In::E);
+  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
+  QKT* krot = static_cast<QKT*>(ws);
+  QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
+  int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(tiles) + stream_tiles_bytes(1, p.P, p.T, p.V, p.F));
+  const int nkb = (p.W + 127) / 128, nqk = (p.W * p.G + 127) / 128;
+  hipLaunchKernelGGL((rope_window_kernel<bf16, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const bf16*>(kc), krot, aligned, nkb, static_cast<const bf16*>(q), qrot, tiles);
+  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+  KParams pf = p;   // the frame segments
+  pf.seg0 = 0;
+  pf.nseg = p.V * p.F;
+  pf.qtok = p.T;
+  pf.nqb = ceil_div(p.T, 32 * p.TBW);
+  const int grid = pf.Hkv * pf.n_hsub * pf.nqb * pf.nseg;
+  hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pf, static_cast<const QKT*>(qrot),
+                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, part, tiles);
+  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+  hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, pf, part, out);
+  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+  if (p.P > 0) {
+    KParams pp = p;   // the prefix segment
+    pp.seg0 = p.V * p.F;
+    pp.nseg = 1;
+    pp.qtok = p.P;
+    pp.nqb = ceil_div(p.P, 32 * p.TBW);
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(pp.Hkv * pp.n_hsub * pp.nqb), dim3(512), 0, st, pp,
+                       static_cast<const QKT*>(qrot), static_cast<const QKT*>(krot), static_cast<const bf16*>(vc),
+                       out, part, tiles);
   }
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
@@ -2155,6 +2248,12 @@ int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, 
   }
   return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st)
                     : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st);
+}
+
+int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
+                   void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return p.D == 128 ? launch_prefill_t<128>(p, q, kc, vc, out, ws, st) : launch_prefill_t<64>(p, q, kc, vc, out, ws, st);
 }
 
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb, void* kc,

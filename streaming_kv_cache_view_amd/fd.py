@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
         L.fd_stream_workspace_bytes.argtypes, L.fd_stream_workspace_bytes.restype = [G], sz
         L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn.restype = ctypes.c_int
+        L.fd_prefill_workspace_bytes.argtypes, L.fd_prefill_workspace_bytes.restype = [G], sz
+        L.fd_prefill_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
+        L.fd_prefill_attn.restype = ctypes.c_int
         L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
         L.fd_verify_attn.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
         L.fd_verify_attn.restype = ctypes.c_int
@@ -62,7 +65,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_stream_workspace_bytes",
-           "fd_stream_attn", "fd_verify_workspace_bytes", "fd_verify_attn", "fd_status_str")
+           "fd_stream_attn", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
+           "fd_verify_attn", "fd_status_str")
 
 
 def make_geom(g, out_dtype: str = "f32") -> FdGeom:
@@ -127,6 +131,20 @@ def stream_attn(g, q_new, k_cache, v_cache, newest_frame: int, out, ws, ws_bytes
         ws_bytes = ws.numel() * ws.element_size()
     _check("fd_stream_attn", lib().fd_stream_attn(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_new), _ptr(k_cache), _ptr(v_cache),
+        int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def prefill_workspace_bytes(g) -> int:
+    return lib().fd_prefill_workspace_bytes(ctypes.byref(make_geom(g)))
+
+
+def prefill_attn(g, q_win, k_cache, v_cache, newest_frame: int, out, ws, ws_bytes: int | None = None,
+                 out_dtype: str = "f32", stream=None):
+    """out [W][Hq][D] = cold-start prefill of every window row (cache-row order) q_win [W][Hq][D]."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("fd_prefill_attn", lib().fd_prefill_attn(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(q_win), _ptr(k_cache), _ptr(v_cache),
         int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 

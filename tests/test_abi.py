@@ -150,6 +150,31 @@ def test_call_errors():
         assert fd.lib().fd_status_str(code).decode() != "unknown status"
 
 
+def test_prefill_call_errors():
+    L = fd.lib()
+    g = _g()                                   # bf16 inputs
+    gp = ctypes.byref(g)
+    pws = L.fd_prefill_workspace_bytes(gp)
+    # rotated keys, every window row's rotated queries (W = 8 + 2*4*16 = 136 rows), the tile
+    # table (frame (v, j): prefix + v*F + j earlier frames + diagonal, one 64-key tile each here;
+    # then the prefix segment) and two partial slots per (row block, frame chunk)
+    W = 8 + 2 * 4 * 16
+    align = lambda x: (x + 255) // 256 * 256
+    n_tiles = sum(1 + sg + 1 for sg in range(2 * 4)) + 1
+    n_rb = g.n_kv_heads * 1 * 1
+    assert pws == (align(g.n_kv_heads * W * 64 * 2) + align(W * 4 * 64 * 2) + align(n_tiles * 8)
+                   + n_rb * 8 * 2 * (128 * 64 + 256) * 4)
+    assert L.fd_prefill_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == 0
+    assert L.fd_prefill_attn(ctypes.byref(_g(in_dtype=fd.FD_F32)), FAKE, FAKE, FAKE, 5, FAKE, FAKE, pws,
+                             None) == -3                                        # bf16 only
+    assert L.fd_prefill_attn(gp, None, FAKE, FAKE, 5, FAKE, FAKE, pws, None) == -1
+    assert L.fd_prefill_attn(gp, FAKE, FAKE, FAKE, 5, None, FAKE, pws, None) == -1
+    assert L.fd_prefill_attn(gp, FAKE, FAKE, FAKE, 2, FAKE, FAKE, pws, None) == -4   # window not full
+    assert L.fd_prefill_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, FAKE, pws - 1, None) == -7
+    assert L.fd_prefill_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, None, pws, None) == -7
+    assert L.fd_prefill_attn(gp, MISALIGNED, FAKE, FAKE, 5, FAKE, FAKE, pws, None) == -5
+
+
 def test_workspace_size_covers_largest_block():
     g = synth.CONFIGS[4].geom
     ws = fd.verify_workspace_bytes(g, 8)

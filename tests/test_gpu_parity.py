@@ -261,3 +261,88 @@ def test_verify_edge_geometries(w):
     g = w.geom
     b = max(1, min(32 // (g.n_q_heads // g.n_kv_heads), g.tail_cap))
     check_verify(w, 0, w.first_t, max(0, g.tail_cap - b), b)
+
+
+# ---------------------------------------------------------------------------- cold-start prefill
+def window_queries(w, layer, t):
+    """Queries of every window row in cache-row order [W][Hq][D], and the map cache row ->
+    logical row (prefix, then view 0 oldest..newest, view 1, ...)."""
+    g = w.geom
+    P, T, F = g.prefix_len, g.tok_per_frame, g.n_frames
+    q = np.empty((g.window, g.n_q_heads, g.head_dim), np.float64)
+    logical = np.empty(g.window, np.int64)
+    if P:
+        q[:P] = synth.prefix_q(w, layer)
+        logical[:P] = np.arange(P)
+    slots = fd_oracle.expected_ring_rows(g, t)
+    for v in range(g.n_views):
+        for s, fid in enumerate(slots):
+            r0 = P + (v * F + s) * T
+            j = fid - (t - F + 1)                      # age of the frame (oldest = 0)
+            q[r0: r0 + T] = synth.frame_q(w, layer, v, fid)
+            logical[r0: r0 + T] = P + (v * F + j) * T + np.arange(T)
+    return q, logical
+
+
+def check_prefill(w, layer, t, rows=None, out_dtype="f32"):
+    g = w.geom
+    H.say(f"prefill cfg {w.cfg_id} ({w.name}) layer {layer} t {t}")
+    kc, vc = H.window_caches(w, layer, t)
+    q, logical = window_queries(w, layer, t)
+    ws = torch.empty(fd.prefill_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    out = torch.empty((g.window, g.n_q_heads, g.head_dim),
+                      dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=H.DEV)
+    fd.prefill_attn(g, H.dev(q, g), kc, vc, t, out, ws, out_dtype=out_dtype)
+    got = out.float().cpu().numpy().astype(np.float64)
+    win = fd_oracle.StreamWindow(g, *synth.prefix_kv(w, layer))
+    for f in range(t + 1):
+        for v in range(g.n_views):
+            win.push(v, f, *synth.frame_kv(w, layer, v, f))
+    q_log = np.empty_like(q)
+    q_log[logical] = q
+    kw, vw = win.kv()
+    pos = fd_oracle.window_positions(g, kw.shape[0])
+    sel = np.arange(g.window) if rows is None else np.asarray(rows)
+    want = fd_oracle.attend(q_log[logical[sel]], kw, vw, pos[logical[sel]], pos, g.rope_theta)
+    tol = H.TOL[g.dtype] + (0.02 if out_dtype == "bf16" else 0.0)
+    err = H.max_err(got[sel], want)
+    H.say(f"  {len(sel)} rows: max-abs {err:.3e} (tol {tol})")
+    assert err <= tol
+    return got, kc, vc
+
+
+@pytest.mark.parametrize("t", [3, 6])
+def test_prefill_small(t):
+    """Config 2 shapes: every window row (W = 1,088) against the oracle, at the first full
+    window (slots in frame order) and at a later ring phase."""
+    check_prefill(synth.CONFIGS[2], 0, t)
+
+
+def test_prefill_matches_stream_rows():
+    """The newest frames' rows of a cold-start prefill are the streaming call's output."""
+    w = synth.CONFIGS[2]
+    g = w.geom
+    t = 6
+    got, kc, vc = check_prefill(w, 0, t, rows=[0, 1, 500, 1087])
+    st = H.stream_out(w, 0, kc, vc, t).cpu().numpy()
+    s_new = t % g.n_frames
+    for v in range(g.n_views):
+        r0 = g.prefix_len + (v * g.n_frames + s_new) * g.tok_per_frame
+        err = H.max_err(got[r0: r0 + g.tok_per_frame], st[v * g.tok_per_frame: (v + 1) * g.tok_per_frame])
+        assert err <= 2e-3, (v, err)
+
+
+def test_prefill_backbone_sampled():
+    """Config 3 shapes (W = 4,608 queries over 4,608 keys): sampled rows of every segment."""
+    w = synth.CONFIGS[3]
+    g = w.geom
+    rng = np.random.default_rng(11)
+    rows = np.sort(np.concatenate([rng.choice(g.prefix_len, 24, replace=False),
+                                   g.prefix_len + rng.choice(g.window - g.prefix_len, 104, replace=False),
+                                   [0, g.prefix_len - 1, g.prefix_len, g.window - 1]]))
+    check_prefill(w, 0, w.first_t + 1, rows=rows, out_dtype="bf16")
+
+
+@pytest.mark.parametrize("w", [x for x in EXTRA if x.geom.dtype == synth.BF16], ids=lambda w: w.name)
+def test_prefill_edge_geometries(w):
+    check_prefill(w, 0, w.first_t)
