@@ -189,6 +189,27 @@ def oracle_verify(geom, window: StreamWindow, k_tail, v_tail, q_blk, k_blk, v_bl
 
 
 # ----------------------------------------------------------------------------
+# K/V projection of a new frame (Technical Summary, "5. System Optimizations", "Kernel
+# Fusion": the Q, K, V projections are merged into single kernels; README, "System
+# optimizations": static KV cache).  The projected keys are what the cache stores, before
+# rotary embedding (Methodology 1, "Positional Encoding").
+# ----------------------------------------------------------------------------
+def oracle_kv_projection(x, w_kv, n_kv_heads: int, head_dim: int):
+    """K, V [T][Hkv][D] = x [T][hidden] times the K and V weights.
+
+    w_kv: [2*Hkv*D][hidden], one output feature per row: rows [0, Hkv*D) give K (feature
+    h*D + d is head h, dimension d), the next Hkv*D rows give V.  fp64, pre-RoPE.
+    """
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w_kv, np.float64)
+    n = n_kv_heads * head_dim
+    k = x @ w[:n].T
+    v = x @ w[n: 2 * n].T
+    t = x.shape[0]
+    return k.reshape(t, n_kv_heads, head_dim), v.reshape(t, n_kv_heads, head_dim)
+
+
+# ----------------------------------------------------------------------------
 # The physical cache image after in-order inserts (bit-exact expectation)
 # ----------------------------------------------------------------------------
 def expected_ring_rows(geom, newest_frame: int):

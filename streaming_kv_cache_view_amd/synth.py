@@ -38,6 +38,8 @@ KIND = {
     "Ktail": 5, "Vtail": 6,    # reasoning-token K/V        [R][Hkv][D]
     "Qblk": 7, "Kblk": 8, "Vblk": 9,  # verify block        [B][H*][D]
     "Qpre": 10,                # prefix-token queries (full-window tests only)
+    "Xh": 11,                  # hidden states of a frame's tokens [T][hidden] (projection only)
+    "Wkv": 12,                 # K and V projection weights [2*Hkv*D][hidden] (projection only)
 }
 
 
@@ -175,6 +177,21 @@ def block_qkv(w: Workload, layer: int, blk_len: int):
     return (draw(w, layer, "Qblk", -1, -1, (blk_len, g.n_q_heads, g.head_dim)),
             draw(w, layer, "Kblk", -1, -1, (blk_len, g.n_kv_heads, g.head_dim)),
             draw(w, layer, "Vblk", -1, -1, (blk_len, g.n_kv_heads, g.head_dim)))
+
+
+def frame_hidden(w: Workload, layer: int, view: int, frame: int, hidden: int):
+    """Hidden states [T][hidden] of one frame's tokens (inputs of the K/V projection)."""
+    return draw(w, layer, "Xh", view, frame, (w.geom.tok_per_frame, hidden))
+
+
+def kv_weights(w: Workload, layer: int, hidden: int):
+    """K then V projection weights [2*Hkv*D][hidden] (one output feature per row, as a linear
+    layer stores them), N(0, 1/hidden) so that projected values are about unit scale."""
+    g = w.geom
+    rng = _rng(w.cfg_id, layer, "Wkv", -1, -1)
+    x = rng.standard_normal((2 * g.n_kv_heads * g.head_dim, hidden), dtype=np.float32) * np.float32(
+        1.0 / np.sqrt(hidden))
+    return round_bf16(x) if g.dtype == BF16 else x
 
 
 def new_frames(w: Workload, layer: int, frame: int):

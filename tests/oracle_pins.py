@@ -328,6 +328,27 @@ def pin_verify_sdpa():
     assert err <= 1e-12, err
 
 
+def pin_kv_projection():
+    """Brute-force sums on a tiny case; one-hot hidden states pick out weight columns; the
+    head / dimension split of the output features."""
+    rng = np.random.default_rng(21)
+    t, hidden, hkv, d = 3, 5, 2, 4
+    x = rng.standard_normal((t, hidden))
+    w = rng.standard_normal((2 * hkv * d, hidden))
+    k, v = fd_oracle.oracle_kv_projection(x, w, hkv, d)
+    for i in range(t):
+        for h in range(hkv):
+            for e in range(d):
+                sk = sum(x[i, j] * w[h * d + e, j] for j in range(hidden))
+                sv = sum(x[i, j] * w[hkv * d + h * d + e, j] for j in range(hidden))
+                assert abs(k[i, h, e] - sk) <= 1e-12 and abs(v[i, h, e] - sv) <= 1e-12
+    eye = np.eye(hidden)[:t]
+    k, v = fd_oracle.oracle_kv_projection(eye, w, hkv, d)
+    for i in range(t):
+        assert np.array_equal(k[i].reshape(-1), w[: hkv * d, i])
+        assert np.array_equal(v[i].reshape(-1), w[hkv * d:, i])
+
+
 ALL_PINS = [
     pin_rope_closed_form,
     pin_rope_group_properties,
@@ -343,4 +364,5 @@ ALL_PINS = [
     pin_ring_slots,
     pin_expected_cache_layout,
     pin_verify_sdpa,
+    pin_kv_projection,
 ]
