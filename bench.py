@@ -215,7 +215,7 @@ def main():
     mean = lambda a: sum(a) / len(a)
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
-    v16_us = graph_ms_per_step = prefill_us = None
+    v16_us = graph_ms_per_step = prefill_us = kvproj_us = None
     F = g.n_frames
     if not args.core_only:
         # verify with 16-token draft blocks (64 query rows per kv head)
@@ -254,6 +254,25 @@ def main():
                 pf_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
         prefill_us = sum(pf_ms) / len(pf_ms) * 1e3
         del qw, ow, pws
+
+        # K/V projection of the new frames with the ring-slot insert as its epilogue
+        hidden = g.n_q_heads * g.head_dim
+        xs = [rnd(g.n_new, hidden) for _ in range(L)]
+        wkv = [(torch.randn(2 * g.n_kv_heads * g.head_dim, hidden, generator=gen, device=dev)
+                / hidden ** 0.5).to(torch.bfloat16) for _ in range(L)]
+        kp_ms = []
+        for rep_i in range(2):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+            ev[0].record()
+            for l in range(L):
+                fd.kv_project_insert(g, xs[l], wkv[l], kc[l], vc[l], t16)
+                ev[l + 1].record()
+            torch.cuda.synchronize()
+            if rep_i > 0:
+                kp_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
+        kvproj_us = sum(kp_ms) / len(kp_ms) * 1e3
+        kvproj_flops = 2 * g.n_new * (2 * g.n_kv_heads * g.head_dim) * hidden
+        del xs, wkv
 
         # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
         # kernel argument depending on the newest frame only through it
@@ -347,6 +366,12 @@ def main():
             "stream_over_prefill_time": round(att_us / prefill_us, 4),
             "stream_over_prefill_flops": round(flops_layer / flops_prefill, 4),
             "note": "cold-start prefill of all 4,608 window rows (fd_prefill_attn) beside the streaming call"},
+        "kv_projection": None if kvproj_us is None else {
+            "us_per_call": round(kvproj_us, 2),
+            "achieved_tflops": round(kvproj_flops / (kvproj_us * 1e-6) / 1e12, 2),
+            "frac": round(kvproj_flops / (kvproj_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "fd_kv_project_insert: 1,024 tokens x hidden 4,096 -> K and V (8 heads x 128), "
+                    "written into the ring slot"},
         "graph": None if graph_ms_per_step is None else {
             "ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
             "graphs": F, "launches_per_step": L * 6,

@@ -118,6 +118,21 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache,
                        const void* k_new, const void* v_new,
                        int64_t frame_idx, void* hip_stream);
 
+/* Project the new frame of every view to K and V and insert them into its ring slot, in one
+ * kernel (Technical Summary, "5. System Optimizations", "Kernel Fusion": the Q, K, V
+ * projections are merged into single kernels; here the K/V projection's epilogue is the
+ * insert of the Token Layout passage).  bf16 inputs only.
+ *   x_new  : [V*T][hidden] bf16, row v*T + i the hidden state of token i of view v's new frame.
+ *   w_kv   : [2*Hkv*D][hidden] bf16, one output feature per row (as a linear layer stores
+ *            it): rows [0, Hkv*D) the K projection (feature h*D + d = head h, dimension d),
+ *            rows [Hkv*D, 2*Hkv*D) the V projection.
+ *   Writes k_cache/v_cache rows P + (v*F + frame_idx mod F)*T + i, every head: the sums in
+ *   fp32, rounded to bf16 (nearest even), pre-RoPE.  No other cache row is touched.
+ *   hidden: a multiple of 64 (FD_ERR_GEOM otherwise; also when x or w exceed 2 GiB).
+ *   frame_idx >= 0.                                                                      */
+int fd_kv_project_insert(const fd_geom* g, const void* x_new, const void* w_kv, int32_t hidden,
+                         void* k_cache, void* v_cache, int64_t frame_idx, void* hip_stream);
+
 /* Bytes of workspace fd_stream_attn needs: the window's keys rotated at their current
  * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); for bf16 inputs
  * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements), a

@@ -105,6 +105,23 @@ int fd_kv_insert_frame(const fd_geom* g, void* k_cache, void* v_cache, const voi
                            hip_stream);
 }
 
+int fd_kv_project_insert(const fd_geom* g, const void* x_new, const void* w_kv, int32_t hidden, void* k_cache,
+                         void* v_cache, int64_t frame_idx, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (g->in_dtype != FD_BF16) return FD_ERR_DTYPE;
+  if (!x_new || !w_kv || !k_cache || !v_cache) return FD_ERR_NULL;
+  const int64_t M = int64_t(g->n_views) * g->tok_per_frame, N = 2 * int64_t(g->n_kv_heads) * g->head_dim;
+  // k in chunks of 64; 32-bit byte offsets into x and w
+  if (hidden < 64 || hidden % 64 != 0 || N % 128 != 0 || M * hidden * 2 >= (int64_t(1) << 31) ||
+      N * hidden * 2 >= (int64_t(1) << 31))
+    return FD_ERR_GEOM;
+  if (frame_idx < 0) return FD_ERR_FRAME;
+  if (!aligned16(x_new) || !aligned16(w_kv) || !aligned16(k_cache) || !aligned16(v_cache)) return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, frame_idx);
+  return fd::launch_kv_project(p, hidden, int(frame_idx % g->n_frames), x_new, w_kv, k_cache, v_cache, hip_stream);
+}
+
 size_t fd_stream_workspace_bytes(const fd_geom* g) {
   if (check_geom(g) != FD_OK) return 0;
   const size_t window = size_t(g->prefix_len) + size_t(g->n_views) * g->n_frames * g->tok_per_frame;

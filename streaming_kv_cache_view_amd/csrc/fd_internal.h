@@ -96,6 +96,8 @@ int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, 
                   void* out, void* ws, void* stream);
 int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                    void* stream);
+int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, const void* w, void* kc, void* vc,
+                      void* stream);
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb,
                   void* kc, void* vc, void* out, void* ws, void* stream);
 

@@ -210,6 +210,18 @@ __device__ inline uint32_t lds_addr(const void* p) {
 __device__ inline void g2lds16_async(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(gbase), "{m0}"(lds) : "memory");
 }
+// A wave-uniform pointer in scalar registers.  A vector instruction (v_readfirstlane) writes
+// them, and a vector memory instruction that reads an SGPR needs five wait states after such
+// a write; the compiler does not see the reads inside the inline-assembly loads above, so the
+// wait states are issued here, tied to the registers.
+template <typename T>
+__device__ inline T* uni_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  asm volatile("s_nop 4" : "+s"(lo), "+s"(hi));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 // The same with an instruction offset OFF, which the hardware adds to both addresses: the
 // lane's global byte gbase + voff + OFF lands at LDS lds + OFF + 16i.
 template <int OFF>
@@ -1489,6 +1501,106 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 }
 
 // ---------------------------------------------------------------------------------------
+// K/V projection of the new frames with the ring-slot insert as its epilogue (bf16).
+// C[m][n] = sum_k X[m][k] W[n][k]: m = v*T + i the token i of view v's new frame (X
+// [V*T][hidden]), n the output feature (W [2*Hkv*D][hidden], one feature per row as a linear
+// layer stores it): n < Hkv*D is K head n/D, dimension n%D; the next Hkv*D are V.  The fp32
+// sums are rounded to bf16 and written pre-RoPE straight into the cache rows of ring slot s:
+// row P + (v*F + s)*T + i of head n/D (Technical Summary, 5. System Optimizations, "Kernel
+// Fusion"; Methodology 1, "Token Layout").
+// Workgroup tile 64 (m) x 128 (n), four waves of 32 x 64, k in chunks of 64; both tiles go
+// straight to LDS (direct loads, double-buffered), rows of 64 bf16 (128 B, eight 16-byte
+// chunks) with chunk c of row r at position c ^ ((r >> 1) & 7), so the 16 rows one operand
+// read touches land in 16 distinct bank groups.  v_mfma_f32_32x32x16_bf16: A = 32 rows of X,
+// B = 32 rows of W (both k-contiguous).
+// ---------------------------------------------------------------------------------------
+constexpr int kPM = 64, kPN = 128, kPK = 64;
+__device__ inline uint32_t proj_swz(uint32_t r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hidden, int slot,
+                                                         const bf16* __restrict__ x, const bf16* __restrict__ w,
+                                                         bf16* __restrict__ kc, bf16* __restrict__ vc) {
+  constexpr int ROWB = kPK * 2;                 // 128 bytes per staged row
+  constexpr int ABYTES = kPM * ROWB, BBYTES = kPN * ROWB, STAGE = ABYTES + BBYTES;   // 8 + 16 KB
+  __shared__ __attribute__((aligned(16))) unsigned char buf[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w4 = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int M = p.V * p.T, N = 2 * p.Hkv * p.D;
+  const int nblk = N / kPN;
+  const int m0 = (blockIdx.x / nblk) * kPM, n0 = (blockIdx.x % nblk) * kPN;
+  const int wm = (w4 >> 1) * 32, wn = (w4 & 1) * 64;   // this wave's 32 x 64 sub-tile
+  uint32_t ln = lane;
+  asm volatile("" : "+v"(ln));
+  // direct loads: instruction j of the workgroup fills staged rows 8j .. 8j+7 (1 KB); lane i
+  // takes row 8j + i/8 and fetches its chunk (i%8) ^ swz(row).  A: 8 instructions (two per
+  // wave), B: 16 (four per wave).  Global offsets per lane are fixed; the k chunk moves the base.
+  const int64_t rowb = static_cast<int64_t>(hidden) * 2;
+  uint32_t aoff[2], boff[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t r = 8 * (2 * w4 + q) + ln / 8;
+    const int mr = min(m0 + static_cast<int>(r), M - 1);   // rows past M repeat the last
+    aoff[q] = static_cast<uint32_t>(mr) * static_cast<uint32_t>(rowb) + (((ln % 8) ^ proj_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t r = 8 * (4 * w4 + q) + ln / 8;
+    boff[q] = static_cast<uint32_t>(n0 + r) * static_cast<uint32_t>(rowb) + (((ln % 8) ^ proj_swz(r)) << 4);
+  }
+  const uint32_t lds0 = lds_addr(buf);
+  auto stage = [&](int kc_, int sb) {
+    const unsigned char* xa = uni_ptr(reinterpret_cast<const unsigned char*>(x) + static_cast<int64_t>(kc_) * ROWB);
+    const unsigned char* wb = uni_ptr(reinterpret_cast<const unsigned char*>(w) + static_cast<int64_t>(kc_) * ROWB);
+    const uint32_t la = lds0 + sb * STAGE, lb = la + ABYTES;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) g2lds16_async(xa, aoff[q], __builtin_amdgcn_readfirstlane(la + (2 * w4 + q) * 1024));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) g2lds16_async(wb, boff[q], __builtin_amdgcn_readfirstlane(lb + (4 * w4 + q) * 1024));
+  };
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  const int nk = hidden / kPK;
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  wg_barrier();
+  for (int kk = 0; kk < nk; ++kk) {
+    const int sb = kk & 1;
+    if (kk + 1 < nk) stage(kk + 1, sb ^ 1);   // the other buffer was last read before the barrier
+    const unsigned char* A = buf + sb * STAGE;
+    const unsigned char* B = A + ABYTES;
+#pragma unroll
+    for (int u = 0; u < kPK / 16; ++u) {   // 16-wide k steps: chunk 2u + h
+      const uint32_t ra = wm + l32;
+      const u32x4 a = ld16(A + ra * ROWB + (((2 * u + h) ^ proj_swz(ra)) << 4));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t rb = wn + 32 * nb + l32;
+        const u32x4 b = ld16(B + rb * ROWB + (((2 * u + h) ^ proj_swz(rb)) << 4));
+        acc[nb] = BF16Ops::mma(a, b, acc[nb]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // chunk kk+1 has landed
+    wg_barrier();
+  }
+
+  // epilogue: lane l32 holds feature n = n0 + wn + 32nb + l32 of tokens m = m0 + wm + 8(i/4)
+  // + 4h + i%4; 32 lanes write 32 consecutive dimensions of one head (64 contiguous bytes)
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + wn + 32 * nb + l32;
+    const int kv = n / (p.Hkv * p.D), hd = (n / p.D) % p.Hkv, d = n % p.D;
+    bf16* dst = kv == 0 ? kc : vc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = m0 + wm + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (m >= M) continue;
+      const int v = m / p.T, ti = m - v * p.T;
+      const int64_t row = p.P + static_cast<int64_t>(v * p.F + slot) * p.T + ti;
+      dst[(static_cast<int64_t>(hd) * p.S_cap + row) * p.D + d] = static_cast<bf16>(acc[nb][i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Verify, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block token b), in
 // 32-row MFMA blocks, one workgroup per (kv head, row block, split).  Keys are numbered by cache row x: window rows [0, W), reasoning rows
 // [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk and copied into
@@ -2236,6 +2348,16 @@ int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* k
   hipLaunchKernelGGL(insert_kernel, dim3(grid, 2), dim3(256), 0, static_cast<hipStream_t>(stream), p, chunks,
                      static_cast<const u32x4*>(kn), static_cast<const u32x4*>(vn), static_cast<u32x4*>(kc),
                      static_cast<u32x4*>(vc), slot);
+  return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, const void* w, void* kc, void* vc,
+                      void* stream) {
+  const int M = p.V * p.T, N = 2 * p.Hkv * p.D;
+  const unsigned grid = static_cast<unsigned>(((M + kPM - 1) / kPM) * (N / kPN));
+  hipLaunchKernelGGL(kv_project_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p, hidden,
+                     slot, static_cast<const bf16*>(x), static_cast<const bf16*>(w), static_cast<bf16*>(kc),
+                     static_cast<bf16*>(vc));
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 

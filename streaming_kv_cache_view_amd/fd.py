@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.fd_key_position.argtypes, L.fd_key_position.restype = [G, i64, i64, ctypes.POINTER(i64)], ctypes.c_int
         L.fd_kv_insert_frame.argtypes = [G, vp, vp, vp, vp, i64, vp]
         L.fd_kv_insert_frame.restype = ctypes.c_int
+        L.fd_kv_project_insert.argtypes = [G, vp, vp, i32, vp, vp, i64, vp]
+        L.fd_kv_project_insert.restype = ctypes.c_int
         L.fd_stream_workspace_bytes.argtypes, L.fd_stream_workspace_bytes.restype = [G], sz
         L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn.restype = ctypes.c_int
@@ -64,7 +66,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_stream_workspace_bytes",
+EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
            "fd_stream_attn", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
            "fd_verify_attn", "fd_status_str")
 
@@ -114,6 +116,14 @@ def kv_insert_frame(g, k_cache, v_cache, k_new, v_new, frame_idx: int, stream=No
     """k_new/v_new [V][T][Hkv][D] -> ring slot frame_idx mod F of k_cache/v_cache [Hkv][S_cap][D]."""
     _check("fd_kv_insert_frame", lib().fd_kv_insert_frame(
         ctypes.byref(make_geom(g)), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+        int(frame_idx), _stream(stream)))
+
+
+def kv_project_insert(g, x_new, w_kv, k_cache, v_cache, frame_idx: int, stream=None):
+    """Project x_new [V*T][hidden] with w_kv [2*Hkv*D][hidden] and write K/V into ring slot
+    frame_idx mod F of the caches (bf16)."""
+    _check("fd_kv_project_insert", lib().fd_kv_project_insert(
+        ctypes.byref(make_geom(g)), _ptr(x_new), _ptr(w_kv), int(x_new.shape[-1]), _ptr(k_cache), _ptr(v_cache),
         int(frame_idx), _stream(stream)))
 
 

@@ -175,6 +175,20 @@ def test_prefill_call_errors():
     assert L.fd_prefill_attn(gp, MISALIGNED, FAKE, FAKE, 5, FAKE, FAKE, pws, None) == -5
 
 
+def test_kv_project_call_errors():
+    L = fd.lib()
+    gp = ctypes.byref(_g())                     # bf16 inputs; N = 2*Hkv*D = 256
+    f = L.fd_kv_project_insert
+    assert f(ctypes.byref(_g(in_dtype=fd.FD_F32)), FAKE, FAKE, 64, FAKE, FAKE, 0, None) == -3   # bf16 only
+    assert f(gp, None, FAKE, 64, FAKE, FAKE, 0, None) == -1
+    assert f(gp, FAKE, FAKE, 64, FAKE, None, 0, None) == -1
+    assert f(gp, FAKE, FAKE, 96, FAKE, FAKE, 0, None) == -2      # hidden not a multiple of 64
+    assert f(gp, FAKE, FAKE, 0, FAKE, FAKE, 0, None) == -2
+    assert f(gp, FAKE, FAKE, 1 << 22, FAKE, FAKE, 0, None) == -2  # w would exceed 2 GiB
+    assert f(gp, FAKE, FAKE, 64, FAKE, FAKE, -1, None) == -4
+    assert f(gp, FAKE, MISALIGNED, 64, FAKE, FAKE, 0, None) == -5
+
+
 def test_workspace_size_covers_largest_block():
     g = synth.CONFIGS[4].geom
     ws = fd.verify_workspace_bytes(g, 8)

@@ -346,3 +346,43 @@ def test_prefill_backbone_sampled():
 @pytest.mark.parametrize("w", [x for x in EXTRA if x.geom.dtype == synth.BF16], ids=lambda w: w.name)
 def test_prefill_edge_geometries(w):
     check_prefill(w, 0, w.first_t)
+
+
+# ---------------------------------------------------------------------------- K/V projection
+def check_kv_project(w, layer, t, hidden):
+    """Project every view's frame t and insert it: the slot rows against the oracle's
+    projection (bf16 rounding of fp32 sums: |err| <= 2^-8 |ref| + 1e-4), every other row
+    untouched."""
+    g = w.geom
+    H.say(f"kv projection cfg {w.cfg_id} ({w.name}) layer {layer} frame {t} hidden {hidden}")
+    x = np.concatenate([synth.frame_hidden(w, layer, v, t, hidden) for v in range(g.n_views)])
+    wk = synth.kv_weights(w, layer, hidden)
+    kc, vc = H.new_cache(g)
+    fd.kv_project_insert(g, H.dev(x, g), H.dev(wk, g), kc, vc, t)
+    kc_h, vc_h = kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    s = t % g.n_frames
+    worst = 0.0
+    rows = np.zeros(g.cache_rows, bool)
+    for v in range(g.n_views):
+        xv = x[v * g.tok_per_frame: (v + 1) * g.tok_per_frame]
+        k_ref, v_ref = fd_oracle.oracle_kv_projection(xv, wk, g.n_kv_heads, g.head_dim)
+        r0 = g.prefix_len + (v * g.n_frames + s) * g.tok_per_frame
+        rows[r0: r0 + g.tok_per_frame] = True
+        for got, ref in ((kc_h, k_ref), (vc_h, v_ref)):
+            seg = got[:, r0: r0 + g.tok_per_frame, :]                   # [Hkv][T][D]
+            want = np.transpose(ref, (1, 0, 2))
+            err = np.abs(seg - want)
+            assert np.all(err <= 2.0 ** -8 * np.abs(want) + 1e-4), float(err.max())
+            worst = max(worst, float(err.max()))
+    assert np.all(kc_h[:, ~rows, :] == H.SENTINEL) and np.all(vc_h[:, ~rows, :] == H.SENTINEL)
+    H.say(f"  max-abs {worst:.3e}; other rows untouched")
+
+
+@pytest.mark.parametrize("cid,t,hidden", [(2, 5, 256), (2, 2, 1024), (3, 4, 4096)])
+def test_kv_project_insert(cid, t, hidden):
+    check_kv_project(synth.CONFIGS[cid], 0, t, hidden)
+
+
+@pytest.mark.parametrize("w", [x for x in EXTRA if x.geom.dtype == synth.BF16], ids=lambda w: w.name)
+def test_kv_project_edge_geometries(w):
+    check_kv_project(w, 0, w.first_t, 192)
