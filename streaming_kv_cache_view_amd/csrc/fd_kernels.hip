@@ -1509,12 +1509,13 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 // row P + (v*F + s)*T + i of head n/D (Technical Summary, 5. System Optimizations, "Kernel
 // Fusion"; Methodology 1, "Token Layout").
 // Workgroup tile 64 (m) x 128 (n), four waves of 32 x 64, k in chunks of 64; both tiles go
-// straight to LDS (direct loads, double-buffered), rows of 64 bf16 (128 B, eight 16-byte
-// chunks) with chunk c of row r at position c ^ ((r >> 1) & 7), so the 16 rows one operand
-// read touches land in 16 distinct bank groups.  v_mfma_f32_32x32x16_bf16: A = 32 rows of X,
+// straight to LDS (direct loads) through a ring of kPS stages, so kPS-2 chunks are in flight
+// while one is multiplied (a chunk is ~0.1 us of MFMA work against ~1 us of load latency).
+// Rows of 64 bf16 (128 B, eight 16-byte chunks) with chunk c of row r at position
+// c ^ ((r >> 1) & 7), so the 16 rows one operand read touches land in 16 distinct bank groups.  v_mfma_f32_32x32x16_bf16: A = 32 rows of X,
 // B = 32 rows of W (both k-contiguous).
 // ---------------------------------------------------------------------------------------
-constexpr int kPM = 64, kPN = 128, kPK = 64;
+constexpr int kPM = 64, kPN = 128, kPK = 64, kPS = 6;
 __device__ inline uint32_t proj_swz(uint32_t r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hidden, int slot,
@@ -1522,7 +1523,7 @@ __global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hi
                                                          bf16* __restrict__ kc, bf16* __restrict__ vc) {
   constexpr int ROWB = kPK * 2;                 // 128 bytes per staged row
   constexpr int ABYTES = kPM * ROWB, BBYTES = kPN * ROWB, STAGE = ABYTES + BBYTES;   // 8 + 16 KB
-  __shared__ __attribute__((aligned(16))) unsigned char buf[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char buf[kPS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w4 = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int M = p.V * p.T, N = 2 * p.Hkv * p.D;
   const int nblk = N / kPN;
@@ -1559,12 +1560,20 @@ __global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hi
 
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   const int nk = hidden / kPK;
-  stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  wg_barrier();
+  constexpr int NL = 6;   // direct loads per wave and chunk
+  for (int c = 0; c < kPS - 1 && c < nk; ++c) stage(c, c);
   for (int kk = 0; kk < nk; ++kk) {
-    const int sb = kk & 1;
-    if (kk + 1 < nk) stage(kk + 1, sb ^ 1);   // the other buffer was last read before the barrier
+    // chunk kk has landed once at most the loads of the chunks issued after it are pending
+    switch (min(kPS - 2, nk - 1 - kk)) {
+      case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4 * NL)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2 * NL)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(wait_vm(NL)); break;
+      default: __builtin_amdgcn_s_waitcnt(kWaitVm0); break;
+    }
+    wg_barrier();   // ... for every wave; and every wave is done with chunk kk-1
+    const int sb = kk % kPS;
+    if (kk + kPS - 1 < nk) stage(kk + kPS - 1, (kk + kPS - 1) % kPS);   // the slot of chunk kk-1
     const unsigned char* A = buf + sb * STAGE;
     const unsigned char* B = A + ABYTES;
 #pragma unroll
@@ -1578,8 +1587,6 @@ __global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hi
         acc[nb] = BF16Ops::mma(a, b, acc[nb]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // chunk kk+1 has landed
-    wg_barrier();
   }
 
   // epilogue: lane l32 holds feature n = n0 + wn + 32nb + l32 of tokens m = m0 + wm + 8(i/4)
