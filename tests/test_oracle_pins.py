@@ -100,6 +100,37 @@ def _window_newest_first(self):
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
 
+def _kv_proj_swapped(x, w_kv, n_kv_heads, head_dim):
+    k, v = _KV_PROJ(x, w_kv, n_kv_heads, head_dim)
+    return v, k
+
+
+def _kv_proj_head_dim_transposed(x, w_kv, n_kv_heads, head_dim):
+    k, v = _KV_PROJ(x, w_kv, n_kv_heads, head_dim)
+    t = k.shape[0]
+    fix = lambda a: a.reshape(t, head_dim, n_kv_heads).transpose(0, 2, 1)
+    return fix(k), fix(v)
+
+
+def _kv_proj_weight_layout(x, w_kv, n_kv_heads, head_dim):
+    # the weights' memory read as [hidden][2*Hkv*D] (input-major) instead of one feature per row
+    x = np.asarray(x, np.float64)
+    n = n_kv_heads * head_dim
+    w = np.asarray(w_kv, np.float64).reshape(-1, 2 * n)
+    t = x.shape[0]
+    return (x @ w[:, :n]).reshape(t, n_kv_heads, head_dim), (x @ w[:, n:]).reshape(t, n_kv_heads, head_dim)
+
+
+def _full_window_stream_positions(geom, window, q_window):
+    # every query rotated at the newest frame's positions, as a streaming-only oracle would
+    k, v = window.kv()
+    pos = fd_oracle.window_positions(geom, k.shape[0])
+    qpos = np.minimum(pos + geom.tok_per_frame, pos[-1])
+    return fd_oracle.attend(q_window, k, v, qpos, pos, geom.rope_theta)
+
+
+_KV_PROJ = fd_oracle.oracle_kv_projection
+
 MUTANTS = {
     "rope_wrong_sign": ("rope", _rope_wrong_sign),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
@@ -111,6 +142,10 @@ MUTANTS = {
     "query_pos_frame": ("new_query_positions", _nqp_off_by_one_frame),
     "query_pos_token": ("new_query_positions", _nqp_off_by_one_token),
     "ring_off_by_one": ("expected_ring_rows", _ring_off),
+    "kv_proj_swapped": ("oracle_kv_projection", _kv_proj_swapped),
+    "kv_proj_head_dim_transposed": ("oracle_kv_projection", _kv_proj_head_dim_transposed),
+    "kv_proj_weight_layout": ("oracle_kv_projection", _kv_proj_weight_layout),
+    "full_window_query_positions": ("oracle_full_window", _full_window_stream_positions),
 }
 
 
