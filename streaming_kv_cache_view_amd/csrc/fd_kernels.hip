@@ -1508,65 +1508,65 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 // sums are rounded to bf16 and written pre-RoPE straight into the cache rows of ring slot s:
 // row P + (v*F + s)*T + i of head n/D (Technical Summary, 5. System Optimizations, "Kernel
 // Fusion"; Methodology 1, "Token Layout").
-// Workgroup tile 64 (m) x 128 (n), four waves of 32 x 64, k in chunks of 64; both tiles go
-// straight to LDS (direct loads) through a ring of kPS stages, so kPS-2 chunks are in flight
-// while one is multiplied (a chunk is ~0.1 us of MFMA work against ~1 us of load latency).
-// Rows of 64 bf16 (128 B, eight 16-byte chunks) with chunk c of row r at position
-// c ^ ((r >> 1) & 7), so the 16 rows one operand read touches land in 16 distinct bank groups.  v_mfma_f32_32x32x16_bf16: A = 32 rows of X,
-// B = 32 rows of W (both k-contiguous).
+// Workgroup tile 64 (m) x 128 (n), eight waves of 32 x 32 (two per SIMD, so one wave's LDS
+// reads overlap the other's MFMAs), k in chunks of 64; both tiles go straight to LDS (direct
+// loads) through a ring of kPS stages, two chunks in flight while one is multiplied.  Rows of
+// 64 bf16 (128 B, eight 16-byte chunks) with chunk c of row r at position c ^ ((r >> 1) & 7),
+// so the 16 rows one operand read touches land in 16 distinct bank groups.
+// v_mfma_f32_32x32x16_bf16: A = 32 rows of X, B = 32 rows of W (both k-contiguous).
 // ---------------------------------------------------------------------------------------
-constexpr int kPM = 64, kPN = 128, kPK = 64, kPS = 6;
+constexpr int kPM = 64, kPN = 128, kPK = 64, kPS = 4, kPW = 8;
 __device__ inline uint32_t proj_swz(uint32_t r) { return (r >> 1) & 7; }
 
-__global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hidden, int slot,
+__global__ __launch_bounds__(64 * kPW) void kv_project_kernel(const KParams p, int hidden, int slot,
                                                          const bf16* __restrict__ x, const bf16* __restrict__ w,
                                                          bf16* __restrict__ kc, bf16* __restrict__ vc) {
   constexpr int ROWB = kPK * 2;                 // 128 bytes per staged row
   constexpr int ABYTES = kPM * ROWB, BBYTES = kPN * ROWB, STAGE = ABYTES + BBYTES;   // 8 + 16 KB
+  constexpr int NA = ABYTES / 1024, NL = STAGE / 1024 / kPW;   // A instructions; loads per wave
+  static_assert(STAGE % (1024 * kPW) == 0, "whole 1 KB loads per wave");
   __shared__ __attribute__((aligned(16))) unsigned char buf[kPS * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, w4 = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int M = p.V * p.T, N = 2 * p.Hkv * p.D;
   const int nblk = N / kPN;
   const int m0 = (blockIdx.x / nblk) * kPM, n0 = (blockIdx.x % nblk) * kPN;
-  const int wm = (w4 >> 1) * 32, wn = (w4 & 1) * 64;   // this wave's 32 x 64 sub-tile
+  const int wm = (wv >> 2) * 32, wn = (wv & 3) * 32;   // this wave's 32 x 32 sub-tile
   uint32_t ln = lane;
   asm volatile("" : "+v"(ln));
-  // direct loads: instruction j of the workgroup fills staged rows 8j .. 8j+7 (1 KB); lane i
-  // takes row 8j + i/8 and fetches its chunk (i%8) ^ swz(row).  A: 8 instructions (two per
-  // wave), B: 16 (four per wave).  Global offsets per lane are fixed; the k chunk moves the base.
-  const int64_t rowb = static_cast<int64_t>(hidden) * 2;
-  uint32_t aoff[2], boff[4];
+  // direct loads: instruction j of a stage fills staged rows 8j .. 8j+7 (1 KB) of A (j < 8)
+  // or of B (j - 8); lane i takes row 8j + i/8 and fetches its chunk (i%8) ^ swz(row).  Wave
+  // w issues instructions NL*w .. NL*w + NL-1.  Global offsets per lane are fixed; the k chunk
+  // moves the base.
+  const uint32_t rowb = static_cast<uint32_t>(hidden) * 2;
+  uint32_t off[NL];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t r = 8 * (2 * w4 + q) + ln / 8;
-    const int mr = min(m0 + static_cast<int>(r), M - 1);   // rows past M repeat the last
-    aoff[q] = static_cast<uint32_t>(mr) * static_cast<uint32_t>(rowb) + (((ln % 8) ^ proj_swz(r)) << 4);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t r = 8 * (4 * w4 + q) + ln / 8;
-    boff[q] = static_cast<uint32_t>(n0 + r) * static_cast<uint32_t>(rowb) + (((ln % 8) ^ proj_swz(r)) << 4);
+  for (int q = 0; q < NL; ++q) {
+    const int j = NL * wv + q;
+    const uint32_t r = 8 * (j < NA ? j : j - NA) + ln / 8;
+    const int row = j < NA ? min(m0 + static_cast<int>(r), M - 1)   // rows past M repeat the last
+                           : n0 + static_cast<int>(r);
+    off[q] = static_cast<uint32_t>(row) * rowb + (((ln % 8) ^ proj_swz(r)) << 4);
   }
   const uint32_t lds0 = lds_addr(buf);
   auto stage = [&](int kc_, int sb) {
     const unsigned char* xa = uni_ptr(reinterpret_cast<const unsigned char*>(x) + static_cast<int64_t>(kc_) * ROWB);
     const unsigned char* wb = uni_ptr(reinterpret_cast<const unsigned char*>(w) + static_cast<int64_t>(kc_) * ROWB);
-    const uint32_t la = lds0 + sb * STAGE, lb = la + ABYTES;
+    const uint32_t la = lds0 + sb * STAGE;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) g2lds16_async(xa, aoff[q], __builtin_amdgcn_readfirstlane(la + (2 * w4 + q) * 1024));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) g2lds16_async(wb, boff[q], __builtin_amdgcn_readfirstlane(lb + (4 * w4 + q) * 1024));
+    for (int q = 0; q < NL; ++q) {
+      const int j = NL * wv + q;
+      g2lds16_async(j < NA ? xa : wb, off[q], __builtin_amdgcn_readfirstlane(la + j * 1024));
+    }
   };
 
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  f32x16 acc = f32x16{};
   const int nk = hidden / kPK;
-  constexpr int NL = 6;   // direct loads per wave and chunk
   for (int c = 0; c < kPS - 1 && c < nk; ++c) stage(c, c);
   for (int kk = 0; kk < nk; ++kk) {
     // chunk kk has landed once at most the loads of the chunks issued after it are pending
+    static_assert(kPS <= 4, "waits below cover at most two chunks in flight");
     switch (min(kPS - 2, nk - 1 - kk)) {
-      case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4 * NL)); break;
-      case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3 * NL)); break;
       case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2 * NL)); break;
       case 1: __builtin_amdgcn_s_waitcnt(wait_vm(NL)); break;
       default: __builtin_amdgcn_s_waitcnt(kWaitVm0); break;
@@ -1580,30 +1580,24 @@ __global__ __launch_bounds__(256) void kv_project_kernel(const KParams p, int hi
     for (int u = 0; u < kPK / 16; ++u) {   // 16-wide k steps: chunk 2u + h
       const uint32_t ra = wm + l32;
       const u32x4 a = ld16(A + ra * ROWB + (((2 * u + h) ^ proj_swz(ra)) << 4));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t rb = wn + 32 * nb + l32;
-        const u32x4 b = ld16(B + rb * ROWB + (((2 * u + h) ^ proj_swz(rb)) << 4));
-        acc[nb] = BF16Ops::mma(a, b, acc[nb]);
-      }
+      const uint32_t rb = wn + l32;
+      const u32x4 b = ld16(B + rb * ROWB + (((2 * u + h) ^ proj_swz(rb)) << 4));
+      acc = BF16Ops::mma(a, b, acc);
     }
   }
 
-  // epilogue: lane l32 holds feature n = n0 + wn + 32nb + l32 of tokens m = m0 + wm + 8(i/4)
-  // + 4h + i%4; 32 lanes write 32 consecutive dimensions of one head (64 contiguous bytes)
+  // epilogue: lane l32 holds feature n = n0 + wn + l32 of tokens m = m0 + wm + 8(i/4) + 4h
+  // + i%4; 32 lanes write 32 consecutive dimensions of one head (64 contiguous bytes)
+  const int n = n0 + wn + l32;
+  const int kv = n / (p.Hkv * p.D), hd = (n / p.D) % p.Hkv, d = n % p.D;
+  bf16* dst = kv == 0 ? kc : vc;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = n0 + wn + 32 * nb + l32;
-    const int kv = n / (p.Hkv * p.D), hd = (n / p.D) % p.Hkv, d = n % p.D;
-    bf16* dst = kv == 0 ? kc : vc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = m0 + wm + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (m >= M) continue;
-      const int v = m / p.T, ti = m - v * p.T;
-      const int64_t row = p.P + static_cast<int64_t>(v * p.F + slot) * p.T + ti;
-      dst[(static_cast<int64_t>(hd) * p.S_cap + row) * p.D + d] = static_cast<bf16>(acc[nb][i]);
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + wm + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (m >= M) continue;
+    const int v = m / p.T, ti = m - v * p.T;
+    const int64_t row = p.P + static_cast<int64_t>(v * p.F + slot) * p.T + ti;
+    dst[(static_cast<int64_t>(hd) * p.S_cap + row) * p.D + d] = static_cast<bf16>(acc[i]);
   }
 }
 
@@ -2362,7 +2356,7 @@ int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, con
                       void* stream) {
   const int M = p.V * p.T, N = 2 * p.Hkv * p.D;
   const unsigned grid = static_cast<unsigned>(((M + kPM - 1) / kPM) * (N / kPN));
-  hipLaunchKernelGGL(kv_project_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p, hidden,
+  hipLaunchKernelGGL(kv_project_kernel, dim3(grid), dim3(64 * kPW), 0, static_cast<hipStream_t>(stream), p, hidden,
                      slot, static_cast<const bf16*>(x), static_cast<const bf16*>(w), static_cast<bf16*>(kc),
                      static_cast<bf16*>(vc));
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
