@@ -121,6 +121,54 @@ def cpu_baseline(min_seconds: float = 12.0, max_layers: int = 36):
     }
 
 
+def rolling_windows(g, n_windows, gen, host_ahead):
+    """Times n_windows consecutive windows of one layer (insert + streaming-prefill attention,
+    each call bracketed by its own events, back to back behind a queued GPU spin)."""
+    import torch
+    from streaming_kv_cache_view_amd import fd
+    dev = "cuda"
+    rnd = lambda *s: torch.randn(*s, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kc = rnd(g.n_kv_heads, g.cache_rows, g.head_dim)
+    vc = rnd(g.n_kv_heads, g.cache_rows, g.head_dim)
+    n_in = 8   # distinct input sets, used in turn
+    kn = [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(n_in)]
+    vn = [rnd(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim) for _ in range(n_in)]
+    qn = [rnd(g.n_new, g.n_q_heads, g.head_dim) for _ in range(n_in)]
+    out = torch.empty(g.n_new, g.n_q_heads, g.head_dim, device=dev)
+    sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=dev)
+    t0 = g.n_frames   # frames 0 .. F-1 are in the cache
+    ins_ms, att_ms = [], []
+    for rep_i in range(2):   # the first sweep is a warm-up
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_windows + 1)]
+        host_ahead()
+        ev[0].record()
+        for w in range(n_windows):
+            t = t0 + w
+            fd.kv_insert_frame(g, kc, vc, kn[w % n_in], vn[w % n_in], t)
+            ev[2 * w + 1].record()
+            fd.stream_attn(g, qn[w % n_in], kc, vc, t, out, sws)
+            ev[2 * w + 2].record()
+        torch.cuda.synchronize()
+        if rep_i > 0:
+            ins_ms = [ev[2 * w].elapsed_time(ev[2 * w + 1]) for w in range(n_windows)]
+            att_ms = [ev[2 * w + 1].elapsed_time(ev[2 * w + 2]) for w in range(n_windows)]
+    flops = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
+    att_us = sum(att_ms) / len(att_ms) * 1e3
+    tf = flops / (att_us * 1e-6) / 1e12
+    return {
+        "windows": n_windows,
+        "stream_us_per_window": round(att_us, 2),
+        "stream_us_median": round(sorted(att_ms)[len(att_ms) // 2] * 1e3, 2),
+        "stream_us_min": round(min(att_ms) * 1e3, 2),
+        "insert_us_per_window": round(sum(ins_ms) / len(ins_ms) * 1e3, 2),
+        "gflop_per_window": round(flops / 1e9, 2),
+        "achieved_tflops": round(tf, 2),
+        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+        "note": "100 rolling windows of one layer at 8,704 keys (V=4, F=8, T=256, P=512, 32/8 heads, D=128); "
+                "inserts timed separately; timing inputs N(0,1) bf16",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,9 +268,10 @@ def main():
             att_ms.append(ev[1][l].elapsed_time(ev[2][l]))
             ver_ms.append(ev[2][l].elapsed_time(ev[3][l]))
     mean = lambda a: sum(a) / len(a)
+    med = lambda a: sorted(a)[len(a) // 2]
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
-    v16_us = graph_ms_per_step = prefill_us = kvproj_us = None
+    v16_us = graph_ms_per_step = prefill_us = kvproj_us = c5 = vgraph_us = None
     F = g.n_frames
     if not args.core_only:
         # verify with 16-token draft blocks (64 query rows per kv head)
@@ -283,6 +332,34 @@ def main():
         kvproj_us = sum(kp_ms) / len(kp_ms) * 1e3
         kvproj_flops = 2 * g.n_new * (2 * g.n_kv_heads * g.head_dim) * hidden
         del xs, wkv
+
+        # the 36 verify calls of a step captured in one HIP graph: wall time of the sequence
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        tv = frame[0]
+        with torch.cuda.stream(side):
+            vgr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(vgr, stream=side):
+                for l in range(L):
+                    fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], tv, n_tail, blk, vout[l], ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        vgr.replay()
+        torch.cuda.synchronize()
+        vg_ms = []
+        for _ in range(max(2, args.steps // 2)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vgr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            vg_ms.append(e0.elapsed_time(e1))
+        vgraph_us = sorted(vg_ms)[len(vg_ms) // 2] * 1e3 / L
+        del vgr
+
+        # config 5 shapes: 100 rolling windows of one layer (V=4, F=8, T=256, P=512: 8,704 keys),
+        # each an insert of the new frames and a streaming-prefill call; timing inputs N(0,1)
+        c5 = rolling_windows(synth.CONFIGS[5].geom, 100, gen, host_ahead)
 
         # the same window step replayed from HIP graphs: one graph per ring phase (t mod F), every
         # kernel argument depending on the newest frame only through it
@@ -363,6 +440,16 @@ def main():
         },
         "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
                         "verify_attn": round(ver_us, 2)},
+        "per_call_us_median": {k: round(med(x) * 1e3, 2) for k, x in
+                               (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
+        "per_call_us_min": {k: round(min(x) * 1e3, 2) for k, x in
+                            (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
+        "verify_graph": None if vgraph_us is None else {
+            "us_per_call": round(vgraph_us, 2),
+            "gbs": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9, 1),
+            "frac": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": f"the {L} verify calls of a step captured in one HIP graph, median replay / {L}"},
+        "config5": c5,
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
         "verify_block16": None if v16_us is None else {
             "us_per_call": round(v16_us, 2),
