@@ -162,9 +162,8 @@ int fd_stream_attn(const fd_geom* g, const void* q_new,
                    void* hip_stream);
 
 /* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every
- * window row's queries rotated (fp16), the key-tile table and fp32 partial results of
- * frames whose key range is split between workgroups.  0 on invalid geometry or fp32
- * inputs.  The size depends on the geometry only.                                   */
+ * window row's queries rotated (fp16) and the key-tile table.  0 on invalid geometry or
+ * fp32 inputs.  The size depends on the geometry only.                              */
 size_t fd_prefill_workspace_bytes(const fd_geom* g);
 
 /* Non-streaming (cold-start) prefill: every token of the window is a query, under the same

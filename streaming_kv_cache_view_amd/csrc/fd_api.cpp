@@ -54,6 +54,7 @@ fd::KParams make_params(const fd_geom* g, int64_t t) {
   p.seg0 = 0;
   p.nseg = p.V;
   p.qtok = p.T;
+  p.whole = 0;
   p.pos_base = g->pos_base;
   p.t = t;
   p.sm_scale_log2 = float(1.4426950408889634 / std::sqrt(double(p.D)));
@@ -137,9 +138,8 @@ size_t fd_prefill_workspace_bytes(const fd_geom* g) {
   if (check_geom(g) != FD_OK || g->in_dtype != FD_BF16) return 0;
   const fd::KParams p = make_params(g, g->n_frames - 1);
   const size_t krot = size_t(p.Hkv) * p.W * p.D * 2;
-  const int n_rb = p.Hkv * p.n_hsub * p.nqb;   // the frame segments' row blocks (the prefix's need no partials)
-  return fd::align256(krot) + fd::stream_qrot_bytes(p.W, p.Hq, p.D) +
-         fd::stream_tiles_bytes(1, p.P, p.T, p.V, p.F) + fd::stream_partial_bytes(n_rb, p.V * p.F, p.D);
+  // every segment is attended whole by one workgroup: no partials
+  return fd::align256(krot) + fd::stream_qrot_bytes(p.W, p.Hq, p.D) + fd::stream_tiles_bytes(1, p.P, p.T, p.V, p.F);
 }
 
 int fd_prefill_attn(const fd_geom* g, const void* q_win, const void* k_cache, const void* v_cache,

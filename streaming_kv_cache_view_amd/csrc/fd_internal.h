@@ -36,6 +36,9 @@ struct KParams {
   int32_t seg0;       // first segment of this launch
   int32_t nseg;       // segments (and chunks) per row block of this launch
   int32_t qtok;       // query tokens per segment of this launch (T, or P for the prefix)
+  int32_t whole;      // 0: the row block's segments laid end to end and cut into nseg equal
+                      //    chunks (split segments merged by a second kernel);
+                      // 1: chunk c is segment nseg-1-c whole (no split, no merge)
   // verify
   int32_t n_tail, B, nblk, n_split;
   int32_t n_rb;       // 32-row blocks of the G*B verify query rows

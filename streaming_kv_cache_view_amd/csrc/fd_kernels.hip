@@ -442,10 +442,13 @@ struct StreamTiles {
 // When P and T are multiples of RPP no block straddles two segments, so the rotation of
 // row base + r is cs(base) (per block) times cs(r) (per thread); otherwise each element's
 // angle is reduced on its own.
-// For bf16 inputs the workgroups past the first nkb also rotate the new frames' queries
-// (rows (token, query head of the kv head)) at their positions, scale them by
-// log2(e)/sqrt(D) and store them as fp16 in the input's [V*T][Hq][D] order: the attention
-// kernel loads its QK^T operands straight from there.
+// For bf16 inputs the workgroups past the first nkb also rotate the queries (the new frames'
+// tokens, or every window token for a cold start) at their positions, scale them by
+// log2(e)/sqrt(D) and store them as fp16 in the input's [tokens][Hq][D] order: the attention
+// kernel loads its QK^T operands straight from there.  Such a workgroup takes 32 tokens and
+// up to four query heads of the kv head (kRopeQTok x min(G, 4) rows); the heads share a
+// token's angles, so they come from a per-workgroup LDS table of the 32 tokens' (cos, sin).
+// Every thread issues all of its global loads before it computes an angle.
 // ---------------------------------------------------------------------------------------
 __device__ inline int64_t row_pos(const KParams& p, int x) {
   if (x < p.P) return p.pos_base + x;
@@ -453,6 +456,9 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
   const int v = rr / (p.F * p.T), s = (rr / p.T) % p.F, i = rr % p.T;
   return slot_pos(p, v, s) + i;
 }
+
+constexpr int kRopeQTok = 32;   // tokens per query workgroup of the rotation pass
+__host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
@@ -471,6 +477,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   constexpr int NB = ROWS >= RPP ? ROWS / RPP : 1;
   __shared__ double sfreq[H2];
   __shared__ float2 csb[NB][H2];
+  __shared__ float2 qcs[kRopeQTok][H2];
   const int tid = threadIdx.x, kvh = blockIdx.y, row_base = blockIdx.x * ROWS;
   const int rr = tid / CH, c = tid % CH;
   if (tiles && blockIdx.x == 0 && blockIdx.y == 0) {   // the attention kernel's tile table
@@ -478,36 +485,59 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
     for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
       for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
   }
-  if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token tg, head kvh*G + hh)
-    // streaming: the newest frames' rows [V*T]; full window: every window row [W]
-    const int G = p.G, NQ = (p.qmode == 0 ? p.V * p.T : p.W) * G, qr0 = (blockIdx.x - nkb) * ROWS;
+  if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token, head kvh*G + hh)
+    // streaming: the newest frames' tokens [V*T]; full window: every window token [W]
+    constexpr int QP = (4 * kRopeQTok + RPP - 1) / RPP;   // passes for up to four heads
+    const int G = p.G, GH = rope_q_heads(G), NTOK = p.qmode == 0 ? p.V * p.T : p.W;
+    const int qb = blockIdx.x - nkb, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
+    const int nrows = kRopeQTok * GH;
     const float sc = p.sm_scale_log2;
-    double frev[E];   // frequencies in revolutions per position
+    u32x4 raw[QP][2];
+    int64_t offs[QP];
 #pragma unroll
-    for (int e = 0; e < E; ++e) frev[e] = p.inv_freq[E * c + e] * 0.15915494309189535;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int r = qr0 + b * RPP + rr;
-      if (r >= NQ || (ROWS < RPP && rr >= ROWS)) continue;
-      const int tg = r / G, hh = r - tg * G;
-      const int v = tg / p.T, i = tg - v * p.T;
+    for (int b = 0; b < QP; ++b) {   // all loads first
+      const int r = b * RPP + rr, tl = r / GH, tg = tok0 + tl;
+      offs[b] = -1;
+      if (r >= nrows || tg >= NTOK) continue;
+      offs[b] = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hsub * GH + r % GH) * D;
+      raw[b][0] = ld16(q + offs[b] + E * c);
+      raw[b][1] = ld16(q + offs[b] + H2 + E * c);
+    }
+    for (int e = tid; e < kRopeQTok * H2; e += 256) {   // (cos, sin) table of the 32 tokens
+      const int tl = e / H2, i = e % H2, tg = min(tok0 + tl, NTOK - 1);
+      const int v = tg / p.T, it = tg - v * p.T;
       const double pos = static_cast<double>(
-          p.qmode == 0 ? p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + i : row_pos(p, tg));
-      const int64_t off = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hh) * D;
+          p.qmode == 0 ? p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + it : row_pos(p, tg));
+      qcs[tl][i] = cs_rev(pos * (p.inv_freq[i] * kInvTwoPi));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < QP; ++b) {
+      if (offs[b] < 0) continue;
+      const int tl = (b * RPP + rr) / GH;
       float x1[E], x2[E];
-      In::unpack(ld16(q + off + E * c), x1);
-      In::unpack(ld16(q + off + H2 + E * c), x2);
+      In::unpack(raw[b][0], x1);
+      In::unpack(raw[b][1], x2);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float2 cs = cs_rev(pos * frev[e]);
+        const float2 cs = qcs[tl][E * c + e];
         const float a = x1[e], bb = x2[e];
         x1[e] = (a * cs.x - bb * cs.y) * sc;
         x2[e] = (bb * cs.x + a * cs.y) * sc;
       }
-      st16(qrot + off + E * c, QK::pack(x1));
-      st16(qrot + off + H2 + E * c, QK::pack(x2));
+      st16(qrot + offs[b] + E * c, QK::pack(x1));
+      st16(qrot + offs[b] + H2 + E * c, QK::pack(x2));
     }
     return;
+  }
+  u32x4 raw[NB][2];   // all loads first
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int x = row_base + b * RPP + rr;
+    if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
+    const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+    raw[b][0] = ld16(src + E * c);
+    raw[b][1] = ld16(src + H2 + E * c);
   }
   if (tid < H2) sfreq[tid] = p.inv_freq[tid];
   for (int e = tid; e < NB * H2; e += 256) {
@@ -522,10 +552,9 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   for (int b = 0; b < NB; ++b) {
     const int x = row_base + b * RPP + rr;
     if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
-    const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
     float x1[E], x2[E];
-    In::unpack(ld16(src + E * c), x1);
-    In::unpack(ld16(src + H2 + E * c), x2);
+    In::unpack(raw[b][0], x1);
+    In::unpack(raw[b][1], x2);
     const int64_t pos = aligned ? 0 : row_pos(p, x);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -1005,8 +1034,11 @@ static_assert(StageMap<128>::check() && StageMap<64>::check(), "whole-tile stagi
 // tile sequence of view_tiles tiles.  They are laid end to end in the order nseg-1, 0,
 // nseg-2, 1, ... (long and short alternate) and the ntot tiles are cut into nseg chunks,
 // chunk c = [bnd(c), bnd(c+1)).  Every segment has at least one tile, so no chunk is empty.
+// With `whole` set (cold start: many more workgroups than CUs) the order is nseg-1, nseg-2,
+// ..., 0 (longest first) and chunk c is exactly the c-th segment of it: the dispatcher hands
+// the longest jobs out first and the rest fill in, with no split and no merge.
 struct StreamSplit {
-  int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf;
+  int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf, whole;
   __device__ StreamSplit(const KParams& p, int qb) {
     constexpr int TK = kTileKeys;
     nP = (p.P + TK - 1) / TK;
@@ -1017,6 +1049,7 @@ struct StreamSplit {
     seg0 = p.seg0;
     qmode = p.qmode;
     vf = p.V * p.F;
+    whole = p.whole;
     ntot = 0;
     for (int u = 0; u < V; ++u) ntot += view_tiles(u);
   }
@@ -1027,8 +1060,18 @@ struct StreamSplit {
     if (qmode == 0) return nP + (sg * F + F - 1) * tps + ndiag;
     return sg < vf ? nP + sg * tps + ndiag : ndiag;
   }
-  __device__ int order(int oi) const { return (oi & 1) ? oi / 2 : V - 1 - oi / 2; }
-  __device__ int bnd(int c) const { return static_cast<int>((static_cast<int64_t>(c) * ntot) / V); }
+  __device__ int order(int oi) const {
+    if (whole) return V - 1 - oi;
+    return (oi & 1) ? oi / 2 : V - 1 - oi / 2;
+  }
+  __device__ int bnd(int c) const {
+    if (whole) {
+      int pos = 0;
+      for (int oi = 0; oi < c; ++oi) pos += view_tiles(order(oi));
+      return pos;
+    }
+    return static_cast<int>((static_cast<int64_t>(c) * ntot) / V);
+  }
   // start of view v in the end-to-end order
   __device__ int start(int v) const {
     int pos = 0;
@@ -2261,7 +2304,8 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                     : nullptr;
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D) +
                                          stream_tiles_bytes(0, p.P, p.T, p.V, p.F));
-  const int nkb = (p.W + 127) / 128, nqk = b16 ? (p.V * p.T * p.G + 127) / 128 : 0;
+  const int nkb = (p.W + 127) / 128;
+  const int nqk = b16 ? ceil_div(p.V * p.T, kRopeQTok) * (p.G / rope_q_heads(p.G)) : 0;
   hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
                      static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
@@ -2279,9 +2323,10 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
 }
 
 // Full-window (cold-start) prefill, bf16: one rotation pass for the window's keys and every
-// window row's queries, then the attention kernel over the V*F frame segments (and the merge
-// of the segments split between workgroups) and over the prefix segment (one chunk: no
-// split, no merge).
+// window row's queries, then the attention kernel over the V*F frame segments, one workgroup
+// per (row block, segment), longest segments first (V*F times more workgroups than a
+// streaming call, so the dispatcher balances them without splitting any), and over the
+// prefix segment.
 template <int D>
 int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                      hipStream_t st) {
@@ -2291,8 +2336,7 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   QKT* krot = static_cast<QKT*>(ws);
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(tiles) + stream_tiles_bytes(1, p.P, p.T, p.V, p.F));
-  const int nkb = (p.W + 127) / 128, nqk = (p.W * p.G + 127) / 128;
+  const int nkb = (p.W + 127) / 128, nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
   hipLaunchKernelGGL((rope_window_kernel<bf16, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
                      static_cast<const bf16*>(kc), krot, aligned, nkb, static_cast<const bf16*>(q), qrot, tiles);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
@@ -2301,11 +2345,10 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   pf.nseg = p.V * p.F;
   pf.qtok = p.T;
   pf.nqb = ceil_div(p.T, 32 * p.TBW);
+  pf.whole = 1;
   const int grid = pf.Hkv * pf.n_hsub * pf.nqb * pf.nseg;
   hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pf, static_cast<const QKT*>(qrot),
-                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, part, tiles);
-  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-  hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, pf, part, out);
+                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, nullptr, tiles);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   if (p.P > 0) {
     KParams pp = p;   // the prefix segment
@@ -2313,9 +2356,10 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
     pp.nseg = 1;
     pp.qtok = p.P;
     pp.nqb = ceil_div(p.P, 32 * p.TBW);
+    pp.whole = 1;
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(pp.Hkv * pp.n_hsub * pp.nqb), dim3(512), 0, st, pp,
                        static_cast<const QKT*>(qrot), static_cast<const QKT*>(krot), static_cast<const bf16*>(vc),
-                       out, part, tiles);
+                       out, nullptr, tiles);
   }
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }

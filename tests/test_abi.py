@@ -155,15 +155,13 @@ def test_prefill_call_errors():
     g = _g()                                   # bf16 inputs
     gp = ctypes.byref(g)
     pws = L.fd_prefill_workspace_bytes(gp)
-    # rotated keys, every window row's rotated queries (W = 8 + 2*4*16 = 136 rows), the tile
+    # rotated keys, every window row's rotated queries (W = 8 + 2*4*16 = 136 rows) and the tile
     # table (frame (v, j): prefix + v*F + j earlier frames + diagonal, one 64-key tile each here;
-    # then the prefix segment) and two partial slots per (row block, frame chunk)
+    # then the prefix segment); every segment is attended whole, so no partial slots
     W = 8 + 2 * 4 * 16
     align = lambda x: (x + 255) // 256 * 256
     n_tiles = sum(1 + sg + 1 for sg in range(2 * 4)) + 1
-    n_rb = g.n_kv_heads * 1 * 1
-    assert pws == (align(g.n_kv_heads * W * 64 * 2) + align(W * 4 * 64 * 2) + align(n_tiles * 8)
-                   + n_rb * 8 * 2 * (128 * 64 + 256) * 4)
+    assert pws == align(g.n_kv_heads * W * 64 * 2) + align(W * 4 * 64 * 2) + align(n_tiles * 8)
     assert L.fd_prefill_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == 0
     assert L.fd_prefill_attn(ctypes.byref(_g(in_dtype=fd.FD_F32)), FAKE, FAKE, FAKE, 5, FAKE, FAKE, pws,
                              None) == -3                                        # bf16 only
