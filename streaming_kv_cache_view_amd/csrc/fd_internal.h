@@ -13,7 +13,7 @@ constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
 constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
 constexpr int kVerifyWaves = 4;             // waves per verify workgroup, fp32 path
 constexpr int kVerifyBlocksPerWave = 1;
-constexpr int kVerifyWavesDma = 8;          // bf16 path
+constexpr int kVerifyWavesDma = 5;          // bf16 path (5: 31 splits x 8 kv heads at config 4, about one workgroup per CU)
 constexpr int kVerifyBlocksPerWaveDma = 1;
 
 // Everything a kernel needs about one call, passed by value as a kernel argument.

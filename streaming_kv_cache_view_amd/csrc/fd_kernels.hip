@@ -1905,13 +1905,15 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 // token b), in 32-row MFMA blocks, one workgroup per (kv head, row block, split).  Keys are numbered by cache row x: window rows [0, W),
 // reasoning rows [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk
 // and copied into the cache here).  They are cut into 32-key blocks inside segments of
-// contiguous positions; wave w of split s (eight waves, two per SIMD) takes block 8s + w.
+// contiguous positions; wave w of split s (kVerifyWavesDma = NW waves) takes block NW*s + w.
+// Five waves per workgroup make about one workgroup per CU at the backbone shapes (31 splits
+// x 8 kv heads); eight (two per SIMD, 19 splits) measured 3 % slower.
 //
-// The kernel is a single pass over HBM: every K and V byte of the workgroup's eight blocks
-// (128 KB for D = 128) is requested at once, straight into LDS (global_load_lds).  Each wave
+// The kernel is a single pass over HBM: every K and V byte of the workgroup's blocks (16 KB
+// per block for D = 128) is requested at once, straight into LDS (global_load_lds).  Each wave
 // proceeds as soon as its own block has landed: keys are rotated (LDS -> registers, at their
 // current positions; cos / sin per lane from the hardware units), QK^T / softmax / PV run,
-// and the eight waves fold into one (m, l, O) partial per (kv head, split), in a fixed order.
+// and the waves fold into one (m, l, O) partial per (kv head, split), in a fixed order.
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
@@ -1933,6 +1935,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   constexpr int OS = D + 4;
   constexpr int KVB = NW * NBW * BLKB;           // K (or V) bytes of the workgroup
   static_assert(4 * 32 * OS * 4 <= 2 * KVB, "merge slots alias the K / V tiles");
+  static_assert(NW >= 4 && NW <= 8, "the fold: four slots, at most one adding wave each");
   constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
   auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
   auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
@@ -2158,9 +2161,9 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   }
   __syncthreads();   // K / V tiles are dead: the space is reused for the merge
 
-  // ---- fold the eight waves (same rows, different keys) into one partial, in a fixed order:
-  // waves 0-3 write their rescaled O to four LDS slots, waves 4-7 add theirs, the four slots
-  // are summed in slot order.
+  // ---- fold the waves (same rows, different keys) into one partial, in a fixed order: waves
+  // 0-3 write their rescaled O to four LDS slots, waves 4.. add theirs to slot w - 4, the four
+  // slots are summed in slot order.
   const float l_tot = xhalf_sum(l_run);
   if (lane < 32) {
     red_m[w][l32] = m_run;
