@@ -161,6 +161,23 @@ int fd_stream_attn(const fd_geom* g, const void* q_new,
                    int64_t newest_frame, void* out, void* ws, size_t ws_bytes,
                    void* hip_stream);
 
+/* The window step's insert and attention in one launch sequence: exactly
+ * fd_kv_insert_frame(g, k_cache, v_cache, k_new, v_new, newest_frame) followed by
+ * fd_stream_attn(g, q_new, k_cache, v_cache, newest_frame, out, ws, ws_bytes), with the copy
+ * of the new frames done by the rotation pass that reads them anyway (Token Layout passage:
+ * the new frame of each view goes to the end of its segment; Positional Encoding: keys are
+ * cached pre-RoPE and rotated at their current positions), so the insert's own launch and its
+ * pass over the new rows disappear.
+ *   k_new, v_new : [V][T][Hkv][D] in_dtype, pre-RoPE K and V of frame newest_frame.
+ *   q_new, out, ws : as for fd_stream_attn.
+ *   k_cache, v_cache : hold frames newest_frame-F+1 .. newest_frame-1 in their slots; on
+ *            return slot newest_frame mod F holds the new frame (bit-exact copy), and no other
+ *            cache row has changed.
+ *   Errors as for both calls.  newest_frame >= F-1.                                 */
+int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new, const void* q_new,
+                          void* k_cache, void* v_cache, int64_t newest_frame, void* out, void* ws,
+                          size_t ws_bytes, void* hip_stream);
+
 /* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every
  * window row's queries rotated (fp16) and the key-tile table.  0 on invalid geometry or
  * fp32 inputs.  The size depends on the geometry only.                              */

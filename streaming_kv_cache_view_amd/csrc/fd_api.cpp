@@ -170,6 +170,22 @@ int fd_stream_attn(const fd_geom* g, const void* q_new, const void* k_cache, con
   return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream);
 }
 
+int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new, const void* q_new,
+                          void* k_cache, void* v_cache, int64_t newest_frame, void* out, void* ws,
+                          size_t ws_bytes, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (!k_new || !v_new || !q_new || !k_cache || !v_cache || !out) return FD_ERR_NULL;
+  if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
+  if (!ws || ws_bytes < fd_stream_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
+    return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, newest_frame);
+  return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream, k_new,
+                           v_new);
+}
+
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
   if (check_geom(g) != FD_OK) return 0;
   if (blk_len < 1 || blk_len > g->tail_cap) return 0;

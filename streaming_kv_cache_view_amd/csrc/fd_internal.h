@@ -95,8 +95,10 @@ inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
 
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
                   int slot, void* stream);
+// kn / vn non-null: the new frames' K and V ([V][T][Hkv][D]) are inserted into ring slot
+// s_new by the same launch sequence (the rotation pass), before the attention reads them
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,
-                  void* out, void* ws, void* stream);
+                  void* out, void* ws, void* stream, const void* kn = nullptr, const void* vn = nullptr);
 int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                    void* stream);
 int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, const void* w, void* kc, void* vc,

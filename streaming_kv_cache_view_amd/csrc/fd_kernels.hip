@@ -56,6 +56,7 @@ constexpr double kInvTwoPi = 0.15915494309189535;
 // |a| < 2^31), then fp32 polynomials on [-pi/4, pi/4] (Taylor/minimax, error < 1 ulp of fp32
 // there) and the quadrant's swap / signs.
 __device__ inline float2 cs_angle(double a) {
+#pragma clang fp contract(off)   // the same roundings wherever it is inlined
   const double k = rint(a * 0.63661977236758134);           // 2/pi
   const double r = fma(-k, 1.5707963267948966, a) - k * 6.123233995736766e-17;
   const float x = static_cast<float>(r), x2 = x * x;
@@ -77,8 +78,14 @@ __device__ inline float2 cs_rev(double r) {
   return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
 }
 
+// Complex product and rotation with every rounding spelled out (explicit fma after a rounded
+// product), so that each instantiation of a kernel rounds a rotated key identically.
 __device__ inline float2 cmul(float2 a, float2 b) {
-  return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
+  return make_float2(__builtin_fmaf(a.x, b.x, -(a.y * b.y)), __builtin_fmaf(a.y, b.x, a.x * b.y));
+}
+// (a, b) rotated by the angle whose (cos, sin) is cs: (a cos - b sin, b cos + a sin)
+__device__ inline float2 rot2(float a, float b, float2 cs) {
+  return make_float2(__builtin_fmaf(a, cs.x, -(b * cs.y)), __builtin_fmaf(b, cs.x, a * cs.y));
 }
 
 // MFMA operand formats.  A "16-byte chunk" holds E elements of the operand type.
@@ -458,16 +465,37 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
 }
 
 constexpr int kRopeQTok = 32;   // tokens per query workgroup of the rotation pass
+
+// The new frames to insert in the same pass (kn == nullptr: none).  Rows of ring slot s_new
+// are then read from kn / vn ([V][T][Hkv][D], pre-RoPE) instead of the cache, and copied into
+// the cache rows (K and V) on the way, so that the attention kernel that follows reads them
+// there: fd_kv_insert_frame and the rotation in one pass.
+template <typename T>
+struct NewFrame {
+  const T* kn;
+  const T* vn;
+  T* kc;
+  T* vc;
+};
 __host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
 
-template <typename T, int D>
+template <typename T, int D, bool INS>   // INS: the new frames are inserted by this pass (nf)
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
                                                           typename Path<T>::QKT* __restrict__ krot,
                                                           int aligned, int nkb, const T* __restrict__ q,
                                                           typename Path<T>::QKT* __restrict__ qrot,
-                                                          int2* __restrict__ tiles) {
+                                                          int2* __restrict__ tiles, const NewFrame<T> nf) {
+#pragma clang fp contract(off)   // every instantiation rounds a rotated row the same way
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
+  // each value rounded to fp32 first, then to the operand type: no fused multiply-add-convert
+  // (v_fma_mix rounds once, straight to fp16, and the compiler picks it in some instantiations
+  // only, so the two rotation passes would differ in the last bit of a few keys)
+  auto pack_rounded = [](float* f) {
+#pragma unroll
+    for (int e = 0; e < In::E; ++e) asm volatile("" : "+v"(f[e]));
+    return QK::pack(f);
+  };
   using QKT = typename Path<T>::QKT;
   constexpr int E = In::E;
   constexpr int H2 = D / 2;
@@ -522,20 +550,33 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       for (int e = 0; e < E; ++e) {
         const float2 cs = qcs[tl][E * c + e];
         const float a = x1[e], bb = x2[e];
-        x1[e] = (a * cs.x - bb * cs.y) * sc;
-        x2[e] = (bb * cs.x + a * cs.y) * sc;
+        const float2 r = rot2(a, bb, cs);
+        x1[e] = r.x * sc;
+        x2[e] = r.y * sc;
       }
-      st16(qrot + offs[b] + E * c, QK::pack(x1));
-      st16(qrot + offs[b] + H2 + E * c, QK::pack(x2));
+      st16(qrot + offs[b] + E * c, pack_rounded(x1));
+      st16(qrot + offs[b] + H2 + E * c, pack_rounded(x2));
     }
     return;
   }
-  u32x4 raw[NB][2];   // all loads first
+  u32x4 raw[NB][2], vraw[NB][2];   // all loads first
+  bool isnew[NB];                   // a row of the new frame (read from kn / vn)
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int x = row_base + b * RPP + rr;
+    isnew[b] = false;
     if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
     const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+    if (INS && x >= p.P) {
+      const int xr = x - p.P, v = xr / (p.F * p.T), s = (xr / p.T) % p.F, i = xr % p.T;
+      if (s == p.s_new) {
+        const int64_t nrow = (static_cast<int64_t>(v * p.T + i) * p.Hkv + kvh) * D;
+        isnew[b] = true;
+        src = nf.kn + nrow;
+        vraw[b][0] = ld16(nf.vn + nrow + E * c);
+        vraw[b][1] = ld16(nf.vn + nrow + H2 + E * c);
+      }
+    }
     raw[b][0] = ld16(src + E * c);
     raw[b][1] = ld16(src + H2 + E * c);
   }
@@ -561,12 +602,20 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       const int i = E * c + e;
       const float2 cs = aligned ? cmul(csb[b][i], csr[e]) : cs_angle(static_cast<double>(pos) * sfreq[i]);
       const float a = x1[e], bb = x2[e];
-      x1[e] = a * cs.x - bb * cs.y;
-      x2[e] = bb * cs.x + a * cs.y;
+      const float2 r = rot2(a, bb, cs);
+      x1[e] = r.x;
+      x2[e] = r.y;
     }
     QKT* dst = krot + (static_cast<int64_t>(kvh) * p.W + x) * D;
-    st16(dst + E * c, QK::pack(x1));
-    st16(dst + H2 + E * c, QK::pack(x2));
+    st16(dst + E * c, pack_rounded(x1));
+    st16(dst + H2 + E * c, pack_rounded(x2));
+    if (INS && isnew[b]) {   // the new frame's row into the cache: K as read, V
+      const int64_t cdst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
+      st16(nf.kc + cdst + E * c, raw[b][0]);
+      st16(nf.kc + cdst + H2 + E * c, raw[b][1]);
+      st16(nf.vc + cdst + E * c, vraw[b][0]);
+      st16(nf.vc + cdst + H2 + E * c, vraw[b][1]);
+    }
   }
 }
 
@@ -2294,7 +2343,7 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
 
 template <typename T, int D>
 int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
-                    hipStream_t st) {
+                    hipStream_t st, const void* kn, const void* vn) {
   using QKT = typename Path<T>::QKT;
   constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
   const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
@@ -2309,8 +2358,15 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                                          stream_tiles_bytes(0, p.P, p.T, p.V, p.F));
   const int nkb = (p.W + 127) / 128;
   const int nqk = b16 ? ceil_div(p.V * p.T, kRopeQTok) * (p.G / rope_q_heads(p.G)) : 0;
-  hipLaunchKernelGGL((rope_window_kernel<T, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles);
+  const NewFrame<T> nf{static_cast<const T*>(kn), static_cast<const T*>(vn),
+                       kn ? const_cast<T*>(static_cast<const T*>(kc)) : nullptr,
+                       kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
+  if (kn)
+    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles, nf);
+  else
+    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles, nf);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
@@ -2340,8 +2396,9 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
   const int nkb = (p.W + 127) / 128, nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
-  hipLaunchKernelGGL((rope_window_kernel<bf16, D>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const bf16*>(kc), krot, aligned, nkb, static_cast<const bf16*>(q), qrot, tiles);
+  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const bf16*>(kc), krot, aligned, nkb, static_cast<const bf16*>(q), qrot, tiles,
+                     NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr});
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   KParams pf = p;   // the frame segments
   pf.seg0 = 0;
@@ -2410,14 +2467,14 @@ int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, con
 }
 
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc, void* out,
-                  void* ws, void* stream) {
+                  void* ws, void* stream, const void* kn, const void* vn) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_bf16) {
-    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, ws, st)
-                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, ws, st);
+    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, ws, st, kn, vn)
+                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, ws, st, kn, vn);
   }
-  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st)
-                    : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st);
+  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st, kn, vn)
+                    : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st, kn, vn);
 }
 
 int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.fd_stream_workspace_bytes.argtypes, L.fd_stream_workspace_bytes.restype = [G], sz
         L.fd_stream_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn.restype = ctypes.c_int
+        L.fd_stream_attn_insert.argtypes = [G, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
+        L.fd_stream_attn_insert.restype = ctypes.c_int
         L.fd_prefill_workspace_bytes.argtypes, L.fd_prefill_workspace_bytes.restype = [G], sz
         L.fd_prefill_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_prefill_attn.restype = ctypes.c_int
@@ -67,7 +69,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
-           "fd_stream_attn", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
+           "fd_stream_attn", "fd_stream_attn_insert", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
            "fd_verify_attn", "fd_status_str")
 
 
@@ -142,6 +144,17 @@ def stream_attn(g, q_new, k_cache, v_cache, newest_frame: int, out, ws, ws_bytes
     _check("fd_stream_attn", lib().fd_stream_attn(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_new), _ptr(k_cache), _ptr(v_cache),
         int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def stream_attn_insert(g, k_new, v_new, q_new, k_cache, v_cache, newest_frame: int, out, ws,
+                       ws_bytes: int | None = None, out_dtype: str = "f32", stream=None):
+    """kv_insert_frame(k_new, v_new, newest_frame) then stream_attn(q_new, newest_frame), in one
+    launch sequence (the rotation pass copies the new frame into the cache)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("fd_stream_attn_insert", lib().fd_stream_attn_insert(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(k_new), _ptr(v_new), _ptr(q_new), _ptr(k_cache),
+        _ptr(v_cache), int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def prefill_workspace_bytes(g) -> int:

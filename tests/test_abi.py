@@ -126,6 +126,15 @@ def test_call_errors():
     assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws - 1, None) == -7
     assert L.fd_stream_attn(gp, MISALIGNED, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -5
     assert L.fd_stream_attn(gp, FAKE, FAKE, FAKE, 5, FAKE, MISALIGNED, sws, None) == -5
+    S = L.fd_stream_attn_insert
+    assert S(None, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
+    assert S(gp, None, FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1          # no k_new
+    assert S(gp, FAKE, None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1          # no v_new
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, FAKE, sws, None) == -1          # no out
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, sws, None) == -4          # window not full
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws - 1, None) == -7
+    assert S(gp, MISALIGNED, FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -5
+    assert S(gp, FAKE, FAKE, FAKE, MISALIGNED, FAKE, 5, FAKE, FAKE, sws, None) == -5
     assert L.fd_kv_insert_frame(gp, FAKE, None, FAKE, FAKE, 0, None) == -1
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, FAKE, -1, None) == -4
     assert L.fd_kv_insert_frame(gp, FAKE, FAKE, FAKE, MISALIGNED, 0, None) == -5

@@ -386,3 +386,40 @@ def test_kv_project_insert(cid, t, hidden):
 @pytest.mark.parametrize("w", [x for x in EXTRA if x.geom.dtype == synth.BF16], ids=lambda w: w.name)
 def test_kv_project_edge_geometries(w):
     check_kv_project(w, 0, w.first_t, 192)
+
+
+# ---------------------------------------------------------------------------- insert fused into the stream call
+def check_stream_insert(w, layer, t, out_dtype="f32"):
+    """fd_stream_attn_insert against fd_kv_insert_frame followed by fd_stream_attn on an identical
+    copy of the caches: output and both caches bit-identical (the separate calls are checked
+    against the oracle elsewhere; this one also against the oracle directly)."""
+    g = w.geom
+    H.say(f"stream+insert cfg {w.cfg_id} ({w.name}) layer {layer} t {t} out {out_dtype}")
+    kc, vc = H.window_caches(w, layer, t - 1)   # frames 0 .. t-1 inserted
+    kc2, vc2 = kc.clone(), vc.clone()
+    k, v, _ = synth.new_frames(w, layer, t)
+    kn, vn = H.dev(k, g), H.dev(v, g)
+    q = H.q_new(w, layer, t)
+    fd.kv_insert_frame(g, kc, vc, kn, vn, t)
+    ref = H.stream_out(w, layer, kc, vc, t, out_dtype, q=q)
+    out = torch.empty_like(ref)
+    ws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    fd.stream_attn_insert(g, kn, vn, q, kc2, vc2, t, out, ws, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2), "cache images differ"
+    assert torch.equal(out, ref), float((out.float() - ref.float()).abs().max())
+    err = H.max_err(out.float().cpu().numpy().astype(np.float64), oracle_outputs(w, layer, [t])[t])
+    tol = H.TOL[g.dtype] + (0.02 if out_dtype == "bf16" else 0.0)
+    H.say(f"  bit-identical to insert + stream; max-abs vs oracle {err:.3e} (tol {tol})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("cid,dt", [(1, "f32"), (2, "f32"), (3, "f32"), (3, "bf16")])
+def test_stream_insert_fused(cid, dt):
+    w = synth.CONFIGS[cid]
+    check_stream_insert(w, 0, w.first_t + 1, dt)
+
+
+@pytest.mark.parametrize("w", EXTRA, ids=lambda w: w.name)
+def test_stream_insert_fused_edge_geometries(w):
+    check_stream_insert(w, 0, w.first_t + w.geom.n_frames)   # a later ring phase
