@@ -34,9 +34,9 @@ class Window:
     """Static device buffers of one window step over `layers` layers (a graph reads and
     writes these same buffers on every replay)."""
 
-    def __init__(self, g, layers, n_tail, blk, gen):
+    def __init__(self, g, layers, n_tail, blk, gen, fused=False):
         rnd = lambda *s: torch.randn(*s, generator=gen, device=H.DEV).to(torch.bfloat16)
-        self.g, self.L, self.n_tail, self.blk = g, layers, n_tail, blk
+        self.g, self.L, self.n_tail, self.blk, self.fused = g, layers, n_tail, blk, fused
         self.kc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(layers)]
         self.vc = [rnd(g.n_kv_heads, g.cache_rows, g.head_dim) for _ in range(layers)]
         self.kn = [torch.empty(g.n_views, g.tok_per_frame, g.n_kv_heads, g.head_dim, dtype=torch.bfloat16,
@@ -67,8 +67,12 @@ class Window:
     def step(self, t):
         g = self.g
         for l in range(self.L):
-            fd.kv_insert_frame(g, self.kc[l], self.vc[l], self.kn[l], self.vn[l], t)
-            fd.stream_attn(g, self.qn[l], self.kc[l], self.vc[l], t, self.out[l], self.sws)
+            if self.fused:   # insert + attention in one launch sequence
+                fd.stream_attn_insert(g, self.kn[l], self.vn[l], self.qn[l], self.kc[l], self.vc[l], t,
+                                      self.out[l], self.sws)
+            else:
+                fd.kv_insert_frame(g, self.kc[l], self.vc[l], self.kn[l], self.vn[l], t)
+                fd.stream_attn(g, self.qn[l], self.kc[l], self.vc[l], t, self.out[l], self.sws)
             fd.verify_attn(g, self.qb[l], self.kb[l], self.vb[l], self.kc[l], self.vc[l], t, self.n_tail,
                            self.blk, self.vout[l], self.vws)
 
@@ -85,15 +89,15 @@ def window_inputs(g, layers, blk, gen):
     }
 
 
-@pytest.mark.parametrize("cid,layers", [(3, 3), (5, 2)])
-def test_graph_rolling_windows_match_eager(cid, layers):
+@pytest.mark.parametrize("cid,layers,fused", [(3, 3, False), (5, 2, False), (3, 2, True)])
+def test_graph_rolling_windows_match_eager(cid, layers, fused):
     w = synth.CONFIGS[cid]
     g = w.geom
     F, blk, n_tail = g.n_frames, 8, min(200, g.tail_cap - 8)
     gen = torch.Generator(device=H.DEV)
     gen.manual_seed(20 + cid)
-    eager = Window(g, layers, n_tail, blk, gen)
-    graphed = Window(g, layers, n_tail, blk, gen)
+    eager = Window(g, layers, n_tail, blk, gen)   # eager: the separate insert and attention calls
+    graphed = Window(g, layers, n_tail, blk, gen, fused)
     graphed.clone_caches_from(eager)
     t0 = F   # window full
     # one graph per ring phase, captured on a side stream (capture does not run the kernels)
