@@ -1964,7 +1964,7 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 // current positions; cos / sin per lane from the hardware units), QK^T / softmax / PV run,
 // and the waves fold into one (m, l, O) partial per (kv head, split), in a fixed order.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, int NRB>   // NRB: 32-row blocks of query rows per workgroup (1 or 2)
 __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
                                                          const bf16* __restrict__ kb,
                                                          const bf16* __restrict__ vb, bf16* __restrict__ kc,
@@ -1996,12 +1996,22 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   __shared__ float red_m[NW][32], red_l[NW][32];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  // blockIdx.x = (split * n_rb + rb) * Hkv + kvh: the row blocks of one split run side by
-  // side on one XCD and read the same K / V
-  const int kvh = blockIdx.x % p.Hkv, rb = (blockIdx.x / p.Hkv) % p.n_rb, split = blockIdx.x / (p.Hkv * p.n_rb);
-  const int qr = 32 * rb + l32, hh = qr / p.B, bq = qr % p.B;   // query row qr = hh*B + b
-  const bool qvalid = hh < p.G;
-  const int head = kvh * p.G + (qvalid ? hh : 0);
+  // blockIdx.x = (split * nrbg + rbg) * Hkv + kvh, nrbg = ceil(n_rb / NRB): the row-block
+  // groups of one split run side by side on one XCD and read the same K / V.  The workgroup
+  // takes row blocks NRB*rbg + r (r < NRB, those < n_rb): its keys are loaded and rotated once
+  // for all of them.
+  const int nrbg = (p.n_rb + NRB - 1) / NRB;
+  const int kvh = blockIdx.x % p.Hkv, rbg = (blockIdx.x / p.Hkv) % nrbg, split = blockIdx.x / (p.Hkv * nrbg);
+  int bq[NRB], head[NRB];
+  bool qvalid[NRB], rbvalid[NRB];
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) {
+    const int rb = NRB * rbg + r, qr = 32 * rb + l32, hh = qr / p.B;   // query row qr = hh*B + b
+    rbvalid[r] = rb < p.n_rb;
+    bq[r] = qr % p.B;
+    qvalid[r] = rbvalid[r] && hh < p.G;
+    head[r] = kvh * p.G + (qvalid[r] ? hh : 0);
+  }
   const int tailbase = p.W + p.n_tail;   // cache row of block token 0
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
 
@@ -2049,11 +2059,12 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   }
 
   // ---- queries (registers) and every K / V byte of the workgroup (LDS), all in flight
-  u32x4 qraw[NU];
-  {
-    const bf16* qsrc = qb + (static_cast<int64_t>(bq) * p.Hq + head) * D;
+  u32x4 qraw[NRB][NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) qraw[u] = ld16(qsrc + 2 * E * u + E * h);   // invalid rows: zeroed below
+  for (int r = 0; r < NRB; ++r) {
+    const bf16* qsrc = qb + (static_cast<int64_t>(bq[r]) * p.Hq + head[r]) * D;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) qraw[r][u] = ld16(qsrc + 2 * E * u + E * h);   // invalid rows: zeroed below
   }
   // direct loads of this wave's block, interleaved with the (cos, sin) of its key's 32 RoPE
   // angles (they depend on positions only), so the wave computes while the memory pipe drains
@@ -2091,13 +2102,14 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
 
   // ---- queries rotated at their positions, scaled into log2 units, rounded to fp16 (their
   // loads were issued first, so this waits for them only, while the K / V loads land)
-  u32x4 qf[NU];
-  {
+  u32x4 qf[NRB][NU];
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) {
     float fq[NU][E];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[u], fq[u]);
-    const float qs = qvalid ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
-    const double qpos = static_cast<double>(p.pos_base + tailbase + bq);
+    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[r][u], fq[u]);
+    const float qs = qvalid[r] ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
+    const double qpos = static_cast<double>(p.pos_base + tailbase + bq[r]);
 #pragma unroll
     for (int u = 0; u < NU / 2; ++u) {
       double f = fbase[u];
@@ -2111,7 +2123,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
       }
     }
 #pragma unroll
-    for (int u = 0; u < NU; ++u) qf[u] = QK::pack(fq[u]);
+    for (int u = 0; u < NU; ++u) qf[r][u] = QK::pack(fq[u]);
   }
 
   __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's K / V have landed (no other wave's
@@ -2120,7 +2132,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   // ---- block rows: into the cache (their K / V came from k_blk / v_blk)
 #pragma unroll
   for (int lb = 0; lb < NBW; ++lb) {
-    if (rb != 0 || len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
+    if (rbg != 0 || len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
     const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
     const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
     for (int e = lane; e < 32 * KCH; e += 64) {
@@ -2142,10 +2154,15 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
     voff[d] = key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
   }
 
-  f32x16 o[ND];
+  f32x16 o[NRB][ND];
+  float m_run[NRB], l_run[NRB];
 #pragma unroll
-  for (int d = 0; d < ND; ++d) o[d] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int r = 0; r < NRB; ++r) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[r][d] = f32x16{};
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
 #pragma unroll
   for (int lb = 0; lb < NBW; ++lb) {
     if (len[lb] <= 0) continue;
@@ -2170,52 +2187,59 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
         kf[u + NU / 2] = QK::pack(fk[1]);
       }
     }
-    f32x16 s = f32x16{};
 #pragma unroll
-    for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[u], s);
-    float mx = -INFINITY;
+    for (int r = 0; r < NRB; ++r) {   // the rotated keys serve every row block of the workgroup
+      f32x16 s = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
-      const bool ok = (kk < len[lb]) & ((x0[lb] + kk - tailbase) <= bq);
-      s[i] = ok ? s[i] : -INFINITY;
-      mx = fmaxf(mx, s[i]);
-    }
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
-    l_run *= alpha;
+      for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[r][u], s);
+      float mx = -INFINITY;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) o[d] *= alpha;
-    m_run = m_new;
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool ok = (kk < len[lb]) & ((x0[lb] + kk - tailbase) <= bq[r]);
+        s[i] = ok ? s[i] : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+      mx = xhalf_max(mx);
+      const float m_new = fmaxf(m_run[r], mx);
+      const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mu);
+      l_run[r] *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = __builtin_amdgcn_exp2f(s[i] - mu);
-      l_run += s[i];
-    }
+      for (int d = 0; d < ND; ++d) o[r][d] *= alpha;
+      m_run[r] = m_new;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      float pv[E];
+      for (int i = 0; i < 16; ++i) {
+        s[i] = __builtin_amdgcn_exp2f(s[i] - mu);
+        l_run[r] += s[i];
+      }
 #pragma unroll
-      for (int e = 0; e < E; ++e) pv[e] = s[E * cc + e];
-      const u32x4 bop = PV::pack(pv);
+      for (int cc = 0; cc < 2; ++cc) {
+        float pv[E];
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const u32x2 lo = ds_read_tr16(Vt + voff[d] + 16 * cc * ROWB);
-        const u32x2 hi = ds_read_tr16(Vt + voff[d] + (16 * cc + 8) * ROWB);
-        o[d] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, bop, o[d]);
+        for (int e = 0; e < E; ++e) pv[e] = s[E * cc + e];
+        const u32x4 bop = PV::pack(pv);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const u32x2 lo = ds_read_tr16(Vt + voff[d] + 16 * cc * ROWB);
+          const u32x2 hi = ds_read_tr16(Vt + voff[d] + (16 * cc + 8) * ROWB);
+          o[r][d] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, bop, o[r][d]);
+        }
       }
     }
   }
   __syncthreads();   // K / V tiles are dead: the space is reused for the merge
 
-  // ---- fold the waves (same rows, different keys) into one partial, in a fixed order: waves
-  // 0-3 write their rescaled O to four LDS slots, waves 4.. add theirs to slot w - 4, the four
-  // slots are summed in slot order.
-  const float l_tot = xhalf_sum(l_run);
+  // ---- per row block: fold the waves (same rows, different keys) into one partial, in a
+  // fixed order: waves 0-3 write their rescaled O to four LDS slots, waves 4.. add theirs to
+  // slot w - 4, the four slots are summed in slot order.
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) {
+  if (!rbvalid[r]) break;   // uniform: row blocks past n_rb
+  if (r > 0) __syncthreads();   // the previous row block's slots have been read
+  const float l_tot = xhalf_sum(l_run[r]);
   if (lane < 32) {
-    red_m[w][l32] = m_run;
+    red_m[w][l32] = m_run[r];
     red_l[w][l32] = l_tot;
   }
   __syncthreads();
@@ -2226,7 +2250,7 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww)
     if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
-  const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  const float scale = (m_run[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[r] - M);
   float* obuf = reinterpret_cast<float*>(kvbuf);   // four slots of 32 x OS floats
   float* ob = obuf + (w & 3) * 32 * OS;
   if (w < 4) {
@@ -2234,8 +2258,8 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
-        const f32x4 r = {o[d][4 * ig] * scale, o[d][4 * ig + 1] * scale, o[d][4 * ig + 2] * scale, o[d][4 * ig + 3] * scale};
-        *reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h) = r;
+        const f32x4 rv = {o[r][d][4 * ig] * scale, o[r][d][4 * ig + 1] * scale, o[r][d][4 * ig + 2] * scale, o[r][d][4 * ig + 3] * scale};
+        *reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h) = rv;
       }
   }
   __syncthreads();
@@ -2245,22 +2269,23 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         f32x4* dst = reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h);
-        const f32x4 r = {o[d][4 * ig] * scale, o[d][4 * ig + 1] * scale, o[d][4 * ig + 2] * scale, o[d][4 * ig + 3] * scale};
-        *dst = *dst + r;
+        const f32x4 rv = {o[r][d][4 * ig] * scale, o[r][d][4 * ig + 1] * scale, o[r][d][4 * ig + 2] * scale, o[r][d][4 * ig + 3] * scale};
+        *dst = *dst + rv;
       }
   }
   __syncthreads();
-  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + split) * verify_partial_words(D);
+  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + NRB * rbg + r) * p.n_split + split) * verify_partial_words(D);
   for (int e = tid; e < 32 * D / 4; e += 64 * NW) {
-    const int r = e / (D / 4), c = e % (D / 4);
-    f32x4 a = *reinterpret_cast<const f32x4*>(obuf + r * OS + 4 * c);
+    const int row = e / (D / 4), c = e % (D / 4);
+    f32x4 a = *reinterpret_cast<const f32x4*>(obuf + row * OS + 4 * c);
 #pragma unroll
-    for (int sl = 1; sl < 4; ++sl) a = a + *reinterpret_cast<const f32x4*>(obuf + sl * 32 * OS + r * OS + 4 * c);
-    *reinterpret_cast<f32x4*>(dstp + r * D + 4 * c) = a;
+    for (int sl = 1; sl < 4; ++sl) a = a + *reinterpret_cast<const f32x4*>(obuf + sl * 32 * OS + row * OS + 4 * c);
+    *reinterpret_cast<f32x4*>(dstp + row * D + 4 * c) = a;
   }
   if (w == 0 && lane < 32) {
     dstp[32 * D + l32] = M;
     dstp[32 * D + 32 + l32] = L;
+  }
   }
 }
 
@@ -2429,9 +2454,14 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
                     void* out, void* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((verify_dma_kernel<D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
-                       static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
-                       static_cast<T*>(kc), static_cast<T*>(vc), part);
+    if (p.n_rb >= 2)   // two row blocks per workgroup: each key rotated once for both
+      hipLaunchKernelGGL((verify_dma_kernel<D, 2>), dim3(p.Hkv * ((p.n_rb + 1) / 2) * p.n_split),
+                         dim3(64 * kVerifyWavesDma), 0, st, p, static_cast<const T*>(qb), static_cast<const T*>(kb),
+                         static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc), part);
+    else
+      hipLaunchKernelGGL((verify_dma_kernel<D, 1>), dim3(p.Hkv * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
+                         static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
+                         static_cast<T*>(kc), static_cast<T*>(vc), part);
   } else {
     hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(256), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
