@@ -5,13 +5,18 @@
 //  rope_window_kernel  once per call: every window key rotated at its current (shifted)
 //                      position (Methodology 1, "Positional Encoding") into a caller
 //                      workspace, in the QK^T operand format; the cache stays unrotated.
-//                      For bf16 inputs it also rotates and scales the new frames' queries.
+//                      For bf16 inputs it also rotates and scales the queries.  Its
+//                      inserting instantiation also copies the new frame into its ring slot
+//                      (fd_stream_attn_insert).
 //  stream_pp_kernel    (bf16) attention of the new frame's tokens over the view-major window,
 //                      two wave groups in MFMA / softmax ping-pong; the streaming mask is
 //                      generated from the view / slot / token indices, never loaded.  The
 //                      views of a block of query rows are balanced across workgroups.
 //  stream_merge_kernel (bf16) fixed-order merge of the views split between workgroups.
 //  stream_attn_kernel  (fp32) the same attention, both groups in the same phase.
+//  kv_project_kernel   (bf16) K/V projection of the new frames (MFMA GEMM) whose epilogue
+//                      writes them, pre-RoPE, into the ring slot (Technical Summary,
+//                      "Kernel Fusion").
 //  verify_dma_kernel (bf16) / verify_split_kernel (fp32) + verify_merge_kernel
 //                      speculative-verify attention of a short draft block over the whole
 //                      window + reasoning tail (README technique list, "Speculative
