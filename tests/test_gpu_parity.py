@@ -243,9 +243,11 @@ def test_verify_config4_layers():
         check_verify(w, layer, w.first_t, w.n_tail, w.blk_len)
 
 
-# Larger draft blocks: G*B query rows per kv head in several 32-row blocks (G = 4: B = 16 is
-# 64 rows, B = 12 is 48 rows with a partial second block; config 1 has G = 2).
-@pytest.mark.parametrize("cid,n_tail,blk_len", [(2, 40, 16), (2, 3, 12), (1, 8, 24), (1, 0, 16)])
+# Larger draft blocks: G*B query rows per kv head in several 32-row blocks, two per workgroup
+# (G = 4: B = 16 is 64 rows, B = 12 is 48 rows with a partial second block, B = 24 is three
+# blocks (the second workgroup of a split has one), B = 32 four; config 1 has G = 2).
+@pytest.mark.parametrize("cid,n_tail,blk_len", [(2, 40, 16), (2, 3, 12), (2, 17, 24), (2, 0, 32), (1, 8, 24),
+                                                (1, 0, 16)])
 def test_verify_block_rows(cid, n_tail, blk_len):
     check_verify(synth.CONFIGS[cid], 0, 5 if cid == 2 else 4, n_tail, blk_len)
 
