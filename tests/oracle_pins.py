@@ -328,6 +328,28 @@ def pin_verify_sdpa():
     assert err <= 1e-12, err
 
 
+def pin_stream_workload_rolling():
+    """The whole-workload driver (which frames are pushed, which query frame is used at each t,
+    which layer's draws) against scalar brute force at every window of a rolling stream.
+
+    Over 2F+1 consecutive windows of a tiny geometry (the ring wraps twice) and at a layer
+    other than 0, every yielded output equals `brute_force.brute_stream`, which builds the
+    window at t from frame ids t-F+1..t and the queries of frame t by itself.
+    """
+    for w, layer in ((TINY, 2), (TINY_G4, 1)):
+        g = w.geom
+        ts = list(range(g.n_frames - 1, g.n_frames - 1 + 2 * g.n_frames + 1))
+        got = dict(fd_oracle.run_stream_workload(w, layer, ts, synth))
+        assert sorted(got) == ts, (w.name, sorted(got))
+        pk, pv = synth.prefix_kv(w, layer)
+        for t in ts:
+            bf = brute_force.brute_stream(
+                g, pk, pv, lambda v, f: synth.frame_kv(w, layer, v, f),
+                lambda v, f: synth.frame_q(w, layer, v, f), t)
+            err = np.max(np.abs(got[t] - np.array(bf)))
+            assert err <= 1e-12, (w.name, layer, t, err)
+
+
 def pin_kv_projection():
     """Brute-force sums on a tiny case; one-hot hidden states pick out weight columns; the
     head / dimension split of the output features."""
@@ -365,4 +387,5 @@ ALL_PINS = [
     pin_expected_cache_layout,
     pin_verify_sdpa,
     pin_kv_projection,
+    pin_stream_workload_rolling,
 ]

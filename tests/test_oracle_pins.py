@@ -129,6 +129,34 @@ def _full_window_stream_positions(geom, window, q_window):
     return fd_oracle.attend(q_window, k, v, qpos, pos, geom.rope_theta)
 
 
+def _workload_variant(q_lag=0, skip_last_push=False, frame_layer=None):
+    """A copy of the oracle's workload driver with one planted mistake switched on: queries
+    taken from frame t - q_lag, the last view's newest frame pushed only after attention,
+    or the frames drawn from another layer's seeds."""
+    def run(workload, layer, t_values, synth):
+        g = workload.geom
+        pk, pv = synth.prefix_kv(workload, layer)
+        win = fd_oracle.StreamWindow(g, pk, pv)
+        t_values = list(t_values)
+        fl = layer if frame_layer is None else frame_layer
+        for t in range(max(t_values) + 1):
+            for v in range(g.n_views):
+                if skip_last_push and v == g.n_views - 1 and t in t_values:
+                    continue
+                k, vv = synth.frame_kv(workload, fl, v, t)
+                win.push(v, t, k, vv)
+            if t in t_values:
+                if not win.full():
+                    raise AssertionError("window not full")
+                q = np.concatenate([synth.frame_q(workload, layer, v, max(t - q_lag, 0))
+                                    for v in range(g.n_views)])
+                yield t, fd_oracle.oracle_stream(g, win, q)
+            if skip_last_push and t in t_values:
+                k, vv = synth.frame_kv(workload, fl, g.n_views - 1, t)
+                win.push(g.n_views - 1, t, k, vv)
+    return run
+
+
 _KV_PROJ = fd_oracle.oracle_kv_projection
 
 MUTANTS = {
@@ -146,6 +174,9 @@ MUTANTS = {
     "kv_proj_head_dim_transposed": ("oracle_kv_projection", _kv_proj_head_dim_transposed),
     "kv_proj_weight_layout": ("oracle_kv_projection", _kv_proj_weight_layout),
     "full_window_query_positions": ("oracle_full_window", _full_window_stream_positions),
+    "workload_query_frame_lag": ("run_stream_workload", _workload_variant(q_lag=1)),
+    "workload_missing_last_push": ("run_stream_workload", _workload_variant(skip_last_push=True)),
+    "workload_wrong_layer_seed": ("run_stream_workload", _workload_variant(frame_layer=0)),
 }
 
 
