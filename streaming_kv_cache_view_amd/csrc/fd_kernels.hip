@@ -355,7 +355,8 @@ struct TileInfo {
 // pass, one key-tile sequence per query segment.  A segment is the queries of one frame: in a
 // streaming call view v's newest frame, in a full-window call every frame (view v, age j) and
 // the prefix.  Frame (v, j)'s sequence is the prefix tiles, every frame of views < v, view
-// v's frames older than j (in age order), then its own frame (the diagonal, masked per
+// v's frames older than j (all frames in age order, so the walk -- and every sum -- is the
+// same at every ring phase), then its own frame (the diagonal, masked per
 // token); the prefix segment's is the prefix tiles, masked per token.  A row block whose
 // tokens end early uses a prefix of the diagonal.  Entry (segment, t) = {first key row,
 // len | diag << 7 | (first key's token within its segment) << 8}: key rows index the
@@ -427,9 +428,9 @@ struct StreamTiles {
         u = v;
         sl = slot_of_age(p, j);
         diag = 1;
-      } else if (f < v * F) {
+      } else if (f < v * F) {   // frames of earlier views, in age order as well
         u = f / F;
-        sl = f - u * F;
+        sl = slot_of_age(p, f - u * F);
       } else {
         u = v;
         sl = slot_of_age(p, f - v * F);   // age f - v*F < j
@@ -725,14 +726,13 @@ __global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const
     }
     e -= hasP;
     int u, s;
-    if (e < nfull) {
+    if (e < nfull) {   // frames in age order (views < v, then view v's older frames)
       if (e < v * p.F) {
         u = e / p.F;
-        s = e - u * p.F;
+        s = StreamTiles::slot_of_age(p, e - u * p.F);
       } else {
         u = v;
-        const int j = e - v * p.F;
-        s = j < p.s_new ? j : j + 1;
+        s = StreamTiles::slot_of_age(p, e - v * p.F);
       }
       c.nk = tps;
       c.diag = false;

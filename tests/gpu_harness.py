@@ -104,6 +104,44 @@ def run_verify(w, layer, t, n_tail, blk_len, kc=None, vc=None, out_dtype="f32"):
     return out, kc, vc
 
 
+def bf16_half_ulp(x):
+    """Half a bfloat16 ulp at magnitude |x| (8 significant bits): 2^(e-8) for |x| in [2^e, 2^(e+1))."""
+    a = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, (np.floor(np.log2(a)) - 8).astype(np.int64))
+
+
+def out_bound(want, g, out_dtype):
+    """Per-element bound against the fp64 oracle: the input dtype's tolerance, plus for bf16
+    outputs the half ulp that rounding the fp32 result to bf16 adds (at the magnitude the fp32
+    result can reach, |ref| + tolerance)."""
+    tol = TOL[g.dtype]
+    if out_dtype != "bf16":
+        return np.full(np.shape(want), tol)
+    return tol + bf16_half_ulp(np.abs(want) + tol)
+
+
+def check_out(got, want, g, out_dtype, what=""):
+    """Assert |got - want| <= out_bound elementwise; returns the max-abs error."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - want)
+    excess = err - out_bound(want, g, out_dtype)
+    worst = int(np.argmax(excess))
+    assert excess.flat[worst] <= 0, (what, float(err.flat[worst]), float(want.flat[worst]))
+    return float(err.max())
+
+
+def check_bf16_rounding(got_bf16, got_f32, what=""):
+    """A bf16 output is the fp32 output of the same call rounded: within half a bf16 ulp of it
+    (plus 2^-20 relative for fp32 reassociation)."""
+    b = np.asarray(got_bf16, np.float64)
+    f = np.asarray(got_f32, np.float64)
+    err = np.abs(b - f)
+    assert np.all(err <= bf16_half_ulp(f) * (1 + 2.0 ** -20) + 1e-30), (what, float(err.max()))
+
+
 def max_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -108,13 +108,20 @@ def pin_brute_force_verify():
 
 
 def pin_shift_invariance():
-    """Shifting every position by the same amount leaves the output unchanged."""
+    """Shifting every position by the same amount leaves the output unchanged.
+
+    Up to 2^20 the fp64 angles are exact to ~1e-10 rad, so the bound is 1e-9.  At the largest
+    base the C ABI admits (last cache row at 2^31 - 1) an fp64 angle pos * inv_freq carries an
+    absolute rounding error up to 2^31 * 2^-53 = 2^-22 rad, which moves each rotated element by
+    at most that relative amount; 1e-5 bounds the resulting output change with a wide margin.
+    """
     w = TINY
     ref = _stream(w, w.first_t)
-    for c in (1, 1000, 2 ** 20):
+    top = 2 ** 31 - w.geom.cache_rows - 1
+    for c, bound in ((1, 1e-9), (1000, 1e-9), (2 ** 20, 1e-9), (top, 1e-5)):
         w2 = Workload(w.cfg_id, w.name, w.geom.replace(pos_base=c), first_t=w.first_t)
         err = np.max(np.abs(_stream(w2, w.first_t) - ref))
-        assert err <= 1e-9, (c, err)
+        assert err <= bound, (c, err)
 
 
 def _sdpa(qr, kr, v, mask=None, causal=False):
