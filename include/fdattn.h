@@ -22,7 +22,8 @@
  *   - Every pointer argument except `g` is a DEVICE pointer on the current
  *     HIP device, 16-byte aligned.  The caller owns every buffer (caches,
  *     inputs, outputs, workspace); the library allocates nothing and keeps no
- *     state between calls, so calls on different streams with disjoint
+ *     state between calls (one exception: the static scratch array behind
+ *     fd_verify_attn_noalloc), so calls on different streams with disjoint
  *     buffers may run concurrently.
  *   - Calls are asynchronous on `hip_stream` (a hipStream_t, NULL = default
  *     stream), like any kernel launch.
@@ -79,7 +80,9 @@ typedef enum {
   FD_ERR_ALIGN = -5,      /* a device pointer is not 16-byte aligned                 */
   FD_ERR_TAIL = -6,       /* n_tail < 0, blk_len < 1, or n_tail + blk_len > tail_cap  */
   FD_ERR_WORKSPACE = -7,  /* workspace NULL or smaller than fd_verify_workspace_bytes */
-  FD_ERR_HIP = -8         /* the kernel launch failed                                */
+  FD_ERR_HIP = -8,        /* the kernel launch failed                                */
+  FD_ERR_SCRATCH = -9     /* fd_verify_attn_noalloc: the call needs more scratch than
+                             its static array holds (FD_VERIFY_SCRATCH_BYTES)            */
 } fd_status;
 
 /* One layer's geometry.  Constraints checked by every call:
@@ -229,6 +232,26 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk,
                    void* k_cache, void* v_cache, int64_t newest_frame,
                    int32_t n_tail, int32_t blk_len,
                    void* out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Bytes of the static device array behind fd_verify_attn_noalloc (per GPU). */
+#define FD_VERIFY_SCRATCH_BYTES (32u << 20)
+
+/* fd_verify_attn for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, semantics,
+ * kernels and results as fd_verify_attn, without the workspace: the split-KV partials go to a
+ * static __device__ array of FD_VERIFY_SCRATCH_BYTES (32 MiB) that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine); its first call on a device looks up that device's address of
+ * the array once.  Calls needing more than FD_VERIFY_SCRATCH_BYTES of workspace
+ * (fd_verify_workspace_bytes(g, blk_len)) return FD_ERR_SCRATCH before anything is enqueued;
+ * the config-4 backbone shapes need 5 MiB at blk_len 8 and 20 MiB at blk_len 32.
+ * Every call on one GPU shares its array: calls that overlap on one GPU (concurrent streams,
+ * or host threads) race and give undefined results; calls ordered on one stream are safe. */
+int fd_verify_attn_noalloc(const fd_geom* g, const void* q_blk,
+                           const void* k_blk, const void* v_blk,
+                           void* k_cache, void* v_cache, int64_t newest_frame,
+                           int32_t n_tail, int32_t blk_len,
+                           void* out, void* hip_stream);
 
 /* Static description of a status code. */
 const char* fd_status_str(int status);

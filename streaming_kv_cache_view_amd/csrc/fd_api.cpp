@@ -198,9 +198,13 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
                                    fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
 
-int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,
-                   void* k_cache, void* v_cache, int64_t newest_frame, int32_t n_tail,
-                   int32_t blk_len, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
+namespace {
+
+// Checks shared by the verify entry points (everything but the workspace), in the order the
+// header documents.
+int check_verify_args(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache, int64_t newest_frame, int32_t n_tail,
+                      int32_t blk_len, const void* out) {
   int st = check_geom(g);
   if (st != FD_OK) return st;
   if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !out) return FD_ERR_NULL;
@@ -208,10 +212,18 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
   if (n_tail < 0 || blk_len < 1 || int64_t(n_tail) + blk_len > g->tail_cap) return FD_ERR_TAIL;
   if (blk_len > 32 || fd::verify_row_blocks(g->n_q_heads / g->n_kv_heads, blk_len) > fd::kVerifyMaxRowBlocks)
     return FD_ERR_TAIL;
-  if (!ws || ws_bytes < fd_verify_workspace_bytes(g, blk_len)) return FD_ERR_WORKSPACE;
-  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
-    return FD_ERR_ALIGN;
+  return FD_OK;
+}
+
+bool verify_aligned(const void* q_blk, const void* k_blk, const void* v_blk, const void* k_cache,
+                    const void* v_cache, const void* out) {
+  return aligned16(q_blk) && aligned16(k_blk) && aligned16(v_blk) && aligned16(k_cache) && aligned16(v_cache) &&
+         aligned16(out);
+}
+
+int launch_verify_checked(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk, void* k_cache,
+                          void* v_cache, int64_t newest_frame, int32_t n_tail, int32_t blk_len, void* out,
+                          void* ws, void* hip_stream) {
   fd::KParams p = make_params(g, newest_frame);
   p.n_tail = n_tail;
   p.B = blk_len;
@@ -222,6 +234,32 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
                                             : fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
   return fd::launch_verify(p, g->in_dtype == FD_BF16, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws,
                            hip_stream);
+}
+
+}  // namespace
+
+int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,
+                   void* k_cache, void* v_cache, int64_t newest_frame, int32_t n_tail,
+                   int32_t blk_len, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
+  const int st = check_verify_args(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame, n_tail, blk_len, out);
+  if (st != FD_OK) return st;
+  if (!ws || ws_bytes < fd_verify_workspace_bytes(g, blk_len)) return FD_ERR_WORKSPACE;
+  if (!verify_aligned(q_blk, k_blk, v_blk, k_cache, v_cache, out) || !aligned16(ws)) return FD_ERR_ALIGN;
+  return launch_verify_checked(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame, n_tail, blk_len, out, ws,
+                               hip_stream);
+}
+
+int fd_verify_attn_noalloc(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,
+                           void* k_cache, void* v_cache, int64_t newest_frame, int32_t n_tail,
+                           int32_t blk_len, void* out, void* hip_stream) {
+  int st = check_verify_args(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame, n_tail, blk_len, out);
+  if (st != FD_OK) return st;
+  if (fd_verify_workspace_bytes(g, blk_len) > fd::kVerifyScratchBytes) return FD_ERR_SCRATCH;
+  if (!verify_aligned(q_blk, k_blk, v_blk, k_cache, v_cache, out)) return FD_ERR_ALIGN;
+  void* ws = fd::verify_scratch(&st);   // this device's static scratch array (no allocation)
+  if (!ws) return st;
+  return launch_verify_checked(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame, n_tail, blk_len, out, ws,
+                               hip_stream);
 }
 
 const char* fd_status_str(int status) {
@@ -235,6 +273,7 @@ const char* fd_status_str(int status) {
     case FD_ERR_TAIL: return "invalid tail / block length";
     case FD_ERR_WORKSPACE: return "workspace missing or too small";
     case FD_ERR_HIP: return "HIP launch failed";
+    case FD_ERR_SCRATCH: return "problem larger than the static scratch of fd_verify_attn_noalloc";
     default: return "unknown status";
   }
 }

@@ -93,6 +93,13 @@ inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
   return size_t(n_rb) * nseg * 2 * stream_partial_words(D) * sizeof(float);
 }
 
+// Static device scratch of fd_verify_attn_noalloc (a file-scope __device__ array, one copy per
+// GPU, held until the process ends): the verify workspace of any call it accepts.
+constexpr size_t kVerifyScratchBytes = FD_VERIFY_SCRATCH_BYTES;
+// This device's address of that array (looked up once per device with hipGetSymbolAddress);
+// nullptr with *status = FD_ERR_HIP if the lookup fails.
+void* verify_scratch(int* status);
+
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn,
                   int slot, void* stream);
 // kn / vn non-null: the new frames' K and V ([V][T][Hkv][D]) are inserted into ring slot

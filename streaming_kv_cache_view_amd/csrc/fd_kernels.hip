@@ -37,6 +37,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fd_internal.h"
@@ -2478,7 +2479,33 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 
+// Scratch of fd_verify_attn_noalloc: the split-KV partials of verify calls made by callers that
+// cannot allocate.  In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress (verify_scratch below), once per device.
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+
 }  // namespace
+
+void* verify_scratch(int* status) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = FD_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {   // first call on this device, with it current
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *status = FD_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
 
 int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* kn, const void* vn, int slot,
                   void* stream) {

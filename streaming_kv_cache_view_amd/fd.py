@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libfdattn.so")
 
 FD_F32, FD_BF16 = 0, 1
 STATUS = {0: "FD_OK", -1: "FD_ERR_NULL", -2: "FD_ERR_GEOM", -3: "FD_ERR_DTYPE", -4: "FD_ERR_FRAME",
-          -5: "FD_ERR_ALIGN", -6: "FD_ERR_TAIL", -7: "FD_ERR_WORKSPACE", -8: "FD_ERR_HIP"}
+          -5: "FD_ERR_ALIGN", -6: "FD_ERR_TAIL", -7: "FD_ERR_WORKSPACE", -8: "FD_ERR_HIP", -9: "FD_ERR_SCRATCH"}
+VERIFY_SCRATCH_BYTES = 32 << 20   # FD_VERIFY_SCRATCH_BYTES
 
 
 class FdGeom(ctypes.Structure):
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
         L.fd_verify_attn.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
         L.fd_verify_attn.restype = ctypes.c_int
+        L.fd_verify_attn_noalloc.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp]
+        L.fd_verify_attn_noalloc.restype = ctypes.c_int
         L.fd_status_str.argtypes, L.fd_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         _lib = L
     return _lib
@@ -70,7 +73,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
            "fd_stream_attn", "fd_stream_attn_insert", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
-           "fd_verify_attn", "fd_status_str")
+           "fd_verify_attn", "fd_verify_attn_noalloc", "fd_status_str")
 
 
 def make_geom(g, out_dtype: str = "f32") -> FdGeom:
@@ -184,3 +187,11 @@ def verify_attn(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame: int, n_t
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
         _ptr(v_cache), int(newest_frame), int(n_tail), int(blk_len), _ptr(out), _ptr(ws), int(ws_bytes),
         _stream(stream)))
+
+
+def verify_attn_noalloc(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame: int, n_tail: int, blk_len: int,
+                        out, out_dtype: str = "f32", stream=None):
+    """verify_attn without a workspace: the library's static per-GPU scratch holds the partials."""
+    _check("fd_verify_attn_noalloc", lib().fd_verify_attn_noalloc(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
+        _ptr(v_cache), int(newest_frame), int(n_tail), int(blk_len), _ptr(out), _stream(stream)))

@@ -155,8 +155,35 @@ def test_call_errors():
     assert L.fd_verify_attn(gp, *args, 2, 0, 8, FAKE, FAKE, ws, None) == -4
     assert L.fd_verify_attn(gp, *args, 5, 0, 8, MISALIGNED, FAKE, ws, None) == -5
     assert L.fd_verify_attn(gp, None, *args[1:], 5, 0, 8, FAKE, FAKE, ws, None) == -1
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert fd.lib().fd_status_str(code).decode() != "unknown status"
+
+
+def test_verify_noalloc_call_errors():
+    """The allocation-free verify: the same argument checks as fd_verify_attn, and a problem
+    whose workspace exceeds the static array is refused with FD_ERR_SCRATCH before any HIP call."""
+    L = fd.lib()
+    g = _g()
+    gp = ctypes.byref(g)
+    N = L.fd_verify_attn_noalloc
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert N(None, *args, 5, 0, 8, FAKE, None) == -1
+    assert N(gp, None, *args[1:], 5, 0, 8, FAKE, None) == -1
+    assert N(gp, *args, 5, 0, 8, None, None) == -1                 # no out
+    assert N(gp, *args, 2, 0, 8, FAKE, None) == -4
+    assert N(gp, *args, 5, -1, 8, FAKE, None) == -6
+    assert N(gp, *args, 5, 30, 8, FAKE, None) == -6
+    assert N(gp, *args, 5, 0, 8, MISALIGNED, None) == -5
+    # a window large enough that the partials of a 32-token block exceed 32 MiB
+    big = _g(n_views=8, n_frames=8, tok_per_frame=1024, prefix_len=0, n_q_heads=32, n_kv_heads=8,
+             head_dim=128, tail_cap=64)
+    need = L.fd_verify_workspace_bytes(ctypes.byref(big), 32)
+    assert need > fd.VERIFY_SCRATCH_BYTES
+    assert N(ctypes.byref(big), *args, 7, 0, 32, FAKE, None) == -9
+    # the backbone shapes fit: every block length up to 32
+    g4 = fd.make_geom(synth.CONFIGS[4].geom)
+    for b in (1, 8, 16, 32):
+        assert 0 < L.fd_verify_workspace_bytes(ctypes.byref(g4), b) <= fd.VERIFY_SCRATCH_BYTES
 
 
 def test_prefill_call_errors():

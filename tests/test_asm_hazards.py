@@ -38,7 +38,7 @@ def device_asm(tmp_path) -> str:
 
 
 def kernels(asm: str):
-    for name in re.findall(r"^(_Z\S+):", asm, re.M):
+    for name in re.findall(r"^\s*\.type\s+(_Z\S+),@function", asm, re.M):
         a = asm.index(name + ":")
         b = asm.index(".Lfunc_end", a)
         body = [x.strip() for x in asm[a:b].split("\n")]
