@@ -155,7 +155,9 @@ size_t fd_stream_workspace_bytes(const fd_geom* g);
  *   ws     : device workspace of ws_bytes >= fd_stream_workspace_bytes(g); the call first
  *            rotates every window key at its shifted position into it (the cache keeps
  *            the pre-RoPE keys), then attends over it.  No initial contents required;
- *            calls that share one workspace must not overlap.
+ *            calls that share one workspace must not overlap.  On return its first
+ *            Hkv*N*D elements (fp16 for bf16 inputs, fp32 for fp32) hold the rotated window,
+ *            [Hkv][N][D] in cache-row order: the k_view of fd_verify_attn_batched.
  *   Keys seen by token i of view v: the prefix, every frame of views < v, frames
  *   of view v older than the newest, and tokens <= i of view v's newest frame.
  *   newest_frame >= F-1 (full window); tail rows are not read.                      */
@@ -232,6 +234,52 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk,
                    void* k_cache, void* v_cache, int64_t newest_frame,
                    int32_t n_tail, int32_t blk_len,
                    void* out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Bytes of workspace fd_verify_attn_batched needs for n_drafts blocks of blk_len tokens (any
+ * tail lengths that fit in tail_cap); 0 on invalid arguments or fp32 inputs. */
+size_t fd_verify_batched_workspace_bytes(const fd_geom* g, int32_t n_drafts, int32_t blk_len);
+
+/* Speculative verify of n_drafts independent draft blocks over one window in one launch
+ * (README technique list, "Speculative reasoning"; Technical Summary, Methodology section 2:
+ * a drafted block is verified in one forward; Review, "Results": the draft block-size
+ * ablation).  Each draft is a separate continuation of the same window -- e.g. one per sampled
+ * trajectory -- with its own reasoning rows; one launch covers every draft, so the window's
+ * K and V blocks that several drafts read are served from the GPU's caches after the first.
+ * bf16 inputs only (FD_ERR_DTYPE otherwise).
+ *   n_drafts : 1 .. 8.
+ *   k_view  : NULL, or the window's keys already rotated at their positions for newest_frame:
+ *             [Hkv][N][D] fp16 in cache-row order (row x = cache row x rotated at the position
+ *             fd_key_position gives it).  The streaming calls (fd_stream_attn,
+ *             fd_stream_attn_insert, fd_prefill_attn) leave exactly this at the start of their
+ *             workspace, valid until the workspace is reused; fd_rotate_window writes it alone.
+ *             With a view the window's keys are read from it instead of being rotated again;
+ *             the cache stays pre-RoPE either way.  NULL: they are rotated here.
+ *   q_blk   : [n_drafts][B][Hq][D], k_blk, v_blk : [n_drafts][B][Hkv][D], pre-RoPE.
+ *   n_tails : HOST array of n_drafts reasoning-row counts.  Draft d's reasoning rows are cache
+ *             rows N + d*tail_stride + r (r < n_tails[d], written by the caller) at positions
+ *             pos_base + N + r; its block token b is copied into row N + d*tail_stride +
+ *             n_tails[d] + b and sits at position pos_base + N + n_tails[d] + b.
+ *   tail_stride : cache rows between consecutive drafts' tails (ignored for one draft).  Needs
+ *             n_tails[d] + B <= tail_stride for every draft but the last, and (n_drafts-1)*
+ *             tail_stride + n_tails[last] + B <= tail_cap (FD_ERR_TAIL otherwise).
+ *   out     : [n_drafts][B][Hq][D] out_dtype.  Draft d's token b sees the whole window, its own
+ *             n_tails[d] reasoning rows and its own block tokens <= b, nothing of other drafts.
+ *   ws      : as for fd_verify_attn (no initial contents required), ws_bytes >=
+ *             fd_verify_batched_workspace_bytes(g, n_drafts, B).
+ *   With n_drafts = 1 and no view this is fd_verify_attn.  1 <= B <= 32, G*B <= 128.  */
+int fd_verify_attn_batched(const fd_geom* g, int32_t n_drafts, const void* k_view,
+                           const void* q_blk, const void* k_blk, const void* v_blk,
+                           void* k_cache, void* v_cache, int64_t newest_frame,
+                           const int32_t* n_tails, int32_t tail_stride, int32_t blk_len,
+                           void* out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Rotate the window's keys at their positions for newest_frame into k_view (Positional
+ * Encoding passage: keys cached pre-RoPE, rotated at their shifted positions): k_view
+ * [Hkv][N][D] fp16 (bf16 inputs) or fp32 (fp32 inputs), cache-row order; the cache is only
+ * read.  The same rotation the streaming calls perform first; use it to give
+ * fd_verify_attn_batched a view when no streaming call ran on this window.  newest_frame >= F-1. */
+int fd_rotate_window(const fd_geom* g, const void* k_cache, int64_t newest_frame, void* k_view,
+                     void* hip_stream);
 
 /* Bytes of the static device array behind fd_verify_attn_noalloc (per GPU). */
 #define FD_VERIFY_SCRATCH_BYTES (32u << 20)

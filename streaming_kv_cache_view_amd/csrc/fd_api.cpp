@@ -193,9 +193,22 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
   if (blk_len > 32 || fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return 0;
   const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame,
                                      g->tail_cap);
-  const int S = fd::verify_splits(nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);   // the larger count
+  const int S = fd::verify_splits(nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
   return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * fd::verify_row_blocks(G, blk_len) * S *
-                                   fd::verify_partial_words(g->head_dim) * sizeof(float);
+                                                   fd::verify_partial_words(g->head_dim) * sizeof(float);
+}
+
+size_t fd_verify_batched_workspace_bytes(const fd_geom* g, int32_t n_drafts, int32_t blk_len) {
+  if (check_geom(g) != FD_OK || g->in_dtype != FD_BF16) return 0;
+  if (n_drafts < 1 || n_drafts > fd::kVerifyMaxDrafts || blk_len < 1 || blk_len > 32 || blk_len > g->tail_cap)
+    return 0;
+  const int G = g->n_q_heads / g->n_kv_heads;
+  if (fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return 0;
+  // every draft's tail fits in tail_cap: its key list is at most the window's plus tail_cap rows
+  const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame, g->tail_cap);
+  const int S = fd::verify_splits(nblk, fd::kVerifyWavesDma);
+  return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * n_drafts * fd::verify_row_blocks(G, blk_len) *
+                                                   S * fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
 
 namespace {
@@ -227,11 +240,14 @@ int launch_verify_checked(const fd_geom* g, const void* q_blk, const void* k_blk
   fd::KParams p = make_params(g, newest_frame);
   p.n_tail = n_tail;
   p.B = blk_len;
-  p.n_rb = fd::verify_row_blocks(p.G, blk_len);
+  p.n_drafts = 1;
+  p.tail_stride = 0;
+  p.n_tails[0] = n_tail;
+  p.nrb_d = fd::verify_row_blocks(p.G, blk_len);
+  p.n_rb = p.nrb_d;
   p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, n_tail + blk_len);
-  p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16
-                                            ? fd::kVerifyWavesDma * fd::kVerifyBlocksPerWaveDma
-                                            : fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
+  p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16 ? fd::kVerifyWavesDma
+                                                               : fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
   return fd::launch_verify(p, g->in_dtype == FD_BF16, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws,
                            hip_stream);
 }
@@ -247,6 +263,56 @@ int fd_verify_attn(const fd_geom* g, const void* q_blk, const void* k_blk, const
   if (!verify_aligned(q_blk, k_blk, v_blk, k_cache, v_cache, out) || !aligned16(ws)) return FD_ERR_ALIGN;
   return launch_verify_checked(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame, n_tail, blk_len, out, ws,
                                hip_stream);
+}
+
+int fd_verify_attn_batched(const fd_geom* g, int32_t n_drafts, const void* k_view, const void* q_blk,
+                           const void* k_blk, const void* v_blk, void* k_cache, void* v_cache,
+                           int64_t newest_frame, const int32_t* n_tails, int32_t tail_stride,
+                           int32_t blk_len, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (g->in_dtype != FD_BF16) return FD_ERR_DTYPE;
+  if (!q_blk || !k_blk || !v_blk || !k_cache || !v_cache || !out || !n_tails) return FD_ERR_NULL;
+  if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
+  if (n_drafts < 1 || n_drafts > fd::kVerifyMaxDrafts || blk_len < 1 || blk_len > 32) return FD_ERR_TAIL;
+  const int G = g->n_q_heads / g->n_kv_heads;
+  if (fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return FD_ERR_TAIL;
+  // draft d's rows W + d*tail_stride + [0, n_tails[d] + blk_len) inside the tail, without overlap
+  for (int d = 0; d < n_drafts; ++d) {
+    const int64_t need = int64_t(n_tails[d]) + blk_len;
+    if (n_tails[d] < 0) return FD_ERR_TAIL;
+    if (d + 1 < n_drafts && need > tail_stride) return FD_ERR_TAIL;
+    if (int64_t(d) * (n_drafts > 1 ? tail_stride : 0) + need > g->tail_cap) return FD_ERR_TAIL;
+  }
+  if (n_drafts > 1 && tail_stride < 1) return FD_ERR_TAIL;
+  if (!ws || ws_bytes < fd_verify_batched_workspace_bytes(g, n_drafts, blk_len)) return FD_ERR_WORKSPACE;
+  if (!verify_aligned(q_blk, k_blk, v_blk, k_cache, v_cache, out) || !aligned16(ws) || !aligned16(k_view))
+    return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, newest_frame);
+  p.B = blk_len;
+  p.n_drafts = n_drafts;
+  p.tail_stride = n_drafts > 1 ? tail_stride : 0;
+  int maxtail = 0;
+  for (int d = 0; d < n_drafts; ++d) {
+    p.n_tails[d] = n_tails[d];
+    maxtail = n_tails[d] > maxtail ? n_tails[d] : maxtail;
+  }
+  p.n_tail = n_tails[0];
+  p.nrb_d = fd::verify_row_blocks(p.G, blk_len);
+  p.n_rb = n_drafts * p.nrb_d;
+  p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, maxtail + blk_len);
+  p.n_split = fd::verify_splits(p.nblk, fd::kVerifyWavesDma);
+  return fd::launch_verify(p, 1, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws, hip_stream, k_view);
+}
+
+int fd_rotate_window(const fd_geom* g, const void* k_cache, int64_t newest_frame, void* k_view, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (!k_cache || !k_view) return FD_ERR_NULL;
+  if (newest_frame < g->n_frames - 1) return FD_ERR_FRAME;
+  if (!aligned16(k_cache) || !aligned16(k_view)) return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, newest_frame);
+  return fd::launch_rotate_window(p, g->in_dtype == FD_BF16, k_cache, k_view, hip_stream);
 }
 
 int fd_verify_attn_noalloc(const fd_geom* g, const void* q_blk, const void* k_blk, const void* v_blk,

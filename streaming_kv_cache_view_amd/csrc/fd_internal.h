@@ -13,8 +13,9 @@ constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
 constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
 constexpr int kVerifyWaves = 4;             // waves per verify workgroup, fp32 path
 constexpr int kVerifyBlocksPerWave = 1;
-constexpr int kVerifyWavesDma = 5;          // bf16 path (5: 31 splits x 8 kv heads at config 4, about one workgroup per CU)
-constexpr int kVerifyBlocksPerWaveDma = 1;
+constexpr int kVerifyWavesDma = 5;          // bf16 path: one 32-key block per wave (5: 31 splits x 8 kv
+                                            // heads at the backbone shapes, one workgroup per CU)
+constexpr int kVerifyMaxDrafts = 8;         // draft blocks verified by one batched call
 
 // Everything a kernel needs about one call, passed by value as a kernel argument.
 struct KParams {
@@ -39,9 +40,14 @@ struct KParams {
   int32_t whole;      // 0: the row block's segments laid end to end and cut into nseg equal
                       //    chunks (split segments merged by a second kernel);
                       // 1: chunk c is segment nseg-1-c whole (no split, no merge)
-  // verify
-  int32_t n_tail, B, nblk, n_split;
-  int32_t n_rb;       // 32-row blocks of the G*B verify query rows
+  // verify.  A call verifies n_drafts draft blocks of B tokens over one window; draft d's
+  // reasoning rows and block rows sit in cache rows W + d*tail_stride + [0, n_tails[d] + B).
+  int32_t n_tail, B, nblk, n_split;   // n_tail: draft 0's; nblk: key blocks of the longest key list
+  int32_t n_rb;       // 32-row blocks of every draft's G*B query rows: n_drafts * nrb_d
+  int32_t nrb_d;      // 32-row blocks of one draft's G*B query rows
+  int32_t n_drafts;
+  int32_t tail_stride;
+  int32_t n_tails[kVerifyMaxDrafts];
   int64_t pos_base;
   int64_t t;          // newest frame
   float sm_scale_log2;  // log2(e) / sqrt(D)
@@ -50,10 +56,17 @@ struct KParams {
   double inv_freq[kMaxHalf];  // theta^(-2i/D), fp64
 };
 
-// Verify split bookkeeping shared by host and kernels.
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Verify split bookkeeping shared by host and kernels.  A row block's keys are the window's
+// 32-key blocks (inside the prefix and inside each frame slot: contiguous positions) followed by
+// the 32-key blocks of its own draft's tail rows.
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int verify_window_blocks(int P, int V, int F, int T) {
+  return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock);
+}
 inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
-  return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock) + ceil_div(tail_rows, kVerifyBlock);
+  return verify_window_blocks(P, V, F, T) + ceil_div(tail_rows, kVerifyBlock);
 }
 // splits per kv head: each workgroup covers blocks_per_wg key blocks
 inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, blocks_per_wg); }
@@ -70,7 +83,6 @@ constexpr size_t kVerifyWsHeader = 256;
 // view cut between chunks leaves one (m, l, O) partial per piece, merged by a second kernel;
 // the workspace holds, after the rotated keys and queries, two partial slots per (row block,
 // chunk): a chunk's first job may continue a view, its last may be continued.
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
 // rotated, scaled queries (fp16, [rows][Hq][D]) after the rotated keys: rows = V*T (streaming)
 // or W (full window)
@@ -110,7 +122,12 @@ int launch_prefill(const KParams& p, const void* q, const void* kc, const void* 
                    void* stream);
 int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, const void* w, void* kc, void* vc,
                       void* stream);
+// kview non-null (bf16 only): the window's keys already rotated at their positions, fp16
+// [Hkv][W][D] (the streaming calls' workspace start, or launch_rotate_window), read instead of
+// rotating the window's keys in registers
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb,
-                  void* kc, void* vc, void* out, void* ws, void* stream);
+                  void* kc, void* vc, void* out, void* ws, void* stream, const void* kview = nullptr);
+// The rotation pass alone (keys only): kview [Hkv][W][D] of the QK^T operand type
+int launch_rotate_window(const KParams& p, int in_bf16, const void* kc, void* kview, void* stream);
 
 }  // namespace fd

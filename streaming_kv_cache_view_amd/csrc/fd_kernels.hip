@@ -207,6 +207,9 @@ constexpr int kWaitVm0 = 0x0F70;
 
 // s_waitcnt vmcnt(n), n < 64
 constexpr int wait_vm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt left at their maxima): this wave's LDS writes are done,
+// as a bare s_barrier requires before other waves read them
+constexpr int kWaitLgkm0 = 0xC07F;
 // LDS address of a pointer into __shared__ memory
 __device__ inline uint32_t lds_addr(const void* p) {
   typedef __attribute__((address_space(3))) const void lvoid;
@@ -1956,227 +1959,228 @@ __global__ __launch_bounds__(256) void verify_split_kernel(const KParams p, cons
 }
 
 // ---------------------------------------------------------------------------------------
-// Verify for bf16 inputs, split-KV part.  Rows: r = hh*B + b (query head kvh*G + hh, block
-// token b), in 32-row MFMA blocks, one workgroup per (kv head, row block, split).  Keys are numbered by cache row x: window rows [0, W),
-// reasoning rows [W, W+n_tail), block rows [W+n_tail, W+n_tail+B) (read from k_blk / v_blk
-// and copied into the cache here).  They are cut into 32-key blocks inside segments of
-// contiguous positions; wave w of split s (kVerifyWavesDma = NW waves) takes block NW*s + w.
-// Five waves per workgroup make about one workgroup per CU at the backbone shapes (31 splits
-// x 8 kv heads); eight (two per SIMD, 19 splits) measured 3 % slower.
+// Verify for bf16 inputs, split-KV part.  A call verifies n_drafts draft blocks of B tokens over
+// one window.  Draft d's query rows r = hh*B + b (query head kvh*G + hh, block token b) form nrb_d
+// 32-row MFMA blocks; row block rb (of draft rb / nrb_d) attends to the window's keys and then to
+// its own draft's tail: reasoning rows W + d*tail_stride + [0, n_tails[d]) and the block rows
+// after them, which are read from k_blk / v_blk (and copied into the cache here).  Keys are cut
+// into 32-key blocks inside segments of contiguous positions (the prefix, each frame slot, the
+// tail).  One workgroup per (kv head, row block, split); its NW waves take one key block each.
 //
-// The kernel is a single pass over HBM: every K and V byte of the workgroup's blocks (16 KB
-// per block for D = 128) is requested at once, straight into LDS (global_load_lds).  Each wave
-// proceeds as soon as its own block has landed: keys are rotated (LDS -> registers, at their
-// current positions; cos / sin per lane from the hardware units), QK^T / softmax / PV run,
-// and the waves fold into one (m, l, O) partial per (kv head, split), in a fixed order.
+// Every global read of a workgroup is issued up front, straight into LDS (global_load_lds from
+// per-lane addresses): the row block's raw query rows (each wave fetches a share), then each
+// wave's K block, then its V block.  Vector memory operations complete in issue order, so a wave
+// waits for its queries and keys alone, rotates them and runs Q K^T and the softmax while its
+// values are still landing; only P V waits for them.
+//   * The queries are rotated once per workgroup, cooperatively, in LDS.
+//   * A key's angle is its block's base angle (in revolutions, fraction taken in fp64 once per
+//     wave and frequency) plus its offset in the block times the frequency (fp32), then the
+//     hardware sin / cos.
+//   * With a rotated window view (VIEW), window blocks arrive already rotated (fp16) and only
+//     tail blocks are rotated here.
+// The waves fold into one (m, l, O) partial per (kv head, row block, split), in a fixed order;
+// verify_merge_kernel combines the splits.
 // ---------------------------------------------------------------------------------------
-template <int D, int NRB>   // NRB: 32-row blocks of query rows per workgroup (1 or 2)
-__global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const bf16* __restrict__ qb,
-                                                         const bf16* __restrict__ kb,
-                                                         const bf16* __restrict__ vb, bf16* __restrict__ kc,
-                                                         bf16* __restrict__ vc, float* __restrict__ part) {
+
+// Direct global -> LDS load of 16 bytes per lane from a per-lane 64-bit global address (no scalar
+// base register), landing at LDS lds + 16*lane (lds wave-uniform).  From inline assembly: the
+// compiler does not see the load, so the caller orders it with explicit s_waitcnt vmcnt; one
+// wait state follows the write of M0.
+__device__ inline void g2lds16_va(const void* gaddr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "{m0}"(lds) : "memory");
+}
+
+// Key block j of a row block of draft d (the window's blocks, then the draft's tail blocks):
+// first cache row, length (0: past the list), position of its first key, and the cache row of
+// the draft's block token 0 (rows from there on come from k_blk / v_blk).
+struct VerifyBlock {
+  int x0, len, tailbase;
+  int64_t pos0;
+};
+__device__ inline VerifyBlock verify_block(const KParams& p, int d, int j) {
+  const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
+  const int trow0 = p.W + d * p.tail_stride, ntd = p.n_tails[d];
+  VerifyBlock b{0, 0, trow0 + ntd, 0};
+  if (j < nbp) {
+    b.x0 = 32 * j;
+    b.len = min(32, p.P - b.x0);
+    b.pos0 = p.pos_base + b.x0;
+  } else if (j - nbp < nslot * nbs) {
+    const int jj = j - nbp, vs = jj / nbs, st = 32 * (jj % nbs);
+    b.x0 = p.P + vs * p.T + st;
+    b.len = min(32, p.T - st);
+    b.pos0 = slot_pos(p, vs / p.F, vs % p.F) + st;
+  } else {
+    const int st = 32 * (j - nbp - nslot * nbs);
+    if (st < ntd + p.B) {
+      b.x0 = trow0 + st;
+      b.len = min(32, ntd + p.B - st);
+      b.pos0 = p.pos_base + p.W + st;
+    }
+  }
+  return b;
+}
+
+template <int D, bool VIEW>
+__global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
+    const KParams p, const bf16* __restrict__ qb, const bf16* __restrict__ kb, const bf16* __restrict__ vb,
+    bf16* __restrict__ kc, bf16* __restrict__ vc, const _Float16* __restrict__ kview, float* __restrict__ part) {
   using QK = F16Ops;
   using PV = BF16Ops;
+  constexpr int NW = kVerifyWavesDma;            // waves per workgroup, one key block each
+  constexpr int NT = 64 * NW;
   constexpr int E = 8;
   constexpr int H2 = D / 2;
   constexpr int NU = D / 16;                     // QK^T k-steps (chunks 2u + h)
   constexpr int ND = D / 32;
-  constexpr int ROWB = D * 2;                    // K / V row bytes
+  constexpr int ROWB = D * 2;                    // K / V / Q row bytes
   constexpr int KCH = ROWB / 16;                 // 16-byte chunks per row
-  constexpr int BLKB = 32 * ROWB;                // one 32-key block of K (or V)
-  constexpr int NIB = BLKB / 1024;               // direct loads per block and matrix
-  constexpr int NW = kVerifyWavesDma;           // waves per workgroup
-  constexpr int NBW = kVerifyBlocksPerWaveDma;   // blocks per wave
+  constexpr int RPL = 1024 / ROWB;               // rows per 1 KB direct load
+  constexpr int BLKB = 32 * ROWB;                // 32 rows of K, V or Q
+  constexpr int NIB = BLKB / 1024;               // direct loads per 32 rows
+  constexpr int NQW = (NIB + NW - 1) / NW;       // query loads per wave (the last waves one fewer)
   constexpr int OS = D + 4;
-  constexpr int KVB = NW * NBW * BLKB;           // K (or V) bytes of the workgroup
-  static_assert(4 * 32 * OS * 4 <= 2 * KVB, "merge slots alias the K / V tiles");
-  static_assert(NW >= 4 && NW <= 8, "the fold: four slots, at most one adding wave each");
+  constexpr int KVB = NW * BLKB;                 // K (or V) bytes of the workgroup
   constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
+  constexpr int CPR = D / 4;                     // 4-float chunks per output row
+  static_assert(NW >= 4 && NW <= 8, "the fold: four slots, at most one adding wave each");
+  static_assert(4 * 32 * OS * 4 <= 2 * KVB + BLKB, "fold slots alias the tiles");
   auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
   auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
-
-  __shared__ __attribute__((aligned(16))) unsigned char kvbuf[2 * KVB];   // K tiles, then V tiles
-  unsigned char* const kbuf = kvbuf;
-  unsigned char* const vbuf = kvbuf + KVB;
-  __shared__ double frev[H2];                    // theta^(-2i/D) / (2 pi): revolutions per position
-  __shared__ float red_m[NW][32], red_l[NW][32];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  // blockIdx.x = (split * nrbg + rbg) * Hkv + kvh, nrbg = ceil(n_rb / NRB): the row-block
-  // groups of one split run side by side on one XCD and read the same K / V.  The workgroup
-  // takes row blocks NRB*rbg + r (r < NRB, those < n_rb): its keys are loaded and rotated once
-  // for all of them.
-  const int nrbg = (p.n_rb + NRB - 1) / NRB;
-  const int kvh = blockIdx.x % p.Hkv, rbg = (blockIdx.x / p.Hkv) % nrbg, split = blockIdx.x / (p.Hkv * nrbg);
-  int bq[NRB], head[NRB];
-  bool qvalid[NRB], rbvalid[NRB];
-#pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-    const int rb = NRB * rbg + r, qr = 32 * rb + l32, hh = qr / p.B;   // query row qr = hh*B + b
-    rbvalid[r] = rb < p.n_rb;
-    bq[r] = qr % p.B;
-    qvalid[r] = rbvalid[r] && hh < p.G;
-    head[r] = kvh * p.G + (qvalid[r] ? hh : 0);
-  }
-  const int tailbase = p.W + p.n_tail;   // cache row of block token 0
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
 
-  // ---- rotation frequencies, in revolutions per position (computed: a table load from the
-  // kernel arguments would queue behind the K/V loads below)
-  if (tid < H2) frev[tid] = exp2(-(2.0 * tid / D) * p.log2_theta) * 0.15915494309189535;
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * KVB + BLKB];   // K, V, query rows
+  __shared__ double frev[H2];                    // theta^(-2i/D) / (2 pi): revolutions per position
+  __shared__ float gf[H2];                       // the same in fp32
+  __shared__ float frb[NW][H2];                  // fraction of each wave's block base angle
+  __shared__ float red_m[NW][32], red_l[NW][32];
+  unsigned char* const kbuf = tiles;
+  unsigned char* const vbuf = tiles + KVB;
+  unsigned char* const qbuf = tiles + 2 * KVB;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  // blockIdx.x = (split * n_rb + rb) * Hkv + kvh: the row blocks of one split run side by side on
+  // one XCD and read the same window K / V (one HBM read, the rest from L2)
+  const int kvh = blockIdx.x % p.Hkv, rb = (blockIdx.x / p.Hkv) % p.n_rb, split = blockIdx.x / (p.Hkv * p.n_rb);
+  const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;   // draft, row block within the draft
+  const int qr = 32 * rbl + l32, bq = qr % p.B;          // this lane's query row, its block token
+
+  // ---- rotation frequencies (before any direct load: __syncthreads waits for vector memory)
+  if (tid < H2) {
+    const double f = exp2(-(2.0 * tid / D) * p.log2_theta) * kInvTwoPi;
+    frev[tid] = f;
+    gf[tid] = static_cast<float>(f);
+  }
   __syncthreads();
-  // this lane's frequencies are 16u + 8h + e (u < NU/2, e < 8): four bases from the table
-  // (read before any direct load: LDS reads after them would wait for their completion) and
-  // the ratio rho = theta^(-2/D) between consecutive frequencies
-  double fbase[NU / 2];
-#pragma unroll
-  for (int u = 0; u < NU / 2; ++u) fbase[u] = frev[2 * E * u + E * h];
-  const double rho = exp2(-(2.0 / D) * p.log2_theta);
 
-  // ---- this wave's key blocks
-  const int nbp = (p.P + 31) / 32, nbs = (p.T + 31) / 32, nslot = p.V * p.F;
-  int x0[NBW], len[NBW];
-  int64_t pos0[NBW];
-#pragma unroll
-  for (int lb = 0; lb < NBW; ++lb) {
-    const int j = split * NW * NBW + NBW * w + lb;
-    x0[lb] = 0;
-    len[lb] = 0;
-    pos0[lb] = 0;
-    if (j < p.nblk) {
-      if (j < nbp) {
-        x0[lb] = 32 * j;
-        len[lb] = min(32, p.P - x0[lb]);
-        pos0[lb] = p.pos_base + x0[lb];
-      } else if (j - nbp < nslot * nbs) {
-        const int jj = j - nbp, vs = jj / nbs, st = 32 * (jj % nbs);
-        x0[lb] = p.P + vs * p.T + st;
-        len[lb] = min(32, p.T - st);
-        pos0[lb] = slot_pos(p, vs / p.F, vs % p.F) + st;
-      } else {
-        const int st = 32 * (j - nbp - nslot * nbs);
-        x0[lb] = p.W + st;
-        len[lb] = min(32, p.n_tail + p.B - st);
-        pos0[lb] = p.pos_base + p.W + st;
-      }
-    }
-    x0[lb] = uni(x0[lb]);
-    len[lb] = uni(len[lb]);
-  }
+  // ---- this wave's key block (wave-uniform); rotated here unless the view holds it rotated
+  const VerifyBlock kbk = verify_block(p, d, split * NW + w);
+  const int x0 = uni(kbk.x0), klen = uni(kbk.len), tailbase = uni(kbk.tailbase);
+  const bool rot = !VIEW || x0 >= p.W;
+  // global row x of kv head kvh: a cache row, or (x >= tailbase) a row of the draft's block
+  auto row_of = [&](const bf16* cache, const bf16* blk, int x) -> const unsigned char* {
+    return reinterpret_cast<const unsigned char*>(
+        x >= tailbase ? blk + (static_cast<int64_t>(d * p.B + x - tailbase) * p.Hkv + kvh) * D
+                      : cache + (static_cast<int64_t>(kvh) * p.S_cap + x) * D);
+  };
 
-  // ---- queries (registers) and every K / V byte of the workgroup (LDS), all in flight
-  u32x4 qraw[NRB][NU];
+  // ---- every global read in flight: this wave's share of the query rows, its K block, its V
+  // block.  32-row tiles land row r at LDS row r with 16-byte chunk c at position c ^ swz(r).
+  const uint32_t lq = lds_addr(qbuf), lk = uni(lds_addr(kbuf) + w * BLKB), lv = uni(lds_addr(vbuf) + w * BLKB);
 #pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-    const bf16* qsrc = qb + (static_cast<int64_t>(bq[r]) * p.Hq + head[r]) * D;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) qraw[r][u] = ld16(qsrc + 2 * E * u + E * h);   // invalid rows: zeroed below
+  for (int i0 = 0; i0 < NQW; ++i0) {
+    const int i = w + NW * i0;
+    if (i >= NIB) break;   // wave-uniform
+    const int r = RPL * i + lane / KCH, pc = lane % KCH;
+    const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B;
+    const int hq = hh2 < p.G ? hh2 : 0, b2 = hh2 < p.G ? qr2 % p.B : 0;   // rows past G*B: any valid row
+    const bf16* src = qb + (static_cast<int64_t>(d * p.B + b2) * p.Hq + kvh * p.G + hq) * D;
+    g2lds16_va(src + 8 * (pc ^ kswz(r)), uni(lq + i * 1024));
   }
-  // direct loads of this wave's block, interleaved with the (cos, sin) of its key's 32 RoPE
-  // angles (they depend on positions only), so the wave computes while the memory pipe drains
-  static_assert(NBW == 1, "one key block per wave");
-  float2 kcs[NU / 2][E];
-  {
-    unsigned char* Kt = kbuf + w * BLKB;
-    unsigned char* Vt = vbuf + w * BLKB;
-    const uint32_t lr = static_cast<uint32_t>(max(len[0], 1) - 1);
-    const double kpos = static_cast<double>(pos0[0] + l32);
+  if (klen > 0) {
+    const uint32_t lr = static_cast<uint32_t>(klen - 1);   // rows past the block's end: its last row (masked)
 #pragma unroll
     for (int m = 0; m < NIB; ++m) {
-      if (len[0] > 0) {
-        const uint32_t pos = m * 64 + lane, r = min(pos / KCH, lr), c = pos % KCH;
-        const int x = x0[0] + static_cast<int>(r);
-        const bf16* krow = x >= tailbase ? kb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                                         : kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-        const bf16* vrow = x >= tailbase ? vb + (static_cast<int64_t>(x - tailbase) * p.Hkv + kvh) * D
-                                         : vc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-        g2lds16(krow + 8 * (c ^ kswz(pos / KCH)), Kt + m * 1024);
-        g2lds16(vrow + 8 * (c ^ vswz(pos / KCH)), Vt + m * 1024);
-      }
-      if (m < NU / 2) {
-        double f = fbase[m];
+      const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
+      const int x = x0 + static_cast<int>(min(r, lr));
+      const unsigned char* src =
+          rot ? row_of(kc, kb, x) : reinterpret_cast<const unsigned char*>(kview + (static_cast<int64_t>(kvh) * p.W + x) * D);
+      g2lds16_va(src + 16 * (c ^ kswz(r)), lk + m * 1024);
+    }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kcs[m][e] = cs_rev(kpos * f);
-          asm volatile("" : "+v"(kcs[m][e].x), "+v"(kcs[m][e].y));   // computed here, not sunk
-          f *= rho;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < NIB; ++m) {
+      const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
+      g2lds16_va(row_of(vc, vb, x0 + static_cast<int>(min(r, lr))) + 16 * (c ^ vswz(r)), lv + m * 1024);
     }
   }
 
-  // ---- queries rotated at their positions, scaled into log2 units, rounded to fp16 (their
-  // loads were issued first, so this waits for them only, while the K / V loads land)
-  u32x4 qf[NRB][NU];
-#pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-    float fq[NU][E];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) BF16Ops::unpack(qraw[r][u], fq[u]);
-    const float qs = qvalid[r] ? p.sm_scale_log2 : 0.f;   // rows past G*B: zero queries
-    const double qpos = static_cast<double>(p.pos_base + tailbase + bq[r]);
+  // ---- (cos, sin) of this lane's key (row l32 of the block) at its 32 frequencies, while the
+  // loads are in flight: revolutions = frac(pos0 * f) (fp64, one frequency per lane, through LDS)
+  // + l32 * f (fp32), then the hardware sin / cos on the fraction
+  float2 kcs[NU / 2][E];
+  if (rot && klen > 0) {
+    if (lane < H2) {
+      const double rv = static_cast<double>(kbk.pos0) * frev[lane];
+      frb[w][lane] = static_cast<float>(rv - rint(rv));
+    }
+    const float fl = static_cast<float>(l32);
 #pragma unroll
     for (int u = 0; u < NU / 2; ++u) {
-      double f = fbase[u];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float2 cq = cs_rev(qpos * f);
-        f *= rho;
-        const float a = fq[u][e], b = fq[u + NU / 2][e];
-        fq[u][e] = (a * cq.x - b * cq.y) * qs;
-        fq[u + NU / 2][e] = (b * cq.x + a * cq.y) * qs;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) qf[r][u] = QK::pack(fq[u]);
-  }
-
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's K / V have landed (no other wave's
-                                          // LDS is read before the final merge)
-
-  // ---- block rows: into the cache (their K / V came from k_blk / v_blk)
-#pragma unroll
-  for (int lb = 0; lb < NBW; ++lb) {
-    if (rbg != 0 || len[lb] <= 0 || x0[lb] + len[lb] <= tailbase) continue;
-    const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
-    const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
-    for (int e = lane; e < 32 * KCH; e += 64) {
-      const int r = e / KCH, c = e % KCH, x = x0[lb] + r;
-      if (r < len[lb] && x >= tailbase) {
-        const int64_t dst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 8 * c;
-        st16(kc + dst, ld16(Kt + r * ROWB + ((c ^ kswz(r)) << 4)));
-        st16(vc + dst, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
+        const int i = 2 * E * u + E * h + e;
+        const float rv = __builtin_fmaf(fl, gf[i], frb[w][i]);
+        const float f = rv - rintf(rv);
+        kcs[u][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+        asm volatile("" : "+v"(kcs[u][e].x), "+v"(kcs[u][e].y));   // computed here, not sunk
       }
     }
   }
 
-  // lane constants of the PV operand reads (V^T through transposing reads)
-  const int key0 = 4 * h + ((lane & 15) >> 2);
-  int voff[ND];
+  // ---- queries: this wave's share has landed once at most its K and V loads are pending; the
+  // barrier makes every share visible.  Rotated once per workgroup in LDS (in place, fp16, scaled
+  // into log2 units; rows past G*B zero): thread (row, chunk pair) of the first 32*KCH/2 threads.
+  if (klen > 0) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NIB));
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  wg_barrier();
+  if (tid < 32 * (KCH / 2)) {
+    const int r = tid / (KCH / 2), cp = tid % (KCH / 2);
+    const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B, b2 = qr2 % p.B;
+    const float qs = hh2 < p.G ? p.sm_scale_log2 : 0.f;
+    const double qpos = static_cast<double>(p.pos_base + p.W + p.n_tails[d] + b2);
+    unsigned char* c1 = qbuf + r * ROWB + ((cp ^ kswz(r)) << 4);
+    unsigned char* c2 = qbuf + r * ROWB + (((cp + KCH / 2) ^ kswz(r)) << 4);
+    float x1[E], x2[E];
+    BF16Ops::unpack(ld16(c1), x1);
+    BF16Ops::unpack(ld16(c2), x2);
 #pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const int cb2 = (32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-    voff[d] = key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+    for (int e = 0; e < E; ++e) {
+      const float2 cq = cs_rev(qpos * frev[E * cp + e]);
+      const float a = x1[e], b = x2[e];
+      x1[e] = (a * cq.x - b * cq.y) * qs;
+      x2[e] = (b * cq.x + a * cq.y) * qs;
+    }
+    st16(c1, QK::pack(x1));
+    st16(c2, QK::pack(x2));
   }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the rotated queries are in LDS ...
+  wg_barrier();                              // ... for every wave (the K / V loads stay in flight)
+  u32x4 qf[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) qf[u] = ld16(qbuf + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
 
-  f32x16 o[NRB][ND];
-  float m_run[NRB], l_run[NRB];
+  f32x16 o[ND];
 #pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-#pragma unroll
-    for (int d = 0; d < ND; ++d) o[r][d] = f32x16{};
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
-#pragma unroll
-  for (int lb = 0; lb < NBW; ++lb) {
-    if (len[lb] <= 0) continue;
-    const unsigned char* Kt = kbuf + (NBW * w + lb) * BLKB;
-    const unsigned char* Vt = vbuf + (NBW * w + lb) * BLKB;
-    // K row l32 (both halves of every RoPE pair), rotated at its position, fp16
+  for (int dd = 0; dd < ND; ++dd) o[dd] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const unsigned char* Kt = kbuf + w * BLKB;
+  const unsigned char* Vt = vbuf + w * BLKB;
+  u32x4 pb[2];
+  if (klen > 0) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(NIB));   // K has landed (V may still be in flight)
+    // K row l32 (both halves of every RoPE pair): rotated here, or read rotated from the view
     u32x4 kf[NU];
-    {
+    if (rot) {
       float fk[2][E];
 #pragma unroll
       for (int u = 0; u < NU / 2; ++u) {
@@ -2192,60 +2196,70 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
         kf[u] = QK::pack(fk[0]);
         kf[u + NU / 2] = QK::pack(fk[1]);
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) kf[u] = ld16(Kt + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
+    }
+    f32x16 sv = f32x16{};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) sv = QK::mma(kf[u], qf[u], sv);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+      const bool ok = (kk < klen) & ((x0 + kk - tailbase) <= bq);   // block rows: causal
+      sv[i] = ok ? sv[i] : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    m_run = xhalf_max(mx);
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+      l_run += sv[i];
     }
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) {   // the rotated keys serve every row block of the workgroup
-      f32x16 s = f32x16{};
+    for (int cc = 0; cc < 2; ++cc) {
+      float pv[E];
 #pragma unroll
-      for (int u = 0; u < NU; ++u) s = QK::mma(kf[u], qf[r][u], s);
-      float mx = -INFINITY;
+      for (int e = 0; e < E; ++e) pv[e] = sv[E * cc + e];
+      pb[cc] = PV::pack(pv);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // V has landed
+  if (klen > 0) {
+    const int key0 = 4 * h + ((lane & 15) >> 2);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool ok = (kk < len[lb]) & ((x0[lb] + kk - tailbase) <= bq[r]);
-        s[i] = ok ? s[i] : -INFINITY;
-        mx = fmaxf(mx, s[i]);
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int dd = 0; dd < ND; ++dd) {
+        const int cb2 = (32 * dd + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+        const int voff = key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+        const u32x2 lo = ds_read_tr16(Vt + voff + 16 * cc * ROWB);
+        const u32x2 hi = ds_read_tr16(Vt + voff + (16 * cc + 8) * ROWB);
+        o[dd] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[cc], o[dd]);
       }
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run[r], mx);
-      const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[r] - mu);
-      l_run[r] *= alpha;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) o[r][d] *= alpha;
-      m_run[r] = m_new;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = __builtin_amdgcn_exp2f(s[i] - mu);
-        l_run[r] += s[i];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        float pv[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) pv[e] = s[E * cc + e];
-        const u32x4 bop = PV::pack(pv);
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const u32x2 lo = ds_read_tr16(Vt + voff[d] + 16 * cc * ROWB);
-          const u32x2 hi = ds_read_tr16(Vt + voff[d] + (16 * cc + 8) * ROWB);
-          o[r][d] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, bop, o[r][d]);
+    }
+    // the draft's block rows into the cache (their K / V came from k_blk / v_blk), once per draft
+    if (rbl == 0 && x0 + klen > tailbase) {
+      for (int e = lane; e < 32 * KCH; e += 64) {
+        const int r = e / KCH, c = e % KCH, x = x0 + r;
+        if (r < klen && x >= tailbase) {
+          const int64_t dst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 8 * c;
+          st16(kc + dst, ld16(Kt + r * ROWB + ((c ^ kswz(r)) << 4)));
+          st16(vc + dst, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
         }
       }
     }
   }
-  __syncthreads();   // K / V tiles are dead: the space is reused for the merge
+  __syncthreads();   // K / V tiles are dead: the space is reused for the fold
 
-  // ---- per row block: fold the waves (same rows, different keys) into one partial, in a
-  // fixed order: waves 0-3 write their rescaled O to four LDS slots, waves 4.. add theirs to
-  // slot w - 4, the four slots are summed in slot order.
-#pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-  if (!rbvalid[r]) break;   // uniform: row blocks past n_rb
-  if (r > 0) __syncthreads();   // the previous row block's slots have been read
-  const float l_tot = xhalf_sum(l_run[r]);
+  // ---- fold the waves (same rows, different keys) into one partial, in a fixed order: waves 0-3
+  // write their rescaled O to four LDS slots, waves 4.. add theirs to slot w - 4, the four slots are
+  // summed in slot order
+  const float l_tot = xhalf_sum(l_run);
   if (lane < 32) {
-    red_m[w][l32] = m_run[r];
+    red_m[w][l32] = m_run;
     red_l[w][l32] = l_tot;
   }
   __syncthreads();
@@ -2256,33 +2270,28 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww)
     if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
-  const float scale = (m_run[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[r] - M);
-  float* obuf = reinterpret_cast<float*>(kvbuf);   // four slots of 32 x OS floats
+  const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  float* obuf = reinterpret_cast<float*>(tiles);   // four slots of 32 x OS floats
   float* ob = obuf + (w & 3) * 32 * OS;
-  if (w < 4) {
+  auto put = [&](bool add) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        const f32x4 rv = {o[r][d][4 * ig] * scale, o[r][d][4 * ig + 1] * scale, o[r][d][4 * ig + 2] * scale, o[r][d][4 * ig + 3] * scale};
-        *reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h) = rv;
-      }
-  }
-  __syncthreads();
-  if (w >= 4) {
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
+    for (int dd = 0; dd < ND; ++dd)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
-        f32x4* dst = reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * d + 8 * ig + 4 * h);
-        const f32x4 rv = {o[r][d][4 * ig] * scale, o[r][d][4 * ig + 1] * scale, o[r][d][4 * ig + 2] * scale, o[r][d][4 * ig + 3] * scale};
-        *dst = *dst + rv;
+        f32x4* dst = reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * dd + 8 * ig + 4 * h);
+        const f32x4 rv = {o[dd][4 * ig] * scale, o[dd][4 * ig + 1] * scale, o[dd][4 * ig + 2] * scale, o[dd][4 * ig + 3] * scale};
+        *dst = add ? *dst + rv : rv;
       }
-  }
+  };
+  if (w < 4) put(false);
   __syncthreads();
-  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + NRB * rbg + r) * p.n_split + split) * verify_partial_words(D);
-  for (int e = tid; e < 32 * D / 4; e += 64 * NW) {
-    const int row = e / (D / 4), c = e % (D / 4);
+  if constexpr (NW > 4) {
+    if (w >= 4) put(true);
+    __syncthreads();
+  }
+  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + split) * verify_partial_words(D);
+  for (int e = tid; e < 32 * CPR; e += NT) {
+    const int row = e / CPR, c = e % CPR;
     f32x4 a = *reinterpret_cast<const f32x4*>(obuf + row * OS + 4 * c);
 #pragma unroll
     for (int sl = 1; sl < 4; ++sl) a = a + *reinterpret_cast<const f32x4*>(obuf + sl * 32 * OS + row * OS + 4 * c);
@@ -2291,7 +2300,6 @@ __global__ __launch_bounds__(512) void verify_dma_kernel(const KParams p, const 
   if (w == 0 && lane < 32) {
     dstp[32 * D + l32] = M;
     dstp[32 * D + 32 + l32] = L;
-  }
   }
 }
 
@@ -2305,7 +2313,8 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
   constexpr int MAXF = 8;   // splits folded per thread per pass
   const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;   // kv head k on the XCD that wrote it
   const int rr = r % 32;                                        // row within row block r / 32
-  const int hh = r / p.B, b = r % p.B;
+  const int dft = (r / 32) / p.nrb_d, rl = r - 32 * p.nrb_d * dft;   // draft, row within the draft
+  const int hh = rl / p.B, b = rl % p.B;
   if (hh >= p.G) return;
   const int cpr = p.D / 4;                    // 4-float chunks per row
   const int sg = threadIdx.x / cpr, c = threadIdx.x % cpr;
@@ -2363,7 +2372,7 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
     At += f * sA[g * cpr + c];
   }
   const f32x4 res = At * (1.f / Lt);
-  const int64_t oidx = (static_cast<int64_t>(b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
+  const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
   if (p.out_bf16) {
     bf16 b4[4] = {static_cast<bf16>(res[0]), static_cast<bf16>(res[1]), static_cast<bf16>(res[2]), static_cast<bf16>(res[3])};
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + oidx) = *reinterpret_cast<const u32x2*>(b4);
@@ -2457,17 +2466,18 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
 
 template <typename T, int D>
 int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void* vb, void* kc, void* vc,
-                    void* out, void* ws, hipStream_t st) {
+                    void* out, void* ws, hipStream_t st, const void* kview) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
   if constexpr (std::is_same<T, bf16>::value) {
-    if (p.n_rb >= 2)   // two row blocks per workgroup: each key rotated once for both
-      hipLaunchKernelGGL((verify_dma_kernel<D, 2>), dim3(p.Hkv * ((p.n_rb + 1) / 2) * p.n_split),
-                         dim3(64 * kVerifyWavesDma), 0, st, p, static_cast<const T*>(qb), static_cast<const T*>(kb),
-                         static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc), part);
+    const dim3 grid(p.Hkv * p.n_rb * p.n_split), block(64 * kVerifyWavesDma);
+    if (kview)
+      hipLaunchKernelGGL((verify_dma_kernel<D, true>), grid, block, 0, st, p, static_cast<const T*>(qb),
+                         static_cast<const T*>(kb), static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc),
+                         static_cast<const _Float16*>(kview), part);
     else
-      hipLaunchKernelGGL((verify_dma_kernel<D, 1>), dim3(p.Hkv * p.n_split), dim3(64 * kVerifyWavesDma), 0, st, p,
-                         static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
-                         static_cast<T*>(kc), static_cast<T*>(vc), part);
+      hipLaunchKernelGGL((verify_dma_kernel<D, false>), grid, block, 0, st, p, static_cast<const T*>(qb),
+                         static_cast<const T*>(kb), static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc),
+                         static_cast<const _Float16*>(nullptr), part);
   } else {
     hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(256), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
@@ -2476,6 +2486,19 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
                      static_cast<const float*>(part), out);
+  return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
+}
+
+// The rotation pass alone (keys only, no queries, no tile table, no insert).
+template <typename T, int D>
+int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStream_t st) {
+  constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
+  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
+  const int nkb = (p.W + 127) / 128;
+  hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb, p.Hkv), dim3(256), 0, st, p, static_cast<const T*>(kc),
+                     static_cast<typename Path<T>::QKT*>(kview), aligned, nkb, static_cast<const T*>(nullptr),
+                     static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr),
+                     NewFrame<T>{nullptr, nullptr, nullptr, nullptr});
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 
@@ -2546,14 +2569,21 @@ int launch_prefill(const KParams& p, const void* q, const void* kc, const void* 
 }
 
 int launch_verify(const KParams& p, int in_bf16, const void* qb, const void* kb, const void* vb, void* kc,
-                  void* vc, void* out, void* ws, void* stream) {
+                  void* vc, void* out, void* ws, void* stream, const void* kview) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_bf16) {
-    return p.D == 128 ? launch_verify_t<bf16, 128>(p, qb, kb, vb, kc, vc, out, ws, st)
-                      : launch_verify_t<bf16, 64>(p, qb, kb, vb, kc, vc, out, ws, st);
+    return p.D == 128 ? launch_verify_t<bf16, 128>(p, qb, kb, vb, kc, vc, out, ws, st, kview)
+                      : launch_verify_t<bf16, 64>(p, qb, kb, vb, kc, vc, out, ws, st, kview);
   }
-  return p.D == 128 ? launch_verify_t<float, 128>(p, qb, kb, vb, kc, vc, out, ws, st)
-                    : launch_verify_t<float, 64>(p, qb, kb, vb, kc, vc, out, ws, st);
+  return p.D == 128 ? launch_verify_t<float, 128>(p, qb, kb, vb, kc, vc, out, ws, st, nullptr)
+                    : launch_verify_t<float, 64>(p, qb, kb, vb, kc, vc, out, ws, st, nullptr);
+}
+
+int launch_rotate_window(const KParams& p, int in_bf16, const void* kc, void* kview, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (in_bf16)
+    return p.D == 128 ? launch_rotate_window_t<bf16, 128>(p, kc, kview, st) : launch_rotate_window_t<bf16, 64>(p, kc, kview, st);
+  return p.D == 128 ? launch_rotate_window_t<float, 128>(p, kc, kview, st) : launch_rotate_window_t<float, 64>(p, kc, kview, st);
 }
 
 }  // namespace fd

@@ -64,6 +64,12 @@ def lib() -> ctypes.CDLL:
         L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
         L.fd_verify_attn.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp, sz, vp]
         L.fd_verify_attn.restype = ctypes.c_int
+        L.fd_verify_batched_workspace_bytes.argtypes = [G, i32, i32]
+        L.fd_verify_batched_workspace_bytes.restype = sz
+        L.fd_verify_attn_batched.argtypes = [G, i32, vp, vp, vp, vp, vp, vp, i64, ctypes.POINTER(i32), i32, i32,
+                                             vp, vp, sz, vp]
+        L.fd_verify_attn_batched.restype = ctypes.c_int
+        L.fd_rotate_window.argtypes, L.fd_rotate_window.restype = [G, vp, i64, vp, vp], ctypes.c_int
         L.fd_verify_attn_noalloc.argtypes = [G, vp, vp, vp, vp, vp, i64, i32, i32, vp, vp]
         L.fd_verify_attn_noalloc.restype = ctypes.c_int
         L.fd_status_str.argtypes, L.fd_status_str.restype = [ctypes.c_int], ctypes.c_char_p
@@ -73,7 +79,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
            "fd_stream_attn", "fd_stream_attn_insert", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
-           "fd_verify_attn", "fd_verify_attn_noalloc", "fd_status_str")
+           "fd_verify_attn", "fd_verify_batched_workspace_bytes", "fd_verify_attn_batched", "fd_rotate_window",
+           "fd_verify_attn_noalloc", "fd_status_str")
 
 
 def make_geom(g, out_dtype: str = "f32") -> FdGeom:
@@ -195,3 +202,29 @@ def verify_attn_noalloc(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame: 
     _check("fd_verify_attn_noalloc", lib().fd_verify_attn_noalloc(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
         _ptr(v_cache), int(newest_frame), int(n_tail), int(blk_len), _ptr(out), _stream(stream)))
+
+
+def verify_batched_workspace_bytes(g, n_drafts: int, blk_len: int) -> int:
+    return lib().fd_verify_batched_workspace_bytes(ctypes.byref(make_geom(g)), int(n_drafts), int(blk_len))
+
+
+def verify_attn_batched(g, q_blk, k_blk, v_blk, k_cache, v_cache, newest_frame: int, n_tails, tail_stride: int,
+                        blk_len: int, out, ws, k_view=None, ws_bytes: int | None = None, out_dtype: str = "f32",
+                        stream=None):
+    """out [S][B][Hq][D] = verify of S draft blocks (q_blk [S][B][Hq][D], k_blk / v_blk [S][B][Hkv][D]) over
+    one window; draft d's tail at cache rows N + d*tail_stride, n_tails[d] reasoning rows.  k_view: the
+    rotated window (a streaming call's workspace start, or rotate_window's output) or None."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    n = len(n_tails)
+    arr = (ctypes.c_int32 * n)(*[int(x) for x in n_tails])
+    _check("fd_verify_attn_batched", lib().fd_verify_attn_batched(
+        ctypes.byref(make_geom(g, out_dtype)), n, _ptr(k_view), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk),
+        _ptr(k_cache), _ptr(v_cache), int(newest_frame), arr, int(tail_stride), int(blk_len), _ptr(out), _ptr(ws),
+        int(ws_bytes), _stream(stream)))
+
+
+def rotate_window(g, k_cache, newest_frame: int, k_view, stream=None):
+    """k_view [Hkv][N][D] (fp16 for bf16 inputs) = the window's keys rotated at their positions."""
+    _check("fd_rotate_window", lib().fd_rotate_window(ctypes.byref(make_geom(g)), _ptr(k_cache), int(newest_frame),
+                                                      _ptr(k_view), _stream(stream)))

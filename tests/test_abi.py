@@ -233,3 +233,45 @@ def test_workspace_size_covers_largest_block():
     assert ws >= g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4
     # 16-token blocks: G*16 = 64 query rows per kv head, two 32-row blocks
     assert fd.verify_workspace_bytes(g, 16) >= 2 * g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4
+
+
+def test_verify_batched_call_errors():
+    """Batched verify: bf16 only, 1..8 drafts, every draft's tail rows inside its own stride
+    slice and the whole batch inside tail_cap, workspace sized for the batch, 16-byte alignment
+    (the rotated-key view included)."""
+    L = fd.lib()
+    g = _g(tail_cap=64)
+    gp = ctypes.byref(g)
+    W = L.fd_verify_batched_workspace_bytes
+    ws1, ws2 = W(gp, 1, 8), W(gp, 2, 8)
+    assert 0 < ws1 < ws2 and W(gp, 0, 8) == 0 and W(gp, 9, 8) == 0 and W(gp, 2, 33) == 0
+    assert W(ctypes.byref(_g(in_dtype=fd.FD_F32)), 2, 8) == 0
+    # one draft needs at least the single-call workspace
+    assert ws1 >= L.fd_verify_workspace_bytes(gp, 8)
+    B = L.fd_verify_attn_batched
+    tails = lambda *t: (ctypes.c_int32 * len(t))(*t)
+    blk = [FAKE, FAKE, FAKE, FAKE, FAKE]
+    ok = tails(5, 20)
+    assert B(None, 2, None, *blk, 5, ok, 32, 8, FAKE, FAKE, ws2, None) == -1
+    assert B(ctypes.byref(_g(in_dtype=fd.FD_F32, tail_cap=64)), 2, None, *blk, 5, ok, 32, 8, FAKE, FAKE, ws2,
+             None) == -3
+    assert B(gp, 2, None, *blk, 5, None, 32, 8, FAKE, FAKE, ws2, None) == -1     # no n_tails
+    assert B(gp, 2, None, None, *blk[1:], 5, ok, 32, 8, FAKE, FAKE, ws2, None) == -1
+    assert B(gp, 2, None, *blk, 2, ok, 32, 8, FAKE, FAKE, ws2, None) == -4       # window not full
+    assert B(gp, 0, None, *blk, 5, ok, 32, 8, FAKE, FAKE, ws2, None) == -6       # no drafts
+    assert B(gp, 9, None, *blk, 5, tails(*[0] * 9), 4, 1, FAKE, FAKE, ws2, None) == -6
+    assert B(gp, 2, None, *blk, 5, tails(25, 0), 32, 8, FAKE, FAKE, ws2, None) == -6   # 25+8 > stride 32
+    assert B(gp, 2, None, *blk, 5, tails(0, 30), 32, 8, FAKE, FAKE, ws2, None) == -6   # 32+30+8 > 64
+    assert B(gp, 2, None, *blk, 5, tails(-1, 0), 32, 8, FAKE, FAKE, ws2, None) == -6
+    assert B(gp, 2, None, *blk, 5, tails(0, 0), 0, 8, FAKE, FAKE, ws2, None) == -6     # stride below B
+    assert B(gp, 2, None, *blk, 5, ok, 32, 0, FAKE, FAKE, ws2, None) == -6
+    assert B(gp, 2, None, *blk, 5, ok, 32, 8, FAKE, None, ws2, None) == -7
+    assert B(gp, 2, None, *blk, 5, ok, 32, 8, FAKE, FAKE, ws1, None) == -7           # one draft's worth
+    assert B(gp, 2, MISALIGNED, *blk, 5, ok, 32, 8, FAKE, FAKE, ws2, None) == -5
+    assert B(gp, 2, None, *blk, 5, ok, 32, 8, MISALIGNED, FAKE, ws2, None) == -5
+    R = L.fd_rotate_window
+    assert R(None, FAKE, 5, FAKE, None) == -1
+    assert R(gp, None, 5, FAKE, None) == -1
+    assert R(gp, FAKE, 5, None, None) == -1
+    assert R(gp, FAKE, 2, FAKE, None) == -4
+    assert R(gp, FAKE, 5, MISALIGNED, None) == -5

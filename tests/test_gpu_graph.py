@@ -165,7 +165,7 @@ class SeededStep:
         self.out = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
         self.vout = torch.empty((blk, g.n_q_heads, g.head_dim), device=H.DEV)
         self.sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
-        self.vws = torch.zeros(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=H.DEV)
+        self.vws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=H.DEV)
 
     def load(self, t):
         """Frame t's K, V and queries of every view into the static input buffers."""

@@ -224,6 +224,7 @@ def test_shift_invariance_bf16(c):
     check_stream(w2, 0, [w.first_t + 1])
     check_prefill(w2, 0, w.first_t + 2)
     check_verify(w2, 0, w.first_t + 1, 40, 8)
+    check_verify_batched(w2, 0, w.first_t + 1, [20, 3], 32, 8, "rotate")
 
 
 def test_deterministic():
@@ -296,6 +297,143 @@ def test_verify_edge_geometries(w):
     g = w.geom
     b = max(1, min(32 // (g.n_q_heads // g.n_kv_heads), g.tail_cap))
     check_verify(w, 0, w.first_t, max(0, g.tail_cap - b), b)
+
+
+# ---------------------------------------------------------------------------- batched drafts, rotated view
+def check_verify_batched(w, layer, t, n_tails, stride, blk, view=None, out_dtype="f32"):
+    """S draft blocks over one window in one call: draft d's reasoning rows (seeded per draft)
+    at cache rows N + d*stride, its block after them; every draft against oracle_verify with its
+    own tail and block, block rows copied bit-exactly, other tail rows untouched.  view: None
+    (keys rotated in the kernel), "rotate" (fd_rotate_window) or "stream" (a streaming call's
+    workspace start)."""
+    g = w.geom
+    S = len(n_tails)
+    H.say(f"batched verify cfg {w.cfg_id} layer {layer} t {t} drafts {S} tails {n_tails} stride {stride} "
+          f"B {blk} view {view}")
+    kc, vc = H.window_caches(w, layer, t)
+    drafts = []
+    for d in range(S):
+        kt, vt = synth.tail_kv(w, 100 + d, n_tails[d])     # each draft its own reasoning rows
+        qb, kb, vb = synth.block_qkv(w, 100 + d, blk)
+        r0 = g.window + d * stride
+        kc[:, r0: r0 + n_tails[d]] = H.dev(np.transpose(kt, (1, 0, 2)), g)
+        vc[:, r0: r0 + n_tails[d]] = H.dev(np.transpose(vt, (1, 0, 2)), g)
+        drafts.append((kt, vt, qb, kb, vb))
+    q = H.dev(np.stack([x[2] for x in drafts]), g)
+    k = H.dev(np.stack([x[3] for x in drafts]), g)
+    v = H.dev(np.stack([x[4] for x in drafts]), g)
+    kview = None
+    if view == "rotate":
+        kview = torch.empty((g.n_kv_heads, g.window, g.head_dim), dtype=torch.float16, device=H.DEV)
+        fd.rotate_window(g, kc, t, kview)
+    elif view == "stream":
+        sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+        o = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
+        fd.stream_attn(g, H.q_new(w, layer, t), kc, vc, t, o, sws)
+        kview = sws
+    out = torch.empty((S, blk, g.n_q_heads, g.head_dim),
+                      dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=H.DEV)
+    ws = torch.full((fd.verify_batched_workspace_bytes(g, S, blk),), 0xAB, dtype=torch.uint8, device=H.DEV)
+    fd.verify_attn_batched(g, q, k, v, kc, vc, t, n_tails, stride, blk, out, ws, k_view=kview,
+                           out_dtype=out_dtype)
+    got = out.float().cpu().numpy()
+    win = fd_oracle.StreamWindow(g, *synth.prefix_kv(w, layer))
+    for f in range(t + 1):
+        for vv in range(g.n_views):
+            win.push(vv, f, *synth.frame_kv(w, layer, vv, f))
+    worst = 0.0
+    for d, (kt, vt, qb, kb, vb) in enumerate(drafts):
+        want = fd_oracle.oracle_verify(g, win, kt, vt, qb, kb, vb)
+        worst = max(worst, H.check_out(got[d], want, g, out_dtype, ("batched", d)))
+        r0 = g.window + d * stride + n_tails[d]
+        assert torch.equal(kc[:, r0: r0 + blk], H.dev(np.transpose(kb, (1, 0, 2)), g))
+        assert torch.equal(vc[:, r0: r0 + blk], H.dev(np.transpose(vb, (1, 0, 2)), g))
+    end = g.window + (S - 1) * stride + n_tails[-1] + blk
+    assert bool((kc[:, end:] == H.SENTINEL).all()) and bool((vc[:, end:] == H.SENTINEL).all())
+    H.say(f"  max-abs {worst:.3e} over {S} drafts (tol {H.TOL[g.dtype]})")
+    return got
+
+
+@pytest.mark.parametrize("cid,n_tails,stride,view", [
+    (4, [100, 37], 128, None), (4, [0, 5, 17, 33, 12, 30], 42, None), (4, [200], 0, "rotate"),
+    (4, [0, 5, 17, 33, 12, 30], 42, "stream"), (2, [20, 3], 32, None), (2, [0, 1, 2, 0, 1, 2], 10, "rotate")])
+def test_verify_batched(cid, n_tails, stride, view):
+    w = synth.CONFIGS[cid]
+    check_verify_batched(w, 0, w.first_t + 1, n_tails, stride, 8, view)
+
+
+def test_verify_batched_block16_and_bf16_out():
+    """16-token drafts (two row blocks each) and a bf16 output."""
+    w = synth.CONFIGS[4]
+    check_verify_batched(w, 3, w.first_t, [40, 3], 100, 16, "rotate")
+    check_verify_batched(w, 5, w.first_t, [60, 90, 0], 100, 8, None, out_dtype="bf16")
+
+
+def test_verify_repeat_bit_identical():
+    """Consecutive calls on one workspace (its partial slots reused) give bit-identical outputs:
+    single-draft config 4 and a three-draft call with a view."""
+    w = synth.CONFIGS[4]
+    g = w.geom
+    t = w.first_t
+    kc, vc = H.window_caches(w, 0, t)
+    kt, vt = synth.tail_kv(w, 0, 200)
+    kc[:, g.window: g.window + 200] = H.dev(np.transpose(kt, (1, 0, 2)), g)
+    vc[:, g.window: g.window + 200] = H.dev(np.transpose(vt, (1, 0, 2)), g)
+    qb, kb, vb = (H.dev(x, g) for x in synth.block_qkv(w, 0, 8))
+    ws = torch.zeros(fd.verify_workspace_bytes(g, 8), dtype=torch.uint8, device=H.DEV)
+    outs = []
+    for _ in range(6):
+        o = torch.empty((8, g.n_q_heads, g.head_dim), device=H.DEV)
+        fd.verify_attn(g, qb, kb, vb, kc, vc, t, 200, 8, o, ws)
+        outs.append(o)
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    kview = torch.empty((g.n_kv_heads, g.window, g.head_dim), dtype=torch.float16, device=H.DEV)
+    fd.rotate_window(g, kc, t, kview)
+    q3 = torch.stack([qb] * 3)
+    k3, v3 = torch.stack([kb] * 3), torch.stack([vb] * 3)
+    ws3 = torch.zeros(fd.verify_batched_workspace_bytes(g, 3, 8), dtype=torch.uint8, device=H.DEV)
+    outs = []
+    for _ in range(6):
+        o = torch.empty((3, 8, g.n_q_heads, g.head_dim), device=H.DEV)
+        fd.verify_attn_batched(g, q3, k3, v3, kc, vc, t, [50, 20, 0], 80, 8, o, ws3, k_view=kview)
+        outs.append(o)
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    H.say("  six consecutive calls bit-identical (single draft; three drafts with a view)")
+
+
+def test_rotate_window_matches_oracle_rotation():
+    """fd_rotate_window: every window key rotated at its current position, as the oracle's fp64
+    rotation rounded to fp16 (within half an fp16 ulp plus 2^-20 of the pair's input magnitude for
+    the fp32 angle and rotation arithmetic); and the streaming call leaves the same bytes at its
+    workspace start."""
+    for cid in (2, 5):
+        w = synth.CONFIGS[cid]
+        g = w.geom
+        t = w.first_t + 3
+        kc, vc = H.window_caches(w, 0, t)
+        kview = torch.empty((g.n_kv_heads, g.window, g.head_dim), dtype=torch.float16, device=H.DEV)
+        fd.rotate_window(g, kc, t, kview)
+        got = kview.float().cpu().numpy().astype(np.float64)
+        kraw = kc[:, : g.window].float().cpu().numpy().astype(np.float64)      # [Hkv][W][D]
+        pos = np.array([fd.key_position(g, t, x) for x in range(g.window)])
+        want = np.transpose(fd_oracle.rope(np.transpose(kraw, (1, 0, 2)), pos, g.rope_theta), (1, 0, 2))
+        a = np.maximum(np.abs(want), 2.0 ** -14)
+        half_ulp = np.ldexp(1.0, (np.floor(np.log2(a)) - 11).astype(np.int64))
+        # fp32 angle and rotation error scales with the pair's input magnitude (a rotated
+        # element can cancel to near zero): 2^-20 of |x1| + |x2|
+        pair = np.abs(kraw) + np.abs(np.concatenate([kraw[..., 64:], kraw[..., :64]], axis=-1))
+        err = np.abs(got - want)
+        excess = err - (half_ulp + 2.0 ** -20 * pair + 1e-7)
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        assert excess[i] <= 0, ("worst", cid, i, float(got[i]), float(want[i]), float(kraw[i]),
+                                float(kraw[i[0], i[1], (i[2] + 64) % 128]), int(pos[i[1]]))
+        sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+        o = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
+        fd.stream_attn(g, H.q_new(w, 0, t), kc, vc, t, o, sws)
+        torch.cuda.synchronize()
+        assert torch.equal(sws[: kview.numel() * 2].view(torch.float16), kview.reshape(-1))
+        H.say(f"  cfg {cid}: rotated window within half an fp16 ulp of the oracle's rotation; "
+              f"equal to the streaming workspace's start")
 
 
 # ---------------------------------------------------------------------------- cold-start prefill
