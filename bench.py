@@ -23,6 +23,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -90,10 +92,20 @@ def verify_pairs(g, n_tail, blk) -> int:
     return blk * (g.window + n_tail) + blk * (blk + 1) // 2
 
 
-def cpu_baseline(min_seconds: float = 12.0, max_layers: int = 36):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload: config-3
-    streaming-prefill layers, one after another, until min_seconds have elapsed (or all
-    max_layers are done).  Returns its algorithmic TFLOP/s (same FLOP count as the GPU)."""
+def verify_bytes(g, n_tail, blk, esz=2) -> int:
+    """Algorithmic bytes of one verify call: the window's, the tail's and the block's K and V
+    read once, the block's queries read and the fp32 outputs written."""
+    return ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
+            + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+
+
+def cpu_baseline(seconds: float = 24.0):
+    """The fp64 oracle (as it stands) on bounded samples of the same workloads, each leg given
+    about a third of `seconds` (whole units only, at least one): config-3 streaming-prefill
+    layers, config-4 verify layers (of 36) and consecutive config-5 rolling windows.  Inputs
+    are generated outside the timed region; only the oracle's attention calls (full window
+    re-rotation, explicit mask) are timed.  Rates use the GPU legs' algorithmic FLOP and byte
+    counts."""
     import oracle.fd_oracle as fd_oracle
     from streaming_kv_cache_view_amd import synth
     try:
@@ -102,23 +114,75 @@ def cpu_baseline(min_seconds: float = 12.0, max_layers: int = 36):
     except Exception:
         blas_threads = 1
     cores = len(os.sched_getaffinity(0))
+    leg = seconds / 3
+
+    def window(w, layer, t):
+        g = w.geom
+        pk, pv = synth.prefix_kv(w, layer)
+        win = fd_oracle.StreamWindow(g, pk, pv)
+        for f in range(t + 1):
+            for v in range(g.n_views):
+                k, vv = synth.frame_kv(w, layer, v, f)
+                win.push(v, f, k, vv)
+        return win
+
+    # config 3: streaming prefill, one layer after another
     w3 = synth.CONFIGS[3]
-    g = w3.geom
-    flops, layers = 0, 0
-    t0 = time.perf_counter()
-    while layers < max_layers and time.perf_counter() - t0 < min_seconds:
-        for _t, _out in fd_oracle.run_stream_workload(w3, layers, [w3.first_t], synth):
-            flops += 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
-        layers += 1
-    t_stream = time.perf_counter() - t0
+    g3 = w3.geom
+    t_s, n_s = 0.0, 0
+    while n_s < 36 and (n_s == 0 or t_s < leg):
+        win = window(w3, n_s, w3.first_t)
+        q = np.concatenate([synth.frame_q(w3, n_s, v, w3.first_t) for v in range(g3.n_views)])
+        t0 = time.perf_counter()
+        fd_oracle.oracle_stream(g3, win, q)
+        t_s += time.perf_counter() - t0
+        n_s += 1
+    stream_tf = 4 * g3.head_dim * g3.n_q_heads * stream_pairs(g3) * n_s / t_s / 1e12
+    # config 4: the 8-token verify, one layer after another (all 36 when they fit)
+    w4 = synth.CONFIGS[4]
+    g4 = w4.geom
+    t_v, n_v = 0.0, 0
+    while n_v < 36 and (n_v == 0 or t_v < leg):
+        win = window(w4, n_v, w4.first_t)
+        kt, vt = synth.tail_kv(w4, n_v, w4.n_tail)
+        qb, kb, vb = synth.block_qkv(w4, n_v, w4.blk_len)
+        t0 = time.perf_counter()
+        fd_oracle.oracle_verify(g4, win, kt, vt, qb, kb, vb)
+        t_v += time.perf_counter() - t0
+        n_v += 1
+    ver_gbs = verify_bytes(g4, w4.n_tail, w4.blk_len) * n_v / t_v / 1e9
+    # config 5: consecutive rolling windows of layer 0 from the first full one
+    w5 = synth.CONFIGS[5]
+    g5 = w5.geom
+    pk, pv = synth.prefix_kv(w5, 0)
+    win = fd_oracle.StreamWindow(g5, pk, pv)
+    t_5, n_5, t = 0.0, 0, 0
+    while n_5 < w5.windows and (n_5 == 0 or t_5 < leg):
+        for v in range(g5.n_views):
+            k, vv = synth.frame_kv(w5, 0, v, t)
+            win.push(v, t, k, vv)
+        if t >= w5.first_t:
+            q = np.concatenate([synth.frame_q(w5, 0, v, t) for v in range(g5.n_views)])
+            t0 = time.perf_counter()
+            fd_oracle.oracle_stream(g5, win, q)
+            t_5 += time.perf_counter() - t0
+            n_5 += 1
+        t += 1
+    c5_tf = 4 * g5.head_dim * g5.n_q_heads * stream_pairs(g5) * n_5 / t_5 / 1e12
     return {
-        "value": flops / t_stream / 1e12,
+        "value": round(stream_tf, 5),
         "unit": "TFLOP/s",
         "cores": min(cores, blas_threads),
+        "cores_visible": cores,
+        "blas_threads": blas_threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle streaming prefill of config 3, layers 0..{layers - 1} of 36 "
-                  f"(window build + full re-rotation + explicit mask), {t_stream:.1f} s; "
-                  f"host cores visible {cores}, BLAS threads {blas_threads}",
+        "sample": f"fp64 oracle, inputs generated untimed: streaming prefill of config 3, layers 0..{n_s - 1} "
+                  f"of 36 ({t_s:.1f} s); value is this leg",
+        "verify": {"value": round(ver_gbs, 4), "unit": "GB/s",
+                   "sample": f"config-4 verify (8-token block over 4608+{w4.n_tail}+{w4.blk_len} keys), "
+                             f"layers 0..{n_v - 1} of 36 ({t_v:.1f} s)"},
+        "config5": {"value": round(c5_tf, 5), "unit": "TFLOP/s",
+                    "sample": f"config-5 rolling windows 0..{n_5 - 1} of 100, layer 0 ({t_5:.1f} s)"},
     }
 
 
@@ -177,8 +241,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="oracle sample length (whole config-3 layers until this many seconds)")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="oracle sample length over its three legs (config-3 layers, config-4 verify "
+                         "layers, config-5 windows; whole units)")
     ap.add_argument("--core-only", action="store_true",
                     help="only the window step and its per-call timing (no block-16 verify, no graph "
                          "replay): the per-kernel averages of a profiled run then cover one call type each")
@@ -278,7 +343,8 @@ def main():
     med = lambda a: sorted(a)[len(a) // 2]
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
 
-    v16_us = graph_ms_per_step = prefill_us = kvproj_us = c5 = vgraph_us = None
+    v16_us = graph_ms_per_step = prefill_us = kvproj_us = c5 = vgraph_us = batched = None
+    esz_in = 2
     F = g.n_frames
     if not args.core_only:
         # verify with 16-token draft blocks (64 query rows per kv head)
@@ -301,6 +367,47 @@ def main():
             if rep_i > 0:   # the first sweep is a warm-up
                 v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
         v16_us = sum(v16_ms) / len(v16_ms) * 1e3
+
+        # batched verify: S independent 8-token drafts with their own reasoning tails over one
+        # window in one call, with and without the rotated window a streaming call leaves in its
+        # workspace (here from fd_rotate_window); tails in a cache with room for six of them
+        gb = g.replace(tail_cap=6 * (n_tail + blk))
+        kcb = [rnd(g.n_kv_heads, gb.cache_rows, g.head_dim) for _ in range(L)]
+        vcb = [rnd(g.n_kv_heads, gb.cache_rows, g.head_dim) for _ in range(L)]
+        kview = [torch.empty(g.n_kv_heads, g.window, g.head_dim, dtype=torch.float16, device=dev) for _ in range(L)]
+        for l in range(L):
+            fd.rotate_window(gb, kcb[l], t16, kview[l])
+        batched = {}
+        for tails in ((200, 120), (200, 150, 100, 175, 125, 50)):
+            S = len(tails)
+            qs = [rnd(S, blk, g.n_q_heads, g.head_dim) for _ in range(L)]
+            ks = [rnd(S, blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
+            vs = [rnd(S, blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
+            ob = torch.empty(S, blk, g.n_q_heads, g.head_dim, device=dev)
+            wsb = torch.empty(fd.verify_batched_workspace_bytes(gb, S, blk), dtype=torch.uint8, device=dev)
+            nbytes = ((g.window + sum(tails) + S * blk) * g.n_kv_heads * g.head_dim * esz_in * 2
+                      + S * blk * g.n_q_heads * g.head_dim * (esz_in + 4))
+            for use_view in (False, True):
+                b_ms = []
+                for rep_i in range(1 + max(1, args.steps // 4)):
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+                    host_ahead()
+                    ev[0].record()
+                    for l in range(L):
+                        fd.verify_attn_batched(gb, qs[l], ks[l], vs[l], kcb[l], vcb[l], t16, tails, n_tail + blk,
+                                               blk, ob, wsb, k_view=kview[l] if use_view else None)
+                        ev[l + 1].record()
+                    torch.cuda.synchronize()
+                    if rep_i > 0:
+                        b_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
+                us = sum(b_ms) / len(b_ms) * 1e3
+                gbs = nbytes / (us * 1e-6) / 1e9
+                batched[f"S{S}{'_view' if use_view else ''}"] = {
+                    "us_per_call": round(us, 2), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "drafts": S, "n_tails": list(tails), "k_view": use_view,
+                    "bytes_per_call": nbytes}
+            del qs, ks, vs, ob, wsb
+        del kcb, vcb, kview
 
         # cold-start (non-streaming) prefill: every window row a query, same mask
         pws = torch.empty(fd.prefill_workspace_bytes(g), dtype=torch.uint8, device=dev)
@@ -395,12 +502,10 @@ def main():
 
     esz = 2
     flops_layer = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
-    vbytes_layer = ((g.window + n_tail + blk) * g.n_kv_heads * g.head_dim * esz * 2
-                    + blk * g.n_q_heads * g.head_dim * esz + blk * g.n_q_heads * g.head_dim * 4)
+    vbytes_layer = verify_bytes(g, n_tail, blk, esz)
     flops_prefill = 4 * g.head_dim * g.n_q_heads * (g.window * (g.window + 1) // 2)
     b16 = 16
-    v16bytes_layer = ((g.window + n_tail + b16) * g.n_kv_heads * g.head_dim * esz * 2
-                      + b16 * g.n_q_heads * g.head_dim * esz + b16 * g.n_q_heads * g.head_dim * 4)
+    v16bytes_layer = verify_bytes(g, n_tail, b16, esz)
     ibytes_layer = 2 * 2 * g.n_views * g.tok_per_frame * g.n_kv_heads * g.head_dim * esz
     value = flops_layer * L / (ms_per_step * 1e-3) / 1e12
     att_tflops = flops_layer / (att_us * 1e-6) / 1e12
@@ -456,6 +561,10 @@ def main():
             "gbs": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9, 1),
             "frac": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "note": f"the {L} verify calls of a step captured in one HIP graph, median replay / {L}"},
+        "verify_batched": None if batched is None else dict(batched, note=(
+            "fd_verify_attn_batched: S 8-token drafts with their own reasoning tails over one window per "
+            "call; algorithmic bytes = window K/V once + every draft's tail and block K/V + queries + fp32 "
+            "outputs; _view: window keys read from the rotated fp16 view")),
         "config5": c5,
         "insert_gbs": round(ibytes_layer / (ins_us * 1e-6) / 1e9, 1),
         "verify_block16": None if v16_us is None else {

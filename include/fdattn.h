@@ -53,9 +53,18 @@
  *   (x[i], x[i+D/2]) is rotated by pos * theta^(-2i/D).  Query head h reads
  *   kv head h / (Hq/Hkv).  Scores are scaled by 1/sqrt(D); query position p_q
  *   sees key position p_k iff p_k <= p_q.  Accumulation is fp32 throughout.
- *   bf16 inputs: rotated Q and K are rounded to fp16 for Q K^T (fp16 matrix
- *   cores; elements of rotated Q/K must stay within fp16 range, |x| < 65504),
- *   softmax probabilities to bf16 for P V (bf16 matrix cores, V exact).
+ *   bf16 inputs: rotated K, and rotated Q scaled by log2(e)/sqrt(D), are rounded
+ *   (to nearest even) to fp16 for Q K^T on the fp16 matrix cores; softmax
+ *   probabilities are rounded to bf16 for P V (bf16 matrix cores, V exact).
+ *   fp16 operand range: a rotated element of a stored pair (x, y) = (x[i],
+ *   x[i+D/2]) has magnitude at most sqrt(x^2 + y^2), so no rotated operand
+ *   overflows while every key pair has sqrt(x^2 + y^2) < 65520 (e.g. every
+ *   stored key element |x| <= 46000) and every query pair has
+ *   sqrt(x^2 + y^2) * log2(e)/sqrt(D) < 65520 (D = 128: |x| <= 3.6e5).  Above
+ *   that an element can round to +-inf, depending on the key's or query's
+ *   position, and no error is reported: a score that becomes -inf drops its
+ *   key silently, one that becomes +inf or NaN (inf * 0, inf - inf) makes the
+ *   whole output row NaN.  fp32 inputs have no such bound.
  *   fp32 inputs: both products on the fp32 matrix cores.  Outputs are fp32
  *   unless out_dtype is FD_BF16.
  */

@@ -191,9 +191,13 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
   if (blk_len < 1 || blk_len > g->tail_cap) return 0;
   const int G = g->n_q_heads / g->n_kv_heads;
   if (blk_len > 32 || fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return 0;
-  const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame,
-                                     g->tail_cap);
-  const int S = fd::verify_splits(nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
+  // partial slots per (kv head, row block) for the longest tail: split-KV workgroups of the fp32
+  // kernel; window and tail units of the bf16 kernel
+  const int S = g->in_dtype == FD_BF16
+                    ? fd::verify_dma_slots(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame, g->tail_cap)
+                    : fd::verify_splits(fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames,
+                                                          g->tok_per_frame, g->tail_cap),
+                                        fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
   return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * fd::verify_row_blocks(G, blk_len) * S *
                                                    fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
@@ -204,9 +208,8 @@ size_t fd_verify_batched_workspace_bytes(const fd_geom* g, int32_t n_drafts, int
     return 0;
   const int G = g->n_q_heads / g->n_kv_heads;
   if (fd::verify_row_blocks(G, blk_len) > fd::kVerifyMaxRowBlocks) return 0;
-  // every draft's tail fits in tail_cap: its key list is at most the window's plus tail_cap rows
-  const int nblk = fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame, g->tail_cap);
-  const int S = fd::verify_splits(nblk, fd::kVerifyWavesDma);
+  // every draft's tail fits in tail_cap: its slots are at most those of a tail_cap-row tail
+  const int S = fd::verify_dma_slots(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame, g->tail_cap);
   return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * n_drafts * fd::verify_row_blocks(G, blk_len) *
                                                    S * fd::verify_partial_words(g->head_dim) * sizeof(float);
 }
@@ -246,8 +249,13 @@ int launch_verify_checked(const fd_geom* g, const void* q_blk, const void* k_blk
   p.nrb_d = fd::verify_row_blocks(p.G, blk_len);
   p.n_rb = p.nrb_d;
   p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, n_tail + blk_len);
-  p.n_split = fd::verify_splits(p.nblk, g->in_dtype == FD_BF16 ? fd::kVerifyWavesDma
-                                                               : fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
+  if (g->in_dtype == FD_BF16) {
+    p.n_ws = fd::verify_window_units(p.P, p.V, p.F, p.T);
+    p.n_ts = fd::verify_tail_units(n_tail + blk_len);
+    p.n_split = p.n_ws + p.n_ts;
+  } else {
+    p.n_split = fd::verify_splits(p.nblk, fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
+  }
   return fd::launch_verify(p, g->in_dtype == FD_BF16, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws,
                            hip_stream);
 }
@@ -301,7 +309,9 @@ int fd_verify_attn_batched(const fd_geom* g, int32_t n_drafts, const void* k_vie
   p.nrb_d = fd::verify_row_blocks(p.G, blk_len);
   p.n_rb = n_drafts * p.nrb_d;
   p.nblk = fd::verify_blocks(p.P, p.V, p.F, p.T, maxtail + blk_len);
-  p.n_split = fd::verify_splits(p.nblk, fd::kVerifyWavesDma);
+  p.n_ws = fd::verify_window_units(p.P, p.V, p.F, p.T);
+  p.n_ts = fd::verify_tail_units(maxtail + blk_len);
+  p.n_split = p.n_ws + p.n_ts;
   return fd::launch_verify(p, 1, q_blk, k_blk, v_blk, k_cache, v_cache, out, ws, hip_stream, k_view);
 }
 

@@ -13,8 +13,8 @@ constexpr int kTileKeys = 64;     // keys per K/V tile in the streaming kernel
 constexpr int kVerifyBlock = 32;  // keys per MFMA block in the verify kernel
 constexpr int kVerifyWaves = 4;             // waves per verify workgroup, fp32 path
 constexpr int kVerifyBlocksPerWave = 1;
-constexpr int kVerifyWavesDma = 5;          // bf16 path: one 32-key block per wave (5: 31 splits x 8 kv
-                                            // heads at the backbone shapes, one workgroup per CU)
+constexpr int kVerifyWavesDma = 5;          // bf16 path: waves per workgroup, one 32-key block each
+                                            // (31 units x 8 kv heads at the backbone shapes: every CU)
 constexpr int kVerifyMaxDrafts = 8;         // draft blocks verified by one batched call
 
 // Everything a kernel needs about one call, passed by value as a kernel argument.
@@ -42,7 +42,9 @@ struct KParams {
                       // 1: chunk c is segment nseg-1-c whole (no split, no merge)
   // verify.  A call verifies n_drafts draft blocks of B tokens over one window; draft d's
   // reasoning rows and block rows sit in cache rows W + d*tail_stride + [0, n_tails[d] + B).
-  int32_t n_tail, B, nblk, n_split;   // n_tail: draft 0's; nblk: key blocks of the longest key list
+  int32_t n_tail, B, nblk, n_split;   // n_tail: draft 0's; nblk: key blocks of the longest key list;
+                                      // n_split: partial slots per (kv head, row block)
+  int32_t n_ws, n_ts;   // bf16 path: units over the window's blocks, and per draft over its tail
   int32_t n_rb;       // 32-row blocks of every draft's G*B query rows: n_drafts * nrb_d
   int32_t nrb_d;      // 32-row blocks of one draft's G*B query rows
   int32_t n_drafts;
@@ -61,8 +63,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Verify split bookkeeping shared by host and kernels.  A row block's keys are the window's
 // 32-key blocks (inside the prefix and inside each frame slot: contiguous positions) followed by
 // the 32-key blocks of its own draft's tail rows.
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
-inline int verify_window_blocks(int P, int V, int F, int T) {
+constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+constexpr int verify_window_blocks(int P, int V, int F, int T) {
   return ceil_div(P, kVerifyBlock) + V * F * ceil_div(T, kVerifyBlock);
 }
 inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
@@ -72,6 +74,17 @@ inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
 inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, blocks_per_wg); }
 // fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
+// bf16 path: key blocks per workgroup ("unit"); units over the window's blocks; units over one
+// draft's tail of tail_rows rows (reasoning rows + block rows); partial slots per (kv head, row
+// block) with tails up to tail_rows: one per unit
+constexpr int kVerifyUnitBlocks = kVerifyWavesDma;
+constexpr int verify_window_units(int P, int V, int F, int T) {
+  return ceil_div(verify_window_blocks(P, V, F, T), kVerifyUnitBlocks);
+}
+constexpr int verify_tail_units(int tail_rows) { return ceil_div(ceil_div(tail_rows, kVerifyBlock), kVerifyUnitBlocks); }
+constexpr int verify_dma_slots(int P, int V, int F, int T, int tail_rows) {
+  return verify_window_units(P, V, F, T) + verify_tail_units(tail_rows);
+}
 // 32-row blocks of the G*B query rows of one kv head (at most kVerifyMaxRowBlocks)
 constexpr int kVerifyMaxRowBlocks = 4;
 inline int verify_row_blocks(int G, int B) { return ceil_div(G * B, 32); }

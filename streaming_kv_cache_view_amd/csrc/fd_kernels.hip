@@ -2021,165 +2021,217 @@ __device__ inline VerifyBlock verify_block(const KParams& p, int d, int j) {
   return b;
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n that is a multiple of NIB up to 4*NIB (the
+// immediate-operand form for each case)
+template <int NIB>
+__device__ inline void wait_vm_blocks(int nblk) {
+  static_assert(4 * NIB < 64, "vmcnt field");
+  switch (nblk) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm(NIB)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2 * NIB)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3 * NIB)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm(4 * NIB)); break;
+  }
+}
+
+// Speculative verify, bf16 inputs: the split-KV kernel.  blockIdx.x = unit * Hkv + kvh, so the
+// units of one kv head run on one XCD (round-robin dispatch over 8 XCDs, Hkv a multiple of 8).
+// Unit u < n_ws covers the window's key blocks [8u, 8u + 8) for every row block of every
+// draft: the window's K and V are read once per call, however many drafts.  Unit
+// n_ws + d*n_ts + t covers draft d's tail blocks [8t, 8t + 8) (its reasoning rows, then its
+// block rows) for draft d's row blocks.  Five waves, one 32-key block each (248 workgroups at
+// the backbone shapes: every CU busy), loaded straight into LDS: K first, V once the rotation tables are built and the queries
+// rotated, so that work runs while K lands.  A key's rotation is the product of its block's
+// base angle (fp64 fraction, one per frequency) and a shared table of (cos, sin)(r f) for the
+// 32 offsets r of a block.  Per row block: every wave computes S^T = K Q^T for its block; the
+// row maxima meet in LDS; each wave writes P = 2^(S - M) (bf16) for its block to LDS; wave
+// w < D/32 then computes O^T = V^T P^T for d-slice w over all the unit's blocks, so O is never
+// folded across waves, and the unit's partial (O in accumulator order, the row max M, the row
+// sum) goes to the workspace for verify_merge_dma_kernel.
 template <int D, bool VIEW>
 __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
     const KParams p, const bf16* __restrict__ qb, const bf16* __restrict__ kb, const bf16* __restrict__ vb,
     bf16* __restrict__ kc, bf16* __restrict__ vc, const _Float16* __restrict__ kview, float* __restrict__ part) {
   using QK = F16Ops;
   using PV = BF16Ops;
-  constexpr int NW = kVerifyWavesDma;            // waves per workgroup, one key block each
+  constexpr int NW = kVerifyWavesDma;            // waves, one 32-key block each
   constexpr int NT = 64 * NW;
+  constexpr int NB = kVerifyUnitBlocks;          // blocks per workgroup
   constexpr int E = 8;
   constexpr int H2 = D / 2;
   constexpr int NU = D / 16;                     // QK^T k-steps (chunks 2u + h)
-  constexpr int ND = D / 32;
+  constexpr int NS = D / 32;                     // d-slices of O (one 32x32 accumulator each)
   constexpr int ROWB = D * 2;                    // K / V / Q row bytes
   constexpr int KCH = ROWB / 16;                 // 16-byte chunks per row
   constexpr int RPL = 1024 / ROWB;               // rows per 1 KB direct load
   constexpr int BLKB = 32 * ROWB;                // 32 rows of K, V or Q
   constexpr int NIB = BLKB / 1024;               // direct loads per 32 rows
-  constexpr int NQW = (NIB + NW - 1) / NW;       // query loads per wave (the last waves one fewer)
-  constexpr int OS = D + 4;
-  constexpr int KVB = NW * BLKB;                 // K (or V) bytes of the workgroup
+  constexpr int NQW = (NIB + NW - 1) / NW;       // query loads per wave (at most)
   constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
-  constexpr int CPR = D / 4;                     // 4-float chunks per output row
-  static_assert(NW >= 4 && NW <= 8, "the fold: four slots, at most one adding wave each");
-  static_assert(4 * 32 * OS * 4 <= 2 * KVB + BLKB, "fold slots alias the tiles");
+  constexpr int PBYTES = NB * 2 * 1024 > H2 * 32 * 8 ? NB * 2 * 1024 : H2 * 32 * 8;   // P^T operands;
+                                                 // first the angle table
+  static_assert(NB == NW && NS <= NW && NQW <= 2, "work split");
   auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
   auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
 
-  __shared__ __attribute__((aligned(16))) unsigned char tiles[2 * KVB + BLKB];   // K, V, query rows
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[NB * BLKB];
+  __shared__ __attribute__((aligned(16))) unsigned char vtile[NB * BLKB];
+  __shared__ __attribute__((aligned(16))) unsigned char qbuf[BLKB];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[PBYTES];       // first: the angle table
   __shared__ double frev[H2];                    // theta^(-2i/D) / (2 pi): revolutions per position
-  __shared__ float gf[H2];                       // the same in fp32
-  __shared__ float frb[NW][H2];                  // fraction of each wave's block base angle
+  __shared__ float2 cbase[NB][H2];               // (cos, sin) of each block's first position
   __shared__ float red_m[NW][32], red_l[NW][32];
-  unsigned char* const kbuf = tiles;
-  unsigned char* const vbuf = tiles + KVB;
-  unsigned char* const qbuf = tiles + 2 * KVB;
+  float2* const ang = reinterpret_cast<float2*>(pbuf);   // ang[i*32 + r] = (cos, sin)(r f_i)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  // blockIdx.x = (split * n_rb + rb) * Hkv + kvh: the row blocks of one split run side by side on
-  // one XCD and read the same window K / V (one HBM read, the rest from L2)
-  const int kvh = blockIdx.x % p.Hkv, rb = (blockIdx.x / p.Hkv) % p.n_rb, split = blockIdx.x / (p.Hkv * p.n_rb);
-  const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;   // draft, row block within the draft
-  const int qr = 32 * rbl + l32, bq = qr % p.B;          // this lane's query row, its block token
-
-  // ---- rotation frequencies (before any direct load: __syncthreads waits for vector memory)
-  if (tid < H2) {
-    const double f = exp2(-(2.0 * tid / D) * p.log2_theta) * kInvTwoPi;
-    frev[tid] = f;
-    gf[tid] = static_cast<float>(f);
-  }
-  __syncthreads();
-
-  // ---- this wave's key block (wave-uniform); rotated here unless the view holds it rotated
-  const VerifyBlock kbk = verify_block(p, d, split * NW + w);
-  const int x0 = uni(kbk.x0), klen = uni(kbk.len), tailbase = uni(kbk.tailbase);
-  const bool rot = !VIEW || x0 >= p.W;
-  // global row x of kv head kvh: a cache row, or (x >= tailbase) a row of the draft's block
-  auto row_of = [&](const bf16* cache, const bf16* blk, int x) -> const unsigned char* {
-    return reinterpret_cast<const unsigned char*>(
-        x >= tailbase ? blk + (static_cast<int64_t>(d * p.B + x - tailbase) * p.Hkv + kvh) * D
-                      : cache + (static_cast<int64_t>(kvh) * p.S_cap + x) * D);
+  const int kvh = blockIdx.x % p.Hkv, unit = blockIdx.x / p.Hkv;
+  const bool tail_unit = unit >= p.n_ws;
+  const int dt = tail_unit ? (unit - p.n_ws) / p.n_ts : 0;   // a tail unit's draft
+  const int tsp = tail_unit ? (unit - p.n_ws) % p.n_ts : 0;   // its tail split
+  const int slot = tail_unit ? p.n_ws + tsp : unit;           // its partial slot
+  const int rb_lo = tail_unit ? dt * p.nrb_d : 0, rb_hi = tail_unit ? rb_lo + p.nrb_d : p.n_rb;
+  const int n_wblk = verify_window_blocks(p.P, p.V, p.F, p.T);
+  // block jb of this unit: window block 8u + jb, or tail block 8t + jb of draft dt
+  auto block = [&](int jb) -> VerifyBlock {
+    if (tail_unit) return verify_block(p, dt, n_wblk + NB * tsp + jb);
+    const int j = NB * unit + jb;
+    return j < n_wblk ? verify_block(p, 0, j) : VerifyBlock{0, 0, p.W, 0};
   };
+  int bmask = 0;   // the unit's blocks that hold keys (a prefix of them)
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) bmask |= (block(jb).len > 0 ? 1 : 0) << jb;
+  bmask = uni(bmask);
+  if (bmask == 0) return;   // a tail split past this draft's tail (whole workgroup)
 
-  // ---- every global read in flight: this wave's share of the query rows, its K block, its V
-  // block.  32-row tiles land row r at LDS row r with 16-byte chunk c at position c ^ swz(r).
-  const uint32_t lq = lds_addr(qbuf), lk = uni(lds_addr(kbuf) + w * BLKB), lv = uni(lds_addr(vbuf) + w * BLKB);
-#pragma unroll
-  for (int i0 = 0; i0 < NQW; ++i0) {
-    const int i = w + NW * i0;
-    if (i >= NIB) break;   // wave-uniform
-    const int r = RPL * i + lane / KCH, pc = lane % KCH;
-    const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B;
-    const int hq = hh2 < p.G ? hh2 : 0, b2 = hh2 < p.G ? qr2 % p.B : 0;   // rows past G*B: any valid row
-    const bf16* src = qb + (static_cast<int64_t>(d * p.B + b2) * p.Hq + kvh * p.G + hq) * D;
-    g2lds16_va(src + 8 * (pc ^ kswz(r)), uni(lq + i * 1024));
-  }
-  if (klen > 0) {
-    const uint32_t lr = static_cast<uint32_t>(klen - 1);   // rows past the block's end: its last row (masked)
-#pragma unroll
-    for (int m = 0; m < NIB; ++m) {
-      const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
-      const int x = x0 + static_cast<int>(min(r, lr));
-      const unsigned char* src =
-          rot ? row_of(kc, kb, x) : reinterpret_cast<const unsigned char*>(kview + (static_cast<int64_t>(kvh) * p.W + x) * D);
-      g2lds16_va(src + 16 * (c ^ kswz(r)), lk + m * 1024);
-    }
-#pragma unroll
-    for (int m = 0; m < NIB; ++m) {
-      const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
-      g2lds16_va(row_of(vc, vb, x0 + static_cast<int>(min(r, lr))) + 16 * (c ^ vswz(r)), lv + m * 1024);
-    }
-  }
+  // ---- this wave's block
+  const VerifyBlock bk = block(w);
+  const int x0 = uni(bk.x0), klen = uni(bk.len), tailb = uni(bk.tailbase);
+  const bool rot = !VIEW || x0 >= p.W;
 
-  // ---- (cos, sin) of this lane's key (row l32 of the block) at its 32 frequencies, while the
-  // loads are in flight: revolutions = frac(pos0 * f) (fp64, one frequency per lane, through LDS)
-  // + l32 * f (fp32), then the hardware sin / cos on the fraction
-  float2 kcs[NU / 2][E];
-  if (rot && klen > 0) {
-    if (lane < H2) {
-      const double rv = static_cast<double>(kbk.pos0) * frev[lane];
-      frb[w][lane] = static_cast<float>(rv - rint(rv));
-    }
-    const float fl = static_cast<float>(l32);
+  // ---- queries of a row block into qbuf: wave w loads KB i = w, w + NW, ... of the 32 rows, row
+  // r at LDS row r with 16-byte chunk c at position c ^ kswz(r); rows past G*B read any valid row
+  const uint32_t lq = lds_addr(qbuf);
+  auto load_q = [&](int rb) {
+    const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
 #pragma unroll
-    for (int u = 0; u < NU / 2; ++u) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = 2 * E * u + E * h + e;
-        const float rv = __builtin_fmaf(fl, gf[i], frb[w][i]);
-        const float f = rv - rintf(rv);
-        kcs[u][e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-        asm volatile("" : "+v"(kcs[u][e].x), "+v"(kcs[u][e].y));   // computed here, not sunk
+    for (int i0 = 0; i0 < NQW; ++i0) {
+      const int i = w + NW * i0;
+      if (i < NIB) {
+        const int r = RPL * i + lane / KCH, pc = lane % KCH;
+        const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B;
+        const int hq = hh2 < p.G ? hh2 : 0, b2 = hh2 < p.G ? qr2 % p.B : 0;
+        const bf16* src = qb + (static_cast<int64_t>(d * p.B + b2) * p.Hq + kvh * p.G + hq) * D;
+        g2lds16_va(src + 8 * (pc ^ kswz(r)), uni(lq + i * 1024));
       }
     }
-  }
-
-  // ---- queries: this wave's share has landed once at most its K and V loads are pending; the
-  // barrier makes every share visible.  Rotated once per workgroup in LDS (in place, fp16, scaled
-  // into log2 units; rows past G*B zero): thread (row, chunk pair) of the first 32*KCH/2 threads.
-  if (klen > 0) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NIB));
-  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  wg_barrier();
-  if (tid < 32 * (KCH / 2)) {
-    const int r = tid / (KCH / 2), cp = tid % (KCH / 2);
-    const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B, b2 = qr2 % p.B;
-    const float qs = hh2 < p.G ? p.sm_scale_log2 : 0.f;
-    const double qpos = static_cast<double>(p.pos_base + p.W + p.n_tails[d] + b2);
-    unsigned char* c1 = qbuf + r * ROWB + ((cp ^ kswz(r)) << 4);
-    unsigned char* c2 = qbuf + r * ROWB + (((cp + KCH / 2) ^ kswz(r)) << 4);
-    float x1[E], x2[E];
-    BF16Ops::unpack(ld16(c1), x1);
-    BF16Ops::unpack(ld16(c2), x2);
+  };
+  // ---- K or V of this wave's block.  A whole block of contiguous cache (or view) rows takes one
+  // scalar base and the lane's offsets; a ragged block, or one reaching the draft's block rows,
+  // takes per-lane addresses with its rows clamped to the last (those keys are masked).
+  auto row_of = [&](const bf16* cache, const bf16* blk, int x) -> const unsigned char* {
+    return reinterpret_cast<const unsigned char*>(
+        x >= tailb ? blk + (static_cast<int64_t>(dt * p.B + x - tailb) * p.Hkv + kvh) * D
+                   : cache + (static_cast<int64_t>(kvh) * p.S_cap + x) * D);
+  };
+  auto load_kv = [&](bool is_v) {
+    const uint32_t ldst = uni(lds_addr(is_v ? vtile : ktile) + w * BLKB);
+    if (klen == 32 && x0 + 32 <= tailb) {
+      const unsigned char* base =
+          (!is_v && !rot) ? reinterpret_cast<const unsigned char*>(kview + (static_cast<int64_t>(kvh) * p.W + x0) * D)
+                          : reinterpret_cast<const unsigned char*>((is_v ? vc : kc) + (static_cast<int64_t>(kvh) * p.S_cap + x0) * D);
+      base = uni_ptr(base);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float2 cq = cs_rev(qpos * frev[E * cp + e]);
-      const float a = x1[e], b = x2[e];
-      x1[e] = (a * cq.x - b * cq.y) * qs;
-      x2[e] = (b * cq.x + a * cq.y) * qs;
+      for (int m = 0; m < NIB; ++m) {
+        const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
+        g2lds16_async(base, r * ROWB + 16 * (c ^ (is_v ? vswz(r) : kswz(r))), ldst + m * 1024);
+      }
+    } else {
+      const uint32_t lr = static_cast<uint32_t>(klen - 1);
+#pragma unroll
+      for (int m = 0; m < NIB; ++m) {
+        const uint32_t r = RPL * m + lane / KCH, c = lane % KCH;
+        const int x = x0 + static_cast<int>(min(r, lr));
+        const unsigned char* src =
+            is_v ? row_of(vc, vb, x)
+                 : (rot ? row_of(kc, kb, x)
+                        : reinterpret_cast<const unsigned char*>(kview + (static_cast<int64_t>(kvh) * p.W + x) * D));
+        g2lds16_va(src + 16 * (c ^ (is_v ? vswz(r) : kswz(r))), ldst + m * 1024);
+      }
     }
-    st16(c1, QK::pack(x1));
-    st16(c2, QK::pack(x2));
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the rotated queries are in LDS ...
-  wg_barrier();                              // ... for every wave (the K / V loads stay in flight)
-  u32x4 qf[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) qf[u] = ld16(qbuf + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
+  };
 
-  f32x16 o[ND];
+  // ---- the first row block's queries and this wave's K in flight (V once the tables are built
+  // and the queries rotated: issuing it here would stall that work behind a full load queue)
+  load_q(rb_lo);
+  if (klen > 0) load_kv(false);
+  const int nq = (w < NIB ? 1 : 0) + (w + NW < NIB ? 1 : 0);   // this wave's query loads
+
+  // ---- rotation tables while K lands: frequencies (fp64), then (cos, sin)(r f_i) for the 32
+  // offsets (fp32 revolutions r f_i, hardware sin / cos) and the fraction of each block's base
+  // angle pos0 f_i (fp64) through the hardware sin / cos
+  if (tid < H2) frev[tid] = exp2(-(2.0 * tid / D) * p.log2_theta) * kInvTwoPi;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  wg_barrier();
+  for (int e = tid; e < H2 * 32; e += NT) {
+    const int i = e / 32, r = e % 32;
+    const float rv = static_cast<float>(r) * static_cast<float>(frev[i]);
+    const float f = rv - rintf(rv);
+    ang[e] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+  }
+  if (rot && klen > 0 && lane < H2) cbase[w][lane] = cs_rev(static_cast<double>(bk.pos0) * frev[lane]);
+
+  // ---- queries of a row block, rotated in place in LDS (fp16, scaled into log2 units; rows past
+  // G*B zero): thread (row, quarter of the RoPE pairs), four pairs each
+  auto rotate_q = [&](int rb) {
+    constexpr int QT = 32 * (H2 / 4);   // work items
+    static_assert(H2 % 4 == 0, "query rotation split");
+    for (int it = tid; it < QT; it += NT) {
+      const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
+      const int r = it / (H2 / 4), i0 = 4 * (it % (H2 / 4));   // pairs (i, i + D/2), i in [i0, i0 + 4)
+      const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B, b2 = qr2 % p.B;
+      const float qs = hh2 < p.G ? p.sm_scale_log2 : 0.f;
+      const double qpos = static_cast<double>(p.pos_base + p.W + p.n_tails[d] + b2);
+      // 8-byte halves of the 16-byte chunks holding elements i0 and i0 + D/2
+      unsigned char* c1 = qbuf + r * ROWB + (((i0 / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
+      unsigned char* c2 = qbuf + r * ROWB + ((((i0 + H2) / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
+      const u32x2 a2 = *reinterpret_cast<const u32x2*>(c1), b2v = *reinterpret_cast<const u32x2*>(c2);
+      float x1[4], x2[4];
 #pragma unroll
-  for (int dd = 0; dd < ND; ++dd) o[dd] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const unsigned char* Kt = kbuf + w * BLKB;
-  const unsigned char* Vt = vbuf + w * BLKB;
-  u32x4 pb[2];
+      for (int j = 0; j < 2; ++j) {
+        x1[2 * j] = __uint_as_float(a2[j] << 16);
+        x1[2 * j + 1] = __uint_as_float(a2[j] & 0xffff0000u);
+        x2[2 * j] = __uint_as_float(b2v[j] << 16);
+        x2[2 * j + 1] = __uint_as_float(b2v[j] & 0xffff0000u);
+      }
+      _Float16 y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 cq = cs_rev(qpos * frev[i0 + e]);
+        const float a = x1[e], b = x2[e];
+        y1[e] = static_cast<_Float16>((a * cq.x - b * cq.y) * qs);
+        y2[e] = static_cast<_Float16>((b * cq.x + a * cq.y) * qs);
+      }
+      *reinterpret_cast<u32x2*>(c1) = __builtin_bit_cast(u32x2, y1);
+      *reinterpret_cast<u32x2*>(c2) = __builtin_bit_cast(u32x2, y2);
+    }
+  };
+  if (klen > 0) __builtin_amdgcn_s_waitcnt(wait_vm(NIB));   // this wave's query loads have landed
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  wg_barrier();   // every query share, the angle table and the base angles visible
+  rotate_q(rb_lo);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  wg_barrier();   // the rotated queries visible
+  if (klen > 0) load_kv(true);
+
+  // ---- K (row l32, both halves of every RoPE pair) into registers: rotated here by
+  // (cos, sin)(pos0 f) x (cos, sin)(l32 f), or read rotated from the view; kept for every row block
+  u32x4 kf[NU];
   if (klen > 0) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(NIB));   // K has landed (V may still be in flight)
-    // K row l32 (both halves of every RoPE pair): rotated here, or read rotated from the view
-    u32x4 kf[NU];
+    __builtin_amdgcn_s_waitcnt(wait_vm(NIB));   // K has landed (V in flight)
+    const unsigned char* Kt = ktile + w * BLKB;
     if (rot) {
       float fk[2][E];
 #pragma unroll
@@ -2188,10 +2240,11 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
         BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * (u + NU / 2) + h) ^ kswz(l32)) << 4)), fk[1]);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float2 ck = kcs[u][e];
-          const float a = fk[0][e], b = fk[1][e];
-          fk[0][e] = a * ck.x - b * ck.y;
-          fk[1][e] = b * ck.x + a * ck.y;
+          const int i = 2 * E * u + E * h + e;
+          const float2 ck = cmul(cbase[w][i], ang[i * 32 + l32]);
+          const float a = fk[0][e], c = fk[1][e];
+          fk[0][e] = a * ck.x - c * ck.y;
+          fk[1][e] = c * ck.x + a * ck.y;
         }
         kf[u] = QK::pack(fk[0]);
         kf[u + NU / 2] = QK::pack(fk[1]);
@@ -2200,106 +2253,118 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
 #pragma unroll
       for (int u = 0; u < NU; ++u) kf[u] = ld16(Kt + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
     }
-    f32x16 sv = f32x16{};
-#pragma unroll
-    for (int u = 0; u < NU; ++u) sv = QK::mma(kf[u], qf[u], sv);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
-      const bool ok = (kk < klen) & ((x0 + kk - tailbase) <= bq);   // block rows: causal
-      sv[i] = ok ? sv[i] : -INFINITY;
-      mx = fmaxf(mx, sv[i]);
-    }
-    m_run = xhalf_max(mx);
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
-      l_run += sv[i];
-    }
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      float pv[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) pv[e] = sv[E * cc + e];
-      pb[cc] = PV::pack(pv);
-    }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // V has landed
-  if (klen > 0) {
-    const int key0 = 4 * h + ((lane & 15) >> 2);
+
+  const int sl = w < NS ? w : 0;   // this wave's d-slice of O^T (waves w < NS)
+  const int key0 = 4 * h + ((lane & 15) >> 2);
+  const int vrd = [&] {   // V^T operand read offset of d-slice sl (ds_read_tr16 layout)
+    const int cb2 = (32 * sl + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    return key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
+  }();
+  const size_t pw = verify_partial_words(D);
+  for (int rb = rb_lo; rb < rb_hi; ++rb) {
+    const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
+    const int bq = (32 * rbl + l32) % p.B;                        // this lane's query block token
+    const int tb = tail_unit ? tailb : p.W + d * p.tail_stride + p.n_tails[d];   // draft d's block rows
+    u32x4 qf[NU];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
+    for (int u = 0; u < NU; ++u) qf[u] = ld16(qbuf + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
+    f32x16 sv = f32x16{};
+    float mx = -INFINITY;
+    if (klen > 0) {
 #pragma unroll
-      for (int dd = 0; dd < ND; ++dd) {
-        const int cb2 = (32 * dd + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-        const int voff = key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
-        const u32x2 lo = ds_read_tr16(Vt + voff + 16 * cc * ROWB);
-        const u32x2 hi = ds_read_tr16(Vt + voff + (16 * cc + 8) * ROWB);
-        o[dd] = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[cc], o[dd]);
+      for (int u = 0; u < NU; ++u) sv = QK::mma(kf[u], qf[u], sv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool ok = (kk < klen) & ((x0 + kk - tb) <= bq);   // block rows: causal
+        sv[i] = ok ? sv[i] : -INFINITY;
+        mx = fmaxf(mx, sv[i]);
       }
     }
-    // the draft's block rows into the cache (their K / V came from k_blk / v_blk), once per draft
-    if (rbl == 0 && x0 + klen > tailbase) {
+    mx = xhalf_max(mx);
+    if (lane < 32) red_m[w][l32] = mx;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();   // every row max; every wave has read qbuf and (first row block) the angle table
+    float M = red_m[0][l32];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, red_m[ww][l32]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float lsum = 0.f;
+    if (klen > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+        lsum += sv[i];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        float pv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) pv[e] = sv[E * cc + e];
+        st16(pbuf + ((w * 2 + cc) * 64 + lane) * 16, PV::pack(pv));
+      }
+    }
+    lsum = xhalf_sum(lsum);
+    if (lane < 32) red_l[w][l32] = lsum;
+    const bool more = rb + 1 < rb_hi;
+    if (more) load_q(rb + 1);   // qbuf is free: every wave read it before the barrier above
+    if (rb == rb_lo) {          // this wave's V has landed
+      if (more && nq == 2) __builtin_amdgcn_s_waitcnt(wait_vm(2));
+      else if (more && nq == 1) __builtin_amdgcn_s_waitcnt(wait_vm(1));
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();   // P, row sums and every V tile visible
+
+    // ---- O^T slice sl over the unit's blocks (waves w < NS)
+    f32x16 o = f32x16{};
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+      if (w >= NS || ((bmask >> jb) & 1) == 0) continue;
+      const unsigned char* Vt = vtile + jb * BLKB;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const u32x2 lo = ds_read_tr16(Vt + vrd + 16 * cc * ROWB);
+        const u32x2 hi = ds_read_tr16(Vt + vrd + (16 * cc + 8) * ROWB);
+        const u32x4 pb = ld16(pbuf + ((jb * 2 + cc) * 64 + lane) * 16);
+        o = PV::mma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o);
+      }
+    }
+    // the draft's block rows into the cache (their K / V came from k_blk / v_blk), once
+    if (tail_unit && rb == rb_lo && klen > 0 && x0 + klen > tailb) {
+      const unsigned char* Kt = ktile + w * BLKB;
+      const unsigned char* Vt = vtile + w * BLKB;
       for (int e = lane; e < 32 * KCH; e += 64) {
         const int r = e / KCH, c = e % KCH, x = x0 + r;
-        if (r < klen && x >= tailbase) {
-          const int64_t dst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 8 * c;
-          st16(kc + dst, ld16(Kt + r * ROWB + ((c ^ kswz(r)) << 4)));
-          st16(vc + dst, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
+        if (r < klen && x >= tailb) {
+          const int64_t o2 = (static_cast<int64_t>(kvh) * p.S_cap + x) * D + 8 * c;
+          st16(kc + o2, ld16(Kt + r * ROWB + ((c ^ kswz(r)) << 4)));
+          st16(vc + o2, ld16(Vt + r * ROWB + ((c ^ vswz(r)) << 4)));
         }
       }
     }
-  }
-  __syncthreads();   // K / V tiles are dead: the space is reused for the fold
-
-  // ---- fold the waves (same rows, different keys) into one partial, in a fixed order: waves 0-3
-  // write their rescaled O to four LDS slots, waves 4.. add theirs to slot w - 4, the four slots are
-  // summed in slot order
-  const float l_tot = xhalf_sum(l_run);
-  if (lane < 32) {
-    red_m[w][l32] = m_run;
-    red_l[w][l32] = l_tot;
-  }
-  __syncthreads();
-  float M = -INFINITY;
+    if (w < NS) {
+      float L = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][l32]);
-  float L = 0.f;
+      for (int ww = 0; ww < NW; ++ww) L += red_l[ww][l32];
+      float* dst = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + slot) * pw;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww)
-    if (red_m[ww][l32] != -INFINITY) L += red_l[ww][l32] * __builtin_amdgcn_exp2f(red_m[ww][l32] - M);
-  const float scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  float* obuf = reinterpret_cast<float*>(tiles);   // four slots of 32 x OS floats
-  float* ob = obuf + (w & 3) * 32 * OS;
-  auto put = [&](bool add) {
-#pragma unroll
-    for (int dd = 0; dd < ND; ++dd)
-#pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        f32x4* dst = reinterpret_cast<f32x4*>(ob + l32 * OS + 32 * dd + 8 * ig + 4 * h);
-        const f32x4 rv = {o[dd][4 * ig] * scale, o[dd][4 * ig + 1] * scale, o[dd][4 * ig + 2] * scale, o[dd][4 * ig + 3] * scale};
-        *dst = add ? *dst + rv : rv;
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(dst + ((sl * 4 + j) * 64 + lane) * 4) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+      if (sl == 0 && lane < 32) {
+        dst[32 * D + l32] = M;
+        dst[32 * D + 32 + l32] = L;
       }
-  };
-  if (w < 4) put(false);
-  __syncthreads();
-  if constexpr (NW > 4) {
-    if (w >= 4) put(true);
-    __syncthreads();
-  }
-  float* dstp = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + split) * verify_partial_words(D);
-  for (int e = tid; e < 32 * CPR; e += NT) {
-    const int row = e / CPR, c = e % CPR;
-    f32x4 a = *reinterpret_cast<const f32x4*>(obuf + row * OS + 4 * c);
-#pragma unroll
-    for (int sl = 1; sl < 4; ++sl) a = a + *reinterpret_cast<const f32x4*>(obuf + sl * 32 * OS + row * OS + 4 * c);
-    *reinterpret_cast<f32x4*>(dstp + row * D + 4 * c) = a;
-  }
-  if (w == 0 && lane < 32) {
-    dstp[32 * D + l32] = M;
-    dstp[32 * D + 32 + l32] = L;
+    }
+    if (more) {   // the next row block's queries: landed (this wave's share), visible, rotated
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      wg_barrier();
+      rotate_q(rb + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      wg_barrier();
+    }
   }
 }
 
@@ -2373,6 +2438,91 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
   }
   const f32x4 res = At * (1.f / Lt);
   const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
+  if (p.out_bf16) {
+    bf16 b4[4] = {static_cast<bf16>(res[0]), static_cast<bf16>(res[1]), static_cast<bf16>(res[2]), static_cast<bf16>(res[3])};
+    *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + oidx) = *reinterpret_cast<const u32x2*>(b4);
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + oidx) = res;
+  }
+}
+
+// Verify merge for the bf16 split kernel: fixed-order log-sum-exp combination, per (kv head, query
+// row), of the partials of the row's draft: the window units' and that draft's tail units', NH
+// key groups each.  O is stored in the accumulator order of the split kernel: element (row q,
+// d = 32s + 8j + 4h + e) at ((s*4 + j)*64 + q + 32h)*4 + e.  One workgroup per (kv head, row),
+// kv head = blockIdx % Hkv as in the split kernel (the partials' XCD); thread (slot group sg,
+// 4 consecutive d).
+template <int D>
+__global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, const float* __restrict__ part,
+                                                               void* __restrict__ out) {
+  constexpr int MAXF = 8;                     // slots folded per thread per pass
+  constexpr int CPR = D / 4;                  // 4-float chunks per row
+  constexpr int SG = 256 / CPR;               // slot groups
+  const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;
+  const int q = r % 32, rb = r / 32;
+  const int dft = rb / p.nrb_d, rl = r - 32 * p.nrb_d * dft;   // draft, row within the draft
+  const int hh = rl / p.B, b = rl % p.B;
+  if (hh >= p.G) return;
+  const int sg = threadIdx.x / CPR, c = threadIdx.x % CPR;
+  const int s = c / 8, j = (c % 8) / 2, hf = c % 2;
+  const int ooff = ((s * 4 + j) * 64 + q + 32 * hf) * 4;
+  // slots of this draft: the window units', then its own tail units'
+  const int ntb = ceil_div(p.n_tails[dft] + p.B, kVerifyBlock);
+  const int n_used = p.n_ws + ceil_div(ntb, kVerifyUnitBlocks);
+  const size_t pw = verify_partial_words(D);
+  const float* base = part + (static_cast<size_t>(kvh) * p.n_rb + rb) * p.n_split * pw;
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = f32x4{};
+  for (int s0 = sg; s0 < n_used; s0 += SG * MAXF) {
+    float mm[MAXF], ll[MAXF];
+    f32x4 ov[MAXF];
+#pragma unroll
+    for (int jj = 0; jj < MAXF; ++jj) {
+      const int sl = s0 + jj * SG;
+      mm[jj] = -INFINITY;
+      ll[jj] = 0.f;
+      ov[jj] = f32x4{};
+      if (sl < n_used) {
+        const float* ps = base + sl * pw;
+        mm[jj] = ps[32 * D + q];
+        ll[jj] = ps[32 * D + 32 + q];
+        ov[jj] = *reinterpret_cast<const f32x4*>(ps + ooff);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < MAXF; ++jj) {
+      if (mm[jj] == -INFINITY) continue;
+      if (mm[jj] > M) {
+        const float f = __builtin_amdgcn_exp2f(M - mm[jj]);
+        acc *= f;
+        L *= f;
+        M = mm[jj];
+      }
+      const float wgt = __builtin_amdgcn_exp2f(mm[jj] - M);
+      acc += wgt * ov[jj];
+      L += wgt * ll[jj];
+    }
+  }
+  __shared__ float sM[256], sL[256];
+  __shared__ f32x4 sA[256];
+  sM[threadIdx.x] = M;
+  sL[threadIdx.x] = L;
+  sA[threadIdx.x] = acc;
+  __syncthreads();
+  if (sg != 0) return;
+  float Mt = -INFINITY;
+  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, sM[g * CPR + c]);
+  float Lt = 0.f;
+  f32x4 At = f32x4{};
+  for (int g = 0; g < SG; ++g) {
+    const float mg = sM[g * CPR + c];
+    if (mg == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(mg - Mt);
+    Lt += f * sL[g * CPR + c];
+    At += f * sA[g * CPR + c];
+  }
+  const f32x4 res = At * (1.f / Lt);
+  const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * D + 4 * c;
   if (p.out_bf16) {
     bf16 b4[4] = {static_cast<bf16>(res[0]), static_cast<bf16>(res[1]), static_cast<bf16>(res[2]), static_cast<bf16>(res[3])};
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + oidx) = *reinterpret_cast<const u32x2*>(b4);
@@ -2469,7 +2619,7 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
                     void* out, void* ws, hipStream_t st, const void* kview) {
   float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + kVerifyWsHeader);
   if constexpr (std::is_same<T, bf16>::value) {
-    const dim3 grid(p.Hkv * p.n_rb * p.n_split), block(64 * kVerifyWavesDma);
+    const dim3 grid(p.Hkv * (p.n_ws + p.n_drafts * p.n_ts)), block(64 * kVerifyWavesDma);
     if (kview)
       hipLaunchKernelGGL((verify_dma_kernel<D, true>), grid, block, 0, st, p, static_cast<const T*>(qb),
                          static_cast<const T*>(kb), static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc),
@@ -2478,14 +2628,17 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
       hipLaunchKernelGGL((verify_dma_kernel<D, false>), grid, block, 0, st, p, static_cast<const T*>(qb),
                          static_cast<const T*>(kb), static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc),
                          static_cast<const _Float16*>(nullptr), part);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+    hipLaunchKernelGGL((verify_merge_dma_kernel<D>), dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
+                       static_cast<const float*>(part), out);
   } else {
     hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(256), 0, st, p,
                        static_cast<const T*>(qb), static_cast<const T*>(kb), static_cast<const T*>(vb),
                        static_cast<T*>(kc), static_cast<T*>(vc), part);
+    if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
+    hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
+                       static_cast<const float*>(part), out);
   }
-  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-  hipLaunchKernelGGL(verify_merge_kernel, dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
-                     static_cast<const float*>(part), out);
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 

@@ -224,15 +224,24 @@ def test_kv_project_call_errors():
 
 
 def test_workspace_size_covers_largest_block():
+    """bf16: one partial per (kv head, row block, unit); units of 8 key blocks over the window,
+    then over a draft's tail (its longest: tail_cap rows).  fp32: one per (kv head, row block,
+    4-block split) of the whole key list."""
     g = synth.CONFIGS[4].geom
-    ws = fd.verify_workspace_bytes(g, 8)
-    # the largest split count is reached when n_tail + B == tail_cap
-    nblk = (-(-g.prefix_len // 32) + g.n_views * g.n_frames * -(-g.tok_per_frame // 32)
-            + -(-g.tail_cap // 32))
-    splits = -(-nblk // 4)
-    assert ws >= g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4
+    pw = (32 * g.head_dim + 64) * 4
+    wblk = -(-g.prefix_len // 32) + g.n_views * g.n_frames * -(-g.tok_per_frame // 32)
+    units = -(-wblk // 8) + -(-(-(-g.tail_cap // 32)) // 8)
+    assert units == 18 + 1
+    assert fd.verify_workspace_bytes(g, 8) >= g.n_kv_heads * units * pw
     # 16-token blocks: G*16 = 64 query rows per kv head, two 32-row blocks
-    assert fd.verify_workspace_bytes(g, 16) >= 2 * g.n_kv_heads * splits * (32 * g.head_dim + 64) * 4
+    assert fd.verify_workspace_bytes(g, 16) >= 2 * g.n_kv_heads * units * pw
+    g64 = g.replace(head_dim=64)
+    assert fd.verify_workspace_bytes(g64, 8) >= g.n_kv_heads * units * (32 * 64 + 64) * 4
+    g32 = g.replace(dtype=synth.F32)
+    splits = -(-(wblk + -(-g.tail_cap // 32)) // 4)
+    assert fd.verify_workspace_bytes(g32, 8) >= g.n_kv_heads * splits * pw
+    # batched: every draft's row blocks
+    assert fd.verify_batched_workspace_bytes(g, 6, 8) >= 6 * g.n_kv_heads * units * pw
 
 
 def test_verify_batched_call_errors():

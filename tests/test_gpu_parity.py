@@ -604,3 +604,100 @@ def test_stream_insert_fused(cid, dt):
 @pytest.mark.parametrize("w", EXTRA, ids=lambda w: w.name)
 def test_stream_insert_fused_edge_geometries(w):
     check_stream_insert(w, 0, w.first_t + w.geom.n_frames)   # a later ring phase
+
+
+# ---------------------------------------------------------------------------- fp16 operand range
+# For bf16 inputs the rotated keys, and the rotated queries scaled by log2(e)/sqrt(D), are
+# rounded to fp16 for the Q K^T matrix cores.  A rotated element is x cos - y sin (or
+# x sin + y cos) of a stored pair (x, y), so its magnitude never exceeds sqrt(x^2 + y^2):
+# stored key elements of +-45,056 (bf16-exact) give at most 63,718, below fp16's largest
+# finite value 65,504.  The test puts such keys in one frequency pair of every key and
+# queries of +-249,856 (scaled: at most 45,061) in another, with the other operand zero in
+# each of those pairs, so the exact scores are those of the remaining pairs: any overflow to
+# inf would show up as a NaN (inf * 0) in the outputs.
+KBIG, QBIG = 45056.0, 249856.0
+PK, PQ = 5, 9        # frequency pairs (i, i + D/2) carrying the large keys / the large queries
+
+
+def _big_k(a, seed):
+    a = np.array(a, np.float32, copy=True)
+    h = a.shape[-1] // 2
+    sg = np.random.default_rng(seed).choice([-1.0, 1.0], size=a.shape[:-1] + (2,)).astype(np.float32)
+    a[..., PK], a[..., PK + h] = KBIG * sg[..., 0], KBIG * sg[..., 1]
+    a[..., PQ] = a[..., PQ + h] = 0.0
+    return a
+
+
+def _big_q(a, seed):
+    a = np.array(a, np.float32, copy=True)
+    h = a.shape[-1] // 2
+    sg = np.random.default_rng(seed).choice([-1.0, 1.0], size=a.shape[:-1] + (2,)).astype(np.float32)
+    a[..., PQ], a[..., PQ + h] = QBIG * sg[..., 0], QBIG * sg[..., 1]
+    a[..., PK] = a[..., PK + h] = 0.0
+    return a
+
+
+def test_fp16_operand_bound():
+    """Streaming, batched verify with and without a rotated view, and single verify at the
+    fp16 operand bound (config-2 shapes, two ring phases): finite and within the bf16
+    tolerance of the oracle."""
+    w = synth.CONFIGS[2]
+    g = w.geom
+    layer, t_last = 0, w.first_t + 1
+    pk, pv = synth.prefix_kv(w, layer)
+    pk = _big_k(pk, 1)
+    win = fd_oracle.StreamWindow(g, pk, pv)
+    kc, vc = H.new_cache(g)
+    kc[:, : g.prefix_len, :] = H.dev(np.transpose(pk, (1, 0, 2)), g)
+    vc[:, : g.prefix_len, :] = H.dev(np.transpose(pv, (1, 0, 2)), g)
+    assert float(kc.abs().max()) == KBIG
+    for t in range(t_last + 1):
+        ks, vs = [], []
+        for v in range(g.n_views):
+            k, vv = synth.frame_kv(w, layer, v, t)
+            k = _big_k(k, 100 + 8 * t + v)
+            win.push(v, t, k, vv)
+            ks.append(k)
+            vs.append(vv)
+        fd.kv_insert_frame(g, kc, vc, H.dev(np.stack(ks), g), H.dev(np.stack(vs), g), t)
+        if t < t_last - 1:
+            continue
+        q = _big_q(np.concatenate([synth.frame_q(w, layer, v, t) for v in range(g.n_views)]), 7 + t)
+        want = fd_oracle.oracle_stream(g, win, q)
+        assert np.isfinite(want).all()
+        got = H.stream_out(w, layer, kc, vc, t, q=H.dev(q, g))
+        err = H.check_out(got.float().cpu().numpy(), want, g, "f32", ("fp16 bound stream", t))
+        H.say(f"  fp16 bound: stream t {t} max-abs {err:.3e}")
+    # verify: one draft through fd_verify_attn, two drafts through the batched call (rotated
+    # view from fd_rotate_window), every tail and block at the bound too
+    n_tails, stride, B = [12, 5], 32, 8
+    kview = torch.empty((g.n_kv_heads, g.window, g.head_dim), dtype=torch.float16, device=H.DEV)
+    fd.rotate_window(g, kc, t_last, kview)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(kview).all()) and float(kview.abs().max()) > 6.0e4
+    qs, kbs, vbs, wants = [], [], [], []
+    for d, nt in enumerate(n_tails):
+        kt, vt = synth.tail_kv(w, 200 + d, nt)
+        kt = _big_k(kt, 300 + d)
+        qb, kb, vb = synth.block_qkv(w, 200 + d, B)
+        qb, kb = _big_q(qb, 400 + d), _big_k(kb, 500 + d)
+        r0 = g.window + d * stride
+        kc[:, r0: r0 + nt] = H.dev(np.transpose(kt, (1, 0, 2)), g)
+        vc[:, r0: r0 + nt] = H.dev(np.transpose(vt, (1, 0, 2)), g)
+        wants.append(fd_oracle.oracle_verify(g, win, kt, vt, qb, kb, vb))
+        qs.append(qb)
+        kbs.append(kb)
+        vbs.append(vb)
+    for view in (None, kview):
+        out = torch.empty((2, B, g.n_q_heads, g.head_dim), dtype=torch.float32, device=H.DEV)
+        ws = torch.empty(fd.verify_batched_workspace_bytes(g, 2, B), dtype=torch.uint8, device=H.DEV)
+        fd.verify_attn_batched(g, H.dev(np.stack(qs), g), H.dev(np.stack(kbs), g), H.dev(np.stack(vbs), g), kc, vc,
+                               t_last, n_tails, stride, B, out, ws, k_view=view)
+        for d in range(2):
+            err = H.check_out(out[d].cpu().numpy(), wants[d], g, "f32", ("fp16 bound batched", d))
+            H.say(f"  fp16 bound: batched verify draft {d} view {view is not None} max-abs {err:.3e}")
+    out = torch.empty((B, g.n_q_heads, g.head_dim), dtype=torch.float32, device=H.DEV)
+    ws = torch.empty(fd.verify_workspace_bytes(g, B), dtype=torch.uint8, device=H.DEV)
+    fd.verify_attn(g, H.dev(qs[0], g), H.dev(kbs[0], g), H.dev(vbs[0], g), kc, vc, t_last, n_tails[0], B, out, ws)
+    err = H.check_out(out.cpu().numpy(), wants[0], g, "f32", "fp16 bound verify")
+    H.say(f"  fp16 bound: verify max-abs {err:.3e}")
