@@ -454,18 +454,17 @@ struct StreamTiles {
 // shifted positions), and written to the workspace as the QK^T operand format (fp16 for
 // bf16 inputs).  The attention kernel that follows then streams rotated tiles, so a key
 // is rotated once per window instead of once per workgroup that reads it.
-// Workgroup = 256 threads = one kv head x 128 window rows; thread = (row within a block of
-// RPP rows, 16-byte chunk of the first half of the row and its RoPE partner chunk).
-// When P and T are multiples of RPP no block straddles two segments, so the rotation of
-// row base + r is cs(base) (per block) times cs(r) (per thread); otherwise each element's
-// angle is reduced on its own.
+// Key workgroup = 256 threads = RPW window rows x up to kRopeHeads kv heads; thread = (row,
+// 16-byte chunk of the first half of the row and its RoPE partner chunk), so a row's angles
+// are computed once (fp64 reduction, cs_angle) for every head of the workgroup.
 // For bf16 inputs the workgroups past the first nkb also rotate the queries (the new frames'
 // tokens, or every window token for a cold start) at their positions, scale them by
 // log2(e)/sqrt(D) and store them as fp16 in the input's [tokens][Hq][D] order: the attention
 // kernel loads its QK^T operands straight from there.  Such a workgroup takes 32 tokens and
-// up to four query heads of the kv head (kRopeQTok x min(G, 4) rows); the heads share a
-// token's angles, so they come from a per-workgroup LDS table of the 32 tokens' (cos, sin).
-// Every thread issues all of its global loads before it computes an angle.
+// up to four query heads of one kv head; thread = (token, chunk pair), the heads sharing the
+// token's angles.
+// Every thread loads its frequencies, then issues all of its row loads, then computes its
+// angles while the rows are in flight: no barrier.
 // ---------------------------------------------------------------------------------------
 __device__ inline int64_t row_pos(const KParams& p, int x) {
   if (x < p.P) return p.pos_base + x;
@@ -475,6 +474,14 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
 }
 
 constexpr int kRopeQTok = 32;   // tokens per query workgroup of the rotation pass
+constexpr int kRopeHeads = 4;   // kv heads per key workgroup of the rotation pass (sharing angles)
+// key workgroups of the rotation pass: RPW = 256 / (D/2 / E) rows (E elements per 16-byte chunk of
+// the input type) times ceil(Hkv / kRopeHeads) head groups
+template <typename T, int D>
+inline int rope_key_workgroups(const KParams& p) {
+  constexpr int RPW = 256 / (D / 2 / (16 / static_cast<int>(sizeof(T))));
+  return ceil_div(p.W, RPW) * ceil_div(p.Hkv, kRopeHeads);
+}
 
 // The new frames to insert in the same pass (kn == nullptr: none).  Rows of ring slot s_new
 // are then read from kn / vn ([V][T][Hkv][D], pre-RoPE) instead of the cache, and copied into
@@ -492,7 +499,7 @@ __host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
 template <typename T, int D, bool INS>   // INS: the new frames are inserted by this pass (nf)
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
                                                           typename Path<T>::QKT* __restrict__ krot,
-                                                          int aligned, int nkb, const T* __restrict__ q,
+                                                          int nkb, const T* __restrict__ q,
                                                           typename Path<T>::QKT* __restrict__ qrot,
                                                           int2* __restrict__ tiles, const NewFrame<T> nf) {
 #pragma clang fp contract(off)   // every instantiation rounds a rotated row the same way
@@ -509,125 +516,121 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   using QKT = typename Path<T>::QKT;
   constexpr int E = In::E;
   constexpr int H2 = D / 2;
-  constexpr int CH = H2 / E;
-  constexpr int RPP = 256 / CH;
-  constexpr int ROWS = 128;
-  constexpr int NB = ROWS >= RPP ? ROWS / RPP : 1;
-  __shared__ double sfreq[H2];
-  __shared__ float2 csb[NB][H2];
-  __shared__ float2 qcs[kRopeQTok][H2];
-  const int tid = threadIdx.x, kvh = blockIdx.y, row_base = blockIdx.x * ROWS;
-  const int rr = tid / CH, c = tid % CH;
-  if (tiles && blockIdx.x == 0 && blockIdx.y == 0) {   // the attention kernel's tile table
+  constexpr int CH = H2 / E;       // threads per row (RoPE chunk pairs)
+  constexpr int RPW = 256 / CH;     // key rows per workgroup
+  const int tid = threadIdx.x;
+  if (tiles && blockIdx.x == 0) {   // the attention kernel's tile table
     const StreamTiles tt(p);
     for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
       for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
   }
   if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token, head kvh*G + hh)
-    // streaming: the newest frames' tokens [V*T]; full window: every window token [W]
-    constexpr int QP = (4 * kRopeQTok + RPP - 1) / RPP;   // passes for up to four heads
+    // thread (token tl, RoPE chunk pair c) for the workgroup's GH heads of kv head kvh, which
+    // share the token's angles; frequencies loaded first, angles computed while the rows fly.
+    // Streaming: the newest frames' tokens [V*T]; full window: every window token [W]
+    const int kvh = (blockIdx.x - nkb) % p.Hkv, tl = tid / CH, c = tid % CH;
     const int G = p.G, GH = rope_q_heads(G), NTOK = p.qmode == 0 ? p.V * p.T : p.W;
-    const int qb = blockIdx.x - nkb, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
-    const int nrows = kRopeQTok * GH;
+    const int qb = (blockIdx.x - nkb) / p.Hkv, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
+    const int tg = tok0 + tl;
+    if (tl >= kRopeQTok || tg >= NTOK) return;
     const float sc = p.sm_scale_log2;
-    u32x4 raw[QP][2];
-    int64_t offs[QP];
+    double fr[E];
 #pragma unroll
-    for (int b = 0; b < QP; ++b) {   // all loads first
-      const int r = b * RPP + rr, tl = r / GH, tg = tok0 + tl;
-      offs[b] = -1;
-      if (r >= nrows || tg >= NTOK) continue;
-      offs[b] = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hsub * GH + r % GH) * D;
-      raw[b][0] = ld16(q + offs[b] + E * c);
-      raw[b][1] = ld16(q + offs[b] + H2 + E * c);
+    for (int e = 0; e < E; ++e) fr[e] = p.inv_freq[E * c + e] * kInvTwoPi;
+    u32x4 raw[4][2];
+    const int64_t base = (static_cast<int64_t>(tg) * p.Hq + kvh * G + hsub * GH) * D;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh >= GH) continue;
+      raw[hh][0] = ld16(q + base + hh * D + E * c);
+      raw[hh][1] = ld16(q + base + hh * D + H2 + E * c);
     }
-    for (int e = tid; e < kRopeQTok * H2; e += 256) {   // (cos, sin) table of the 32 tokens
-      const int tl = e / H2, i = e % H2, tg = min(tok0 + tl, NTOK - 1);
+    float2 cs[E];
+    {
       const int v = tg / p.T, it = tg - v * p.T;
       const double pos = static_cast<double>(
           p.qmode == 0 ? p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T + it : row_pos(p, tg));
-      qcs[tl][i] = cs_rev(pos * (p.inv_freq[i] * kInvTwoPi));
-    }
-    __syncthreads();
 #pragma unroll
-    for (int b = 0; b < QP; ++b) {
-      if (offs[b] < 0) continue;
-      const int tl = (b * RPP + rr) / GH;
+      for (int e = 0; e < E; ++e) cs[e] = cs_rev(pos * fr[e]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh >= GH) continue;
       float x1[E], x2[E];
-      In::unpack(raw[b][0], x1);
-      In::unpack(raw[b][1], x2);
+      In::unpack(raw[hh][0], x1);
+      In::unpack(raw[hh][1], x2);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float2 cs = qcs[tl][E * c + e];
-        const float a = x1[e], bb = x2[e];
-        const float2 r = rot2(a, bb, cs);
+        const float2 r = rot2(x1[e], x2[e], cs[e]);
         x1[e] = r.x * sc;
         x2[e] = r.y * sc;
       }
-      st16(qrot + offs[b] + E * c, pack_rounded(x1));
-      st16(qrot + offs[b] + H2 + E * c, pack_rounded(x2));
+      st16(qrot + base + hh * D + E * c, pack_rounded(x1));
+      st16(qrot + base + hh * D + H2 + E * c, pack_rounded(x2));
     }
     return;
   }
-  u32x4 raw[NB][2], vraw[NB][2];   // all loads first
-  bool isnew[NB];                   // a row of the new frame (read from kn / vn)
+  // ---- keys: thread (row r, RoPE chunk pair c) of the workgroup's RPW rows, for HG kv heads
+  // that share the row's angles; the thread's frequencies are loaded before its rows, so the
+  // angles are computed while the rows are in flight
+  const int nhg = (p.Hkv + kRopeHeads - 1) / kRopeHeads;
+  const int rb = blockIdx.x / nhg, hg = blockIdx.x % nhg;
+  const int r = tid / CH, c = tid % CH, x = rb * RPW + r;
+  const bool live = x < p.W;
+  double fr[E];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int x = row_base + b * RPP + rr;
-    isnew[b] = false;
-    if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
+  for (int e = 0; e < E; ++e) fr[e] = p.inv_freq[E * c + e];
+  int64_t nrow = -1;   // INS: the row's index in k_new / v_new ([V*T] rows) if it is a new-frame row
+  if (INS && live && x >= p.P) {
+    const int xr = x - p.P, v = xr / (p.F * p.T), sl = (xr / p.T) % p.F, i = xr % p.T;
+    if (sl == p.s_new) nrow = v * p.T + i;
+  }
+  u32x4 raw[kRopeHeads][2], vraw[kRopeHeads][2];
+#pragma unroll
+  for (int hh = 0; hh < kRopeHeads; ++hh) {
+    const int kvh = hg * kRopeHeads + hh;
+    if (!live || kvh >= p.Hkv) continue;
     const T* src = kc + (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-    if (INS && x >= p.P) {
-      const int xr = x - p.P, v = xr / (p.F * p.T), s = (xr / p.T) % p.F, i = xr % p.T;
-      if (s == p.s_new) {
-        const int64_t nrow = (static_cast<int64_t>(v * p.T + i) * p.Hkv + kvh) * D;
-        isnew[b] = true;
-        src = nf.kn + nrow;
-        vraw[b][0] = ld16(nf.vn + nrow + E * c);
-        vraw[b][1] = ld16(nf.vn + nrow + H2 + E * c);
-      }
+    if (INS && nrow >= 0) {
+      src = nf.kn + (nrow * p.Hkv + kvh) * D;
+      vraw[hh][0] = ld16(nf.vn + (nrow * p.Hkv + kvh) * D + E * c);
+      vraw[hh][1] = ld16(nf.vn + (nrow * p.Hkv + kvh) * D + H2 + E * c);
     }
-    raw[b][0] = ld16(src + E * c);
-    raw[b][1] = ld16(src + H2 + E * c);
+    raw[hh][0] = ld16(src + E * c);
+    raw[hh][1] = ld16(src + H2 + E * c);
   }
-  if (tid < H2) sfreq[tid] = p.inv_freq[tid];
-  for (int e = tid; e < NB * H2; e += 256) {
-    const int b = e / H2, i = e % H2, x0 = row_base + b * RPP;
-    if (x0 < p.W) csb[b][i] = cs_angle(static_cast<double>(row_pos(p, x0)) * p.inv_freq[i]);
+  float2 cs[E];
+  {
+    const double pos = static_cast<double>(live ? row_pos(p, x) : 0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs[e] = cs_angle(pos * fr[e]);
   }
-  __syncthreads();
-  float2 csr[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) csr[e] = cs_angle(static_cast<double>(rr) * sfreq[E * c + e]);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int x = row_base + b * RPP + rr;
-    if (x >= p.W || (ROWS < RPP && rr >= ROWS)) continue;
+  for (int hh = 0; hh < kRopeHeads; ++hh) {
+    const int kvh = hg * kRopeHeads + hh;
+    if (!live || kvh >= p.Hkv) continue;
     float x1[E], x2[E];
-    In::unpack(raw[b][0], x1);
-    In::unpack(raw[b][1], x2);
-    const int64_t pos = aligned ? 0 : row_pos(p, x);
+    In::unpack(raw[hh][0], x1);
+    In::unpack(raw[hh][1], x2);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int i = E * c + e;
-      const float2 cs = aligned ? cmul(csb[b][i], csr[e]) : cs_angle(static_cast<double>(pos) * sfreq[i]);
-      const float a = x1[e], bb = x2[e];
-      const float2 r = rot2(a, bb, cs);
-      x1[e] = r.x;
-      x2[e] = r.y;
+      const float2 rr2 = rot2(x1[e], x2[e], cs[e]);
+      x1[e] = rr2.x;
+      x2[e] = rr2.y;
     }
     QKT* dst = krot + (static_cast<int64_t>(kvh) * p.W + x) * D;
     st16(dst + E * c, pack_rounded(x1));
     st16(dst + H2 + E * c, pack_rounded(x2));
-    if (INS && isnew[b]) {   // the new frame's row into the cache: K as read, V
+    if (INS && nrow >= 0) {   // the new frame's row into the cache: K as read, V
       const int64_t cdst = (static_cast<int64_t>(kvh) * p.S_cap + x) * D;
-      st16(nf.kc + cdst + E * c, raw[b][0]);
-      st16(nf.kc + cdst + H2 + E * c, raw[b][1]);
-      st16(nf.vc + cdst + E * c, vraw[b][0]);
-      st16(nf.vc + cdst + H2 + E * c, vraw[b][1]);
+      st16(nf.kc + cdst + E * c, raw[hh][0]);
+      st16(nf.kc + cdst + H2 + E * c, raw[hh][1]);
+      st16(nf.vc + cdst + E * c, vraw[hh][0]);
+      st16(nf.vc + cdst + H2 + E * c, vraw[hh][1]);
     }
   }
 }
+
 
 // ---------------------------------------------------------------------------------------
 // Streaming-prefill attention over the rotated window.
@@ -2535,8 +2538,6 @@ template <typename T, int D>
 int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                     hipStream_t st, const void* kn, const void* vn) {
   using QKT = typename Path<T>::QKT;
-  constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
-  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
   QKT* krot = static_cast<QKT*>(ws);
   // bf16 path: rotated, scaled queries, the tile table and the partial slots of split views
   // after the keys
@@ -2546,17 +2547,17 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                     : nullptr;
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D) +
                                          stream_tiles_bytes(0, p.P, p.T, p.V, p.F));
-  const int nkb = (p.W + 127) / 128;
+  const int nkb = rope_key_workgroups<T, D>(p);
   const int nqk = b16 ? ceil_div(p.V * p.T, kRopeQTok) * (p.G / rope_q_heads(p.G)) : 0;
   const NewFrame<T> nf{static_cast<const T*>(kn), static_cast<const T*>(vn),
                        kn ? const_cast<T*>(static_cast<const T*>(kc)) : nullptr,
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
   if (kn)
-    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles, nf);
+    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, nf);
   else
-    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, aligned, nkb, static_cast<const T*>(q), qrot, tiles, nf);
+    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, nf);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
@@ -2580,14 +2581,12 @@ template <int D>
 int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                      hipStream_t st) {
   using QKT = _Float16;
-  constexpr int RPP = 256 / (D / 2 / Path<bf16>::In::E);
-  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
   QKT* krot = static_cast<QKT*>(ws);
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
-  const int nkb = (p.W + 127) / 128, nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
-  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(nkb + nqk, p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const bf16*>(kc), krot, aligned, nkb, static_cast<const bf16*>(q), qrot, tiles,
+  const int nkb = rope_key_workgroups<bf16, D>(p), nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
+  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles,
                      NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr});
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   KParams pf = p;   // the frame segments
@@ -2645,11 +2644,9 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
 // The rotation pass alone (keys only, no queries, no tile table, no insert).
 template <typename T, int D>
 int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStream_t st) {
-  constexpr int RPP = 256 / (D / 2 / Path<T>::In::E);
-  const int aligned = (p.P % RPP == 0) && (p.T % RPP == 0);
-  const int nkb = (p.W + 127) / 128;
-  hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb, p.Hkv), dim3(256), 0, st, p, static_cast<const T*>(kc),
-                     static_cast<typename Path<T>::QKT*>(kview), aligned, nkb, static_cast<const T*>(nullptr),
+  const int nkb = rope_key_workgroups<T, D>(p);
+  hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb), dim3(256), 0, st, p, static_cast<const T*>(kc),
+                     static_cast<typename Path<T>::QKT*>(kview), nkb, static_cast<const T*>(nullptr),
                      static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr),
                      NewFrame<T>{nullptr, nullptr, nullptr, nullptr});
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
