@@ -1310,6 +1310,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   auto kswz = [](uint32_t r) { return StageMap<D>::kswz(r); };
   auto vswz = [](uint32_t key) { return StageMap<D>::vswz(key); };
   int vstart = 0;   // start of segment v in the end-to-end order
+  u32x4 qf[NU];     // QK^T B operand: the lane's query row, d in [16u + 8h, 16u + 8h + 8)
+  int pf = 0;       // the job's first tile and query operands were issued during the last epilogue
   for (int oi = 0; oi < p.nseg; ++oi) {
   const int v = sp.order(oi);   // segment p.seg0 + v of this launch
   const int nv = sp.view_tiles(v);
@@ -1339,7 +1341,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 
   const int ntiles = jb - ja;
   // The job's tiles t = 0 .. ntiles-1 (tile ja + t of view v): group g takes t = g, g+2, ...
-  // and keeps tile t in LDS slot t & 3.  Their table entries are read with scalar loads.
+  // and keeps tile t in LDS slot (t + 3) & 3 (tile 0 in slot 3, the one the epilogue leaves
+  // free, so the next job's tile 0 can land during it).  Table entries are read with scalar loads.
   const int2* jt = tiles + (stt.offset(p.seg0 + v) + ja);
   const int qrow0 = stt.qrow0(p, p.seg0 + v);   // query / output row of the segment's token 0
 
@@ -1350,10 +1353,10 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   const uint32_t lds_buf = lds_addr(buf);
   using SM = StageMap<D>;
   static_assert(SM::NL == NKL && SM::NL == NVL, "staging map");
-  auto stage = [&](int t) {
-    const int2 d = jt[t];
+  auto stage = [&](const int2* tab, int t) {
+    const int2 d = tab[t];
     const int row0 = d.x, lastr = (d.y & 127) - 1;
-    const uint32_t Kb = lds_buf + (t & 3) * SLOT, Vb = Kb + KSLOT;
+    const uint32_t Kb = lds_buf + ((t + 3) & 3) * SLOT, Vb = Kb + KSLOT;
     const int wrs = uni(wr);
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(krot + (static_cast<int64_t>(kvh) * p.W + row0) * D);
     const unsigned char* vb = reinterpret_cast<const unsigned char*>(vc + (static_cast<int64_t>(kvh) * p.S_cap + row0) * D);
@@ -1382,17 +1385,19 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
     }
   };
 
-  // ---- prologue: tile t = grp of the job lands while the query operands load
-  if (grp < ntiles) stage(uni(grp));
-  // QK^T B operand: the lane's query row (rotated and scaled by the rotation pass), d in
-  // [16u + 8h, 16u + 8h + 8)
-  u32x4 qf[NU];
-  {
+  // the lane's query row of the segment whose token 0 is query row r0 (rotated and scaled by the
+  // rotation pass)
+  auto load_q = [&](int r0) {
     const bool valid = my_tok < p.qtok;
-    const _Float16* src = qrot + (static_cast<int64_t>(qrow0 + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
+    const _Float16* src = qrot + (static_cast<int64_t>(r0 + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
 #pragma unroll
     for (int u = 0; u < NU; ++u) qf[u] = valid ? ld16(src + 2 * E * u) : u32x4{0u, 0u, 0u, 0u};
-  }
+  };
+
+  // ---- prologue: tile t = grp of the job lands while the query operands load (tile 0 and the
+  // queries may already be in flight)
+  if (grp < ntiles && !(pf && grp == 0)) stage(jt, uni(grp));
+  if (!pf) load_q(qrow0);
 
   f32x16 o[ND];
 #pragma unroll
@@ -1412,8 +1417,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
     constexpr int RD = (DO_PV ? 2 : 0) + (DO_QK ? 1 : 0);   // LDS reads per step
     constexpr int MF = (DO_PV ? 1 : 0) + (DO_QK ? 1 : 0);   // MFMAs per step
     constexpr int LEAD = 2;
-    const unsigned char* Kb = buf + (st & 3) * SLOT;
-    const unsigned char* Vb = buf + ((st + 2) & 3) * SLOT + KSLOT;   // slot of tile st-2
+    const unsigned char* Kb = buf + ((st + 3) & 3) * SLOT;
+    const unsigned char* Vb = buf + ((st + 1) & 3) * SLOT + KSLOT;   // slot of tile st-2
     u32x4 va[NMF], ka[NMF];
     auto read = [&](int t) {
       if constexpr (DO_PV) {
@@ -1521,14 +1526,32 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
       else if (pv) mfma_phase(std::true_type{}, std::false_type{}, st);
     } else if (stv >= 1 && stv - 1 < ntiles) {
       const int meta = jt[st - 1].y;
-      if (stv + 1 < ntiles) stage(st + 1);
+      if (stv + 1 < ntiles) stage(jt, st + 1);
       softmax(meta);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);   // tile st+1 has landed
     }
     wg_barrier();
   }
 
-  __syncthreads();
+  // ---- the next job's first tile (group 0, into slot 3) and query operands, in flight during
+  // this epilogue (which uses LDS below slot 3 only)
+  pf = 0;
+  {
+    int vs2 = vstart;
+    for (int oi2 = oi + 1; oi2 < p.nseg; ++oi2) {
+      const int v2 = sp.order(oi2), nv2 = sp.view_tiles(v2);
+      const int ja2 = max(c0, vs2) - vs2, jb2 = min(c1, vs2 + nv2) - vs2;
+      vs2 += nv2;
+      if (ja2 >= jb2) continue;
+      if (grp == 0) stage(tiles + (stt.offset(p.seg0 + v2) + ja2), 0);
+      load_q(stt.qrow0(p, p.seg0 + v2));
+      pf = 1;
+      break;
+    }
+  }
+  static_assert(MBYTES <= 3 * SLOT, "the epilogue leaves slot 3 free");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  wg_barrier();
   // ---- merge the two groups (same rows, disjoint key tiles), then O / l
   const float m_eff = fresh ? -INFINITY : m_ref;
   const float l_half = xhalf_sum(l_run);
@@ -1545,7 +1568,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
         *reinterpret_cast<f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h) =
             f32x4{o[d][4 * ig], o[d][4 * ig + 1], o[d][4 * ig + 2], o[d][4 * ig + 3]};
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS only: the prefetched loads stay in flight
+  wg_barrier();
   const bool whole = ja == 0 && jb == nv;
   if (grp == 0) {   // combined rows, in place in LDS (normalised if the job covers the view)
     const float m1 = red_m[wr][l32], l1 = red_l[wr][l32];
@@ -1570,7 +1594,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
       red_l[wr][l32] = lsum;
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS only: the prefetched loads stay in flight
+  wg_barrier();
   // ---- rows out, 16 bytes per lane and whole rows per group of lanes.  Row r of the block
   // is token tok0 + 32*((r/32)/HPW) + r%32 of query head kvh*G + hsub*HPW + (r/32)%HPW.
   const float* rows = reinterpret_cast<const float*>(buf);
