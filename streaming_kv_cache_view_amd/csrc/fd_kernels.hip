@@ -2095,18 +2095,18 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   constexpr int RPL = 1024 / ROWB;               // rows per 1 KB direct load
   constexpr int BLKB = 32 * ROWB;                // 32 rows of K, V or Q
   constexpr int NIB = BLKB / 1024;               // direct loads per 32 rows
-  constexpr int NQW = (NIB + NW - 1) / NW;       // query loads per wave (at most)
+  constexpr int QR = 7;                          // row blocks whose queries are resident at once
   constexpr int KPR = 16 / KCH;                  // rows per 256-byte bank row
   constexpr int PBYTES = NB * 2 * 1024 > H2 * 32 * 8 ? NB * 2 * 1024 : H2 * 32 * 8;   // P^T operands;
                                                  // first the angle table
-  static_assert(NB == NW && NS <= NW && NQW <= 2, "work split");
+  static_assert(NB == NW && NS <= NW, "work split");
   auto kswz = [](uint32_t r) { return (r / KPR) & (KCH - 1); };
   auto vswz = [](uint32_t key) { return 4 * ((key / KPR) & (KCH / 4 - 1)); };
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
 
   __shared__ __attribute__((aligned(16))) unsigned char ktile[NB * BLKB];
   __shared__ __attribute__((aligned(16))) unsigned char vtile[NB * BLKB];
-  __shared__ __attribute__((aligned(16))) unsigned char qbuf[BLKB];
+  __shared__ __attribute__((aligned(16))) unsigned char qbuf[QR * BLKB];
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[PBYTES];       // first: the angle table
   __shared__ double frev[H2];                    // theta^(-2i/D) / (2 pi): revolutions per position
   __shared__ float2 cbase[NB][H2];               // (cos, sin) of each block's first position
@@ -2138,21 +2138,19 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   const int x0 = uni(bk.x0), klen = uni(bk.len), tailb = uni(bk.tailbase);
   const bool rot = !VIEW || x0 >= p.W;
 
-  // ---- queries of a row block into qbuf: wave w loads KB i = w, w + NW, ... of the 32 rows, row
-  // r at LDS row r with 16-byte chunk c at position c ^ kswz(r); rows past G*B read any valid row
+  // ---- queries of row blocks rb0 .. rb0 + nr - 1 into qbuf (row block j at qbuf + j*BLKB):
+  // the nr*NIB 1 KB loads go round-robin to the waves; row r of a block at LDS row r with
+  // 16-byte chunk c at position c ^ kswz(r); rows past G*B read any valid row (zeroed later)
   const uint32_t lq = lds_addr(qbuf);
-  auto load_q = [&](int rb) {
-    const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
-#pragma unroll
-    for (int i0 = 0; i0 < NQW; ++i0) {
-      const int i = w + NW * i0;
-      if (i < NIB) {
-        const int r = RPL * i + lane / KCH, pc = lane % KCH;
-        const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B;
-        const int hq = hh2 < p.G ? hh2 : 0, b2 = hh2 < p.G ? qr2 % p.B : 0;
-        const bf16* src = qb + (static_cast<int64_t>(d * p.B + b2) * p.Hq + kvh * p.G + hq) * D;
-        g2lds16_va(src + 8 * (pc ^ kswz(r)), uni(lq + i * 1024));
-      }
+  auto load_q = [&](int rb0, int nr) {
+    for (int L = w; L < nr * NIB; L += NW) {
+      const int rb = rb0 + L / NIB, i = L % NIB;
+      const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
+      const int r = RPL * i + lane / KCH, pc = lane % KCH;
+      const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B;
+      const int hq = hh2 < p.G ? hh2 : 0, b2 = hh2 < p.G ? qr2 % p.B : 0;
+      const bf16* src = qb + (static_cast<int64_t>(d * p.B + b2) * p.Hq + kvh * p.G + hq) * D;
+      g2lds16_va(src + 8 * (pc ^ kswz(r)), uni(lq + L * 1024));
     }
   };
   // ---- K or V of this wave's block.  A whole block of contiguous cache (or view) rows takes one
@@ -2190,11 +2188,11 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
     }
   };
 
-  // ---- the first row block's queries and this wave's K in flight (V once the tables are built
+  // ---- the first row blocks' queries and this wave's K in flight (V once the tables are built
   // and the queries rotated: issuing it here would stall that work behind a full load queue)
-  load_q(rb_lo);
+  const int nr0 = min(QR, rb_hi - rb_lo);
+  load_q(rb_lo, nr0);
   if (klen > 0) load_kv(false);
-  const int nq = (w < NIB ? 1 : 0) + (w + NW < NIB ? 1 : 0);   // this wave's query loads
 
   // ---- rotation tables while K lands: frequencies (fp64), then (cos, sin)(r f_i) for the 32
   // offsets (fp32 revolutions r f_i, hardware sin / cos) and the fraction of each block's base
@@ -2210,20 +2208,22 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   }
   if (rot && klen > 0 && lane < H2) cbase[w][lane] = cs_rev(static_cast<double>(bk.pos0) * frev[lane]);
 
-  // ---- queries of a row block, rotated in place in LDS (fp16, scaled into log2 units; rows past
-  // G*B zero): thread (row, quarter of the RoPE pairs), four pairs each
-  auto rotate_q = [&](int rb) {
-    constexpr int QT = 32 * (H2 / 4);   // work items
+  // ---- queries of row blocks rb0 .. rb0 + nr - 1, rotated in place in LDS (fp16, scaled into
+  // log2 units; rows past G*B zero): item (row block, row, quarter of the RoPE pairs)
+  auto rotate_q = [&](int rb0, int nr) {
+    constexpr int QT = 32 * (H2 / 4);   // items per row block
     static_assert(H2 % 4 == 0, "query rotation split");
-    for (int it = tid; it < QT; it += NT) {
+    for (int it2 = tid; it2 < nr * QT; it2 += NT) {
+      const int j = it2 / QT, it = it2 - j * QT, rb = rb0 + j;
+      unsigned char* const qb0 = qbuf + j * BLKB;
       const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
       const int r = it / (H2 / 4), i0 = 4 * (it % (H2 / 4));   // pairs (i, i + D/2), i in [i0, i0 + 4)
       const int qr2 = 32 * rbl + r, hh2 = qr2 / p.B, b2 = qr2 % p.B;
       const float qs = hh2 < p.G ? p.sm_scale_log2 : 0.f;
       const double qpos = static_cast<double>(p.pos_base + p.W + p.n_tails[d] + b2);
       // 8-byte halves of the 16-byte chunks holding elements i0 and i0 + D/2
-      unsigned char* c1 = qbuf + r * ROWB + (((i0 / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
-      unsigned char* c2 = qbuf + r * ROWB + ((((i0 + H2) / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
+      unsigned char* c1 = qb0 + r * ROWB + (((i0 / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
+      unsigned char* c2 = qb0 + r * ROWB + ((((i0 + H2) / E) ^ kswz(r)) << 4) + 2 * (i0 % E);
       const u32x2 a2 = *reinterpret_cast<const u32x2*>(c1), b2v = *reinterpret_cast<const u32x2*>(c2);
       float x1[4], x2[4];
 #pragma unroll
@@ -2249,7 +2249,7 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   else __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   wg_barrier();   // every query share, the angle table and the base angles visible
-  rotate_q(rb_lo);
+  rotate_q(rb_lo, nr0);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   wg_barrier();   // the rotated queries visible
   if (klen > 0) load_kv(true);
@@ -2290,13 +2290,25 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
     return key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
   }();
   const size_t pw = verify_partial_words(D);
-  for (int rb = rb_lo; rb < rb_hi; ++rb) {
+  for (int rc = rb_lo; rc < rb_hi; rc += QR) {
+  const int nr = min(QR, rb_hi - rc);
+  if (rc > rb_lo) {   // the next row blocks' queries, once every wave is done with qbuf
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();
+    load_q(rc, nr);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    wg_barrier();
+    rotate_q(rc, nr);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();
+  }
+  for (int rb = rc; rb < rc + nr; ++rb) {
     const int d = rb / p.nrb_d, rbl = rb - d * p.nrb_d;
     const int bq = (32 * rbl + l32) % p.B;                        // this lane's query block token
     const int tb = tail_unit ? tailb : p.W + d * p.tail_stride + p.n_tails[d];   // draft d's block rows
     u32x4 qf[NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) qf[u] = ld16(qbuf + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
+    for (int u = 0; u < NU; ++u) qf[u] = ld16(qbuf + (rb - rc) * BLKB + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
     f32x16 sv = f32x16{};
     float mx = -INFINITY;
     if (klen > 0) {
@@ -2335,13 +2347,7 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
     }
     lsum = xhalf_sum(lsum);
     if (lane < 32) red_l[w][l32] = lsum;
-    const bool more = rb + 1 < rb_hi;
-    if (more) load_q(rb + 1);   // qbuf is free: every wave read it before the barrier above
-    if (rb == rb_lo) {          // this wave's V has landed
-      if (more && nq == 2) __builtin_amdgcn_s_waitcnt(wait_vm(2));
-      else if (more && nq == 1) __builtin_amdgcn_s_waitcnt(wait_vm(1));
-      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
+    if (rb == rb_lo) __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's V has landed
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     wg_barrier();   // P, row sums and every V tile visible
 
@@ -2385,15 +2391,8 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
         dst[32 * D + 32 + l32] = L;
       }
     }
-    if (more) {   // the next row block's queries: landed (this wave's share), visible, rotated
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      wg_barrier();
-      rotate_q(rb + 1);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      wg_barrier();
-    }
   }
+  }   // row-block chunks
 }
 
 // Verify merge: fixed-order log-sum-exp combination of the n_split partials of each kv head.

@@ -369,6 +369,15 @@ def test_verify_batched_block16_and_bf16_out():
     check_verify_batched(w, 5, w.first_t, [60, 90, 0], 100, 8, None, out_dtype="bf16")
 
 
+def test_verify_batched_more_row_blocks_than_resident():
+    """Ten row blocks (five 16-token drafts, two 32-row blocks each): more than the kernel keeps
+    resident at once, so a window unit reloads queries between its row blocks."""
+    w = synth.CONFIGS[2]
+    w2 = Workload(w.cfg_id, w.name, w.geom.replace(tail_cap=192), scale=w.scale, first_t=w.first_t)
+    check_verify_batched(w2, 0, w.first_t + 1, [20, 3, 17, 0, 9], 40, 16, None)
+    check_verify_batched(w2, 1, w.first_t + 2, [12, 3, 10, 0, 9, 1, 5, 2], 22, 8, "rotate")
+
+
 def test_verify_repeat_bit_identical():
     """Consecutive calls on one workspace (its partial slots reused) give bit-identical outputs:
     single-draft config 4 and a three-draft call with a view."""
