@@ -187,8 +187,9 @@ def cpu_baseline(seconds: float = 24.0):
 
 
 def rolling_windows(g, n_windows, gen, host_ahead):
-    """Times n_windows consecutive windows of one layer (insert + streaming-prefill attention,
-    each call bracketed by its own events, back to back behind a queued GPU spin)."""
+    """Times n_windows consecutive windows of one layer: per window the fused insert + streaming
+    attention call (fd_stream_attn_insert), back to back behind a queued GPU spin, HIP events
+    around the sweep; and the same sweep of the attention call alone over the same windows."""
     import torch
     from streaming_kv_cache_view_amd import fd
     dev = "cuda"
@@ -202,35 +203,37 @@ def rolling_windows(g, n_windows, gen, host_ahead):
     out = torch.empty(g.n_new, g.n_q_heads, g.head_dim, device=dev)
     sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=dev)
     t0 = g.n_frames   # frames 0 .. F-1 are in the cache
-    ins_ms, att_ms = [], []
-    for rep_i in range(2):   # the first sweep is a warm-up
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_windows + 1)]
+
+    def sweep(fused):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         host_ahead()
-        ev[0].record()
+        e0.record()
         for w in range(n_windows):
             t = t0 + w
-            fd.kv_insert_frame(g, kc, vc, kn[w % n_in], vn[w % n_in], t)
-            ev[2 * w + 1].record()
-            fd.stream_attn(g, qn[w % n_in], kc, vc, t, out, sws)
-            ev[2 * w + 2].record()
+            if fused:
+                fd.stream_attn_insert(g, kn[w % n_in], vn[w % n_in], qn[w % n_in], kc, vc, t, out, sws)
+            else:
+                fd.stream_attn(g, qn[w % n_in], kc, vc, t, out, sws)
+        e1.record()
         torch.cuda.synchronize()
-        if rep_i > 0:
-            ins_ms = [ev[2 * w].elapsed_time(ev[2 * w + 1]) for w in range(n_windows)]
-            att_ms = [ev[2 * w + 1].elapsed_time(ev[2 * w + 2]) for w in range(n_windows)]
+        return e0.elapsed_time(e1) / n_windows * 1e3
+
+    sweep(True)   # warm-up
+    fused_us = min(sweep(True) for _ in range(2))
+    att_us = min(sweep(False) for _ in range(2))
     flops = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
-    att_us = sum(att_ms) / len(att_ms) * 1e3
     tf = flops / (att_us * 1e-6) / 1e12
     return {
         "windows": n_windows,
         "stream_us_per_window": round(att_us, 2),
-        "stream_us_median": round(sorted(att_ms)[len(att_ms) // 2] * 1e3, 2),
-        "stream_us_min": round(min(att_ms) * 1e3, 2),
-        "insert_us_per_window": round(sum(ins_ms) / len(ins_ms) * 1e3, 2),
+        "stream_insert_us_per_window": round(fused_us, 2),
         "gflop_per_window": round(flops / 1e9, 2),
         "achieved_tflops": round(tf, 2),
         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
         "note": "100 rolling windows of one layer at 8,704 keys (V=4, F=8, T=256, P=512, 32/8 heads, D=128); "
-                "inserts timed separately; timing inputs N(0,1) bf16",
+                "fd_stream_attn per window (the attention alone, rate and frac) and fd_stream_attn_insert "
+                "(the window step with its insert); HIP events around each 100-window sweep; timing inputs "
+                "N(0,1) bf16",
     }
 
 
@@ -292,25 +295,13 @@ def main():
         pair brackets one call's kernels, not the host's time to issue the next call."""
         torch.cuda._sleep(12_000_000)
 
-    def step(ev=None):
-        """One window: per layer the insert of the new frames, the streaming-prefill call and the
-        verify.  The timed step uses the fused insert + attention entry point; the per-call pass
-        (ev given) times the three calls one by one."""
+    def step():
+        """One window: per layer the new frames' insert fused with the streaming-prefill call, then
+        the verify."""
         t = frame[0]
         for l in range(L):
-            if ev is None:
-                fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t, out[l], sws)
-                fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
-                continue
-            ev[0][l].record()
-            fd.kv_insert_frame(g, kc[l], vc[l], kn[l], vn[l], t)
-            ev[1][l].record()
-            fd.stream_attn(g, qn[l], kc[l], vc[l], t, out[l], sws)
-            ev[2][l].record()
-            fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
-            ev[3][l].record()
             fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t, out[l], sws)
-            ev[4][l].record()
+            fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
         frame[0] += 1
 
     for _ in range(args.warmup):
@@ -327,18 +318,30 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # per-call timing (events on the stream the kernels are launched on)
-    ins_ms, att_ms, ver_ms, si_ms = [], [], [], []
-    for _ in range(max(1, args.steps // 2)):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L)] for _ in range(5)]
-        host_ahead()
-        step(ev)
-        torch.cuda.synchronize()
-        for l in range(L):
-            ins_ms.append(ev[0][l].elapsed_time(ev[1][l]))
-            att_ms.append(ev[1][l].elapsed_time(ev[2][l]))
-            ver_ms.append(ev[2][l].elapsed_time(ev[3][l]))
-            si_ms.append(ev[3][l].elapsed_time(ev[4][l]))
+    # per-call timing: each call type swept over the layers back to back behind a queued GPU spin,
+    # two HIP events (on the stream the kernels are launched on) around each sweep, so a figure is
+    # the average time per call with its launch gaps but no event packets between calls
+    def sweep(call, reps):
+        ms = []
+        for rep_i in range(1 + reps):   # the first sweep is a warm-up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            host_ahead()
+            e0.record()
+            for l in range(L):
+                call(l)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep_i > 0:
+                ms.append(e0.elapsed_time(e1) / L)
+        return ms
+
+    t_pc = frame[0]
+    reps = max(2, args.steps // 4)
+    ins_ms = sweep(lambda l: fd.kv_insert_frame(g, kc[l], vc[l], kn[l], vn[l], t_pc), reps)
+    att_ms = sweep(lambda l: fd.stream_attn(g, qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
+    ver_ms = sweep(lambda l: fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t_pc, n_tail, blk, vout[l], ws),
+                   reps)
+    si_ms = sweep(lambda l: fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
     mean = lambda a: sum(a) / len(a)
     med = lambda a: sorted(a)[len(a) // 2]
     att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
@@ -355,18 +358,9 @@ def main():
         vout16 = [torch.empty(b16, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
         ws16 = torch.empty(fd.verify_workspace_bytes(g, b16), dtype=torch.uint8, device=dev)
         t16 = frame[0]
-        v16_ms = []
-        for rep_i in range(1 + max(1, args.steps // 4)):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
-            host_ahead()
-            ev[0].record()
-            for l in range(L):
-                fd.verify_attn(g, qb16[l], kb16[l], vb16[l], kc[l], vc[l], t16, n_tail, b16, vout16[l], ws16)
-                ev[l + 1].record()
-            torch.cuda.synchronize()
-            if rep_i > 0:   # the first sweep is a warm-up
-                v16_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
-        v16_us = sum(v16_ms) / len(v16_ms) * 1e3
+        v16_ms = sweep(lambda l: fd.verify_attn(g, qb16[l], kb16[l], vb16[l], kc[l], vc[l], t16, n_tail, b16,
+                                                vout16[l], ws16), reps)
+        v16_us = mean(v16_ms) * 1e3
 
         # batched verify: S independent 8-token drafts with their own reasoning tails over one
         # window in one call, with and without the rotated window a streaming call leaves in its
@@ -388,19 +382,10 @@ def main():
             nbytes = ((g.window + sum(tails) + S * blk) * g.n_kv_heads * g.head_dim * esz_in * 2
                       + S * blk * g.n_q_heads * g.head_dim * (esz_in + 4))
             for use_view in (False, True):
-                b_ms = []
-                for rep_i in range(1 + max(1, args.steps // 4)):
-                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
-                    host_ahead()
-                    ev[0].record()
-                    for l in range(L):
-                        fd.verify_attn_batched(gb, qs[l], ks[l], vs[l], kcb[l], vcb[l], t16, tails, n_tail + blk,
-                                               blk, ob, wsb, k_view=kview[l] if use_view else None)
-                        ev[l + 1].record()
-                    torch.cuda.synchronize()
-                    if rep_i > 0:
-                        b_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
-                us = sum(b_ms) / len(b_ms) * 1e3
+                b_ms = sweep(lambda l: fd.verify_attn_batched(gb, qs[l], ks[l], vs[l], kcb[l], vcb[l], t16, tails,
+                                                              n_tail + blk, blk, ob, wsb,
+                                                              k_view=kview[l] if use_view else None), reps)
+                us = mean(b_ms) * 1e3
                 gbs = nbytes / (us * 1e-6) / 1e9
                 batched[f"S{S}{'_view' if use_view else ''}"] = {
                     "us_per_call": round(us, 2), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -413,18 +398,8 @@ def main():
         pws = torch.empty(fd.prefill_workspace_bytes(g), dtype=torch.uint8, device=dev)
         qw = [rnd(g.window, g.n_q_heads, g.head_dim) for _ in range(L)]
         ow = [torch.empty(g.window, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
-        pf_ms = []
-        for rep_i in range(2):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
-            host_ahead()
-            ev[0].record()
-            for l in range(L):
-                fd.prefill_attn(g, qw[l], kc[l], vc[l], t16, ow[l], pws)
-                ev[l + 1].record()
-            torch.cuda.synchronize()
-            if rep_i > 0:
-                pf_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
-        prefill_us = sum(pf_ms) / len(pf_ms) * 1e3
+        pf_ms = sweep(lambda l: fd.prefill_attn(g, qw[l], kc[l], vc[l], t16, ow[l], pws), 1)
+        prefill_us = mean(pf_ms) * 1e3
         del qw, ow, pws
 
         # K/V projection of the new frames with the ring-slot insert as its epilogue
@@ -432,18 +407,8 @@ def main():
         xs = [rnd(g.n_new, hidden) for _ in range(L)]
         wkv = [(torch.randn(2 * g.n_kv_heads * g.head_dim, hidden, generator=gen, device=dev)
                 / hidden ** 0.5).to(torch.bfloat16) for _ in range(L)]
-        kp_ms = []
-        for rep_i in range(2):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
-            host_ahead()
-            ev[0].record()
-            for l in range(L):
-                fd.kv_project_insert(g, xs[l], wkv[l], kc[l], vc[l], t16)
-                ev[l + 1].record()
-            torch.cuda.synchronize()
-            if rep_i > 0:
-                kp_ms += [ev[l].elapsed_time(ev[l + 1]) for l in range(L)]
-        kvproj_us = sum(kp_ms) / len(kp_ms) * 1e3
+        kp_ms = sweep(lambda l: fd.kv_project_insert(g, xs[l], wkv[l], kc[l], vc[l], t16), 1)
+        kvproj_us = mean(kp_ms) * 1e3
         kvproj_flops = 2 * g.n_new * (2 * g.n_kv_heads * g.head_dim) * hidden
         del xs, wkv
 
@@ -542,7 +507,7 @@ def main():
             "traffic": committed_traffic("stream_attn_config3_traffic.md"),
         },
         "roofline_verify": {
-            "kernel": "fd_verify_attn (verify_dma_kernel + verify_merge_kernel)",
+            "kernel": "fd_verify_attn (verify_dma_kernel + verify_merge_dma_kernel)",
             "bound": "hbm",
             "achieved": round(ver_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -556,6 +521,7 @@ def main():
                                (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
         "per_call_us_min": {k: round(min(x) * 1e3, 2) for k, x in
                             (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
+        "per_call_note": "each call type swept over the 36 layers back to back; HIP events around each sweep",
         "verify_graph": None if vgraph_us is None else {
             "us_per_call": round(vgraph_us, 2),
             "gbs": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9, 1),
