@@ -96,7 +96,9 @@ constexpr size_t kVerifyWsHeader = 256;
 // view cut between chunks leaves one (m, l, O) partial per piece, merged by a second kernel;
 // the workspace holds, after the rotated keys and queries, two partial slots per (row block,
 // chunk): a chunk's first job may continue a view, its last may be continued.
-constexpr size_t stream_partial_words(int D) { return (size_t)128 * D + 256; }   // O[128][D], (m, l)[128]
+// A slot: O[128][D] in fp16 (each row scaled by a power of two), then (m, l, 1/scale, 0) in
+// fp32 per row.
+constexpr size_t stream_partial_words(int D) { return (size_t)64 * D + 512; }
 // rotated, scaled queries (fp16, [rows][Hq][D]) after the rotated keys: rows = V*T (streaming)
 // or W (full window)
 inline size_t stream_qrot_bytes(int rows, int Hq, int D) { return align256(size_t(rows) * Hq * D * 2); }

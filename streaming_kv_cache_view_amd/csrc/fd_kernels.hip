@@ -1155,28 +1155,48 @@ struct StreamSplit {
 };
 
 // Slot of the partial of a job of view v in chunk c: two per (row block, chunk), 0 for the
-// chunk's first job (which starts at bnd(c)), 1 for its last.
+// chunk's first job (which starts at bnd(c)), 1 for its last.  A slot holds the piece's
+// unnormalised O[128][D] in fp16, each row multiplied by a power of two 2^s that brings its
+// largest magnitude into [2^14, 2^15) (so no row overflows or leaves the normal range, and
+// each value keeps fp16's 11 significant bits), then per row the fp32 (row max m, row sum l,
+// 2^-s, 0).
 template <int D>
 __device__ inline float* stream_slot(float* part, const KParams& p, int rbi, int c, int which) {
   return part + (static_cast<int64_t>(rbi * p.nseg + c) * 2 + which) * stream_partial_words(D);
 }
+// 2^e as a float, for integer e in [-126, 127]
+__device__ inline float exp2_int(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+// Exponent s of a partial row's scale: |x| < 2^(E+1) for the row's largest magnitude
+// mx = 1.f * 2^E, so 2^(14 - E) maps it into [2^14, 2^15); clamped so 2^s and 2^-s are normal
+// floats (mx = 0 or subnormal takes the largest scale).
+__device__ inline int partial_row_scale(float mx) {
+  const int e_bits = static_cast<int>((__float_as_uint(mx) >> 23) & 0xff);
+  return min(max(141 - e_bits, -126), 126);
+}
 
-// Merge of the segments (views) whose tiles were split between chunks: two workgroups per
-// (row block, segment), 64 rows each; segments held whole by one chunk were written by the
-// attention kernel.
-// For the pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
+// Merge of the segments (views) whose tiles were split between chunks.  Chunk boundary c
+// (between chunks c - 1 and c, c = 1..V-1) cuts at most one view; the workgroups of boundary
+// c merge that view if c is the first boundary inside it (a view longer than a chunk is cut
+// by several).  For its pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
 // sum_i 2^(m_i - M) l_i with M = max_i m_i (the online-softmax merge of disjoint key sets),
-// taken in batches of up to 4 pieces whose loads are all in flight together.  A slot holds
-// O[128][D], then (m, l) pairs per row.  Thread tid takes row tid/8 of its half and an
-// eighth of the columns.
+// taken in batches of up to 4 pieces whose loads are all in flight together; piece i's O_i
+// is its stored fp16 row times its 2^-s.  Segments held whole by one chunk were written by
+// the attention kernel.
+// Workgroup = 256 threads over kMergeItems / (HPW*D/4) tokens of one row block, all HPW
+// heads; D/16 workgroups cover the row block's tokens.  Item e (thread tid takes e = tid and
+// tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4)) .. +3: a
+// token's heads are adjacent rows of the output, so each store instruction of a wave writes
+// 1 KB (fp32) of contiguous output, and the many small workgroups spread the writes over
+// the whole output at once (the same bytes written as 16-byte pieces of a 16 KB-strided
+// pattern by 512-thread workgroups took ~1.8x as long).
+constexpr int kMergeItems = 512;   // 4-column items per merge workgroup
 template <int D>
-__global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
+__global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
                                                            void* __restrict__ out) {
-  constexpr int DQ = D / 8, MAXP = 4;
-  // blockIdx.x = ((half*nseg + v)*(n_hsub*nqb) + hsub*nqb + qb)*Hkv + kvh: like the attention
-  // kernel's, consecutive workgroups go round-robin to the XCDs with the kv head fastest, so
-  // (for Hkv a multiple of 8) a row block's partials are merged on the XCD whose L2 they were
-  // written through
+  constexpr int CG = D / 4, NSUB = D / 16, MAXP = 4, IPT = kMergeItems / 256;
+  // blockIdx.x = ((((c - 1)*NSUB + sub)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head
+  // fastest, as in the attention kernel, so (for Hkv a multiple of 8) a row block's partials
+  // are merged on the XCD whose L2 they were written through
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
@@ -1184,61 +1204,91 @@ __global__ __launch_bounds__(512) void stream_merge_kernel(const KParams p, cons
   bid /= p.nqb;
   const int hsub = bid % p.n_hsub;
   bid /= p.n_hsub;
-  const int v = bid % p.nseg, half = bid / p.nseg;   // segment p.seg0 + v
-  const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
+  const int sub = bid % NSUB, cb = bid / NSUB + 1;   // boundary between chunks cb - 1 and cb
   const StreamSplit sp(p, qb);
-  const int sv = sp.start(v), nv = sp.view_tiles(v);
-  const int cf = sp.chunk_of(sv), cl = sp.chunk_of(sv + nv - 1);
-  if (cf == cl) return;
-  const int tid = threadIdx.x, row = 64 * half + (tid >> 3), d0 = (tid & 7) * DQ;
-  const int ww = row >> 5;
-  const int tok = qb * 32 * p.TBW + 32 * (ww / p.HPW) + (row & 31);
-  if (tok >= p.qtok) return;
+  const int x = sp.bnd(cb);
+  int v = -1, sv = 0, nv = 0;   // the view holding tile x of the end-to-end order
+  for (int oi = 0, pos = 0; oi < sp.V; ++oi) {
+    const int u = sp.order(oi), n = sp.view_tiles(u);
+    if (x < pos + n) {
+      v = u;
+      sv = pos;
+      nv = n;
+      break;
+    }
+    pos += n;
+  }
+  if (v < 0 || sv == x || sp.chunk_of(sv) != cb - 1) return;
+  const int cf = cb - 1, cl = sp.chunk_of(sv + nv - 1);
   const int which_cf = sv > sp.bnd(cf) ? 1 : 0;
-  float M = -INFINITY, L = 0.f;
-  float acc[DQ];
+  const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
+  const int per_tok = p.HPW * CG, ntok = kMergeItems / per_tok;
+  const int qrow0 = StreamTiles(p).qrow0(p, p.seg0 + v);
+  int row[IPT], col[IPT];
+  int64_t obase[IPT];
+  bool live[IPT];
 #pragma unroll
-  for (int i = 0; i < DQ; ++i) acc[i] = 0.f;
+  for (int k = 0; k < IPT; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    const int tr = sub * ntok + e / per_tok, hl = (e % per_tok) / CG;   // token within the row block, head
+    col[k] = 4 * (e % CG);
+    row[k] = 32 * (hl + p.HPW * (tr >> 5)) + (tr & 31);   // partial row (ww = row/32: token block, head)
+    const int tok = qb * 32 * p.TBW + tr;
+    live[k] = tok < p.qtok;
+    obase[k] = (static_cast<int64_t>(qrow0 + tok) * p.Hq + kvh * p.G + hsub * p.HPW + hl) * D + col[k];
+  }
+  float M[IPT], L[IPT];
+  f32x4 acc[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    M[k] = -INFINITY;
+    L[k] = 0.f;
+    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   for (int c0 = cf; c0 <= cl; c0 += MAXP) {
-    f32x2 ml[MAXP];
-    f32x4 x[MAXP][DQ / 4];
+    f32x4 ml[MAXP][IPT];
+    u32x2 xv[MAXP][IPT];
 #pragma unroll
     for (int j = 0; j < MAXP; ++j) {
       const int c = c0 + j;
-      if (c <= cl) {
-        const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, c, c == cf ? which_cf : 0);
-        ml[j] = *reinterpret_cast<const f32x2*>(sl + 128 * D + 2 * row);
+      const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, min(c, cl), c == cf ? which_cf : 0);
 #pragma unroll
-        for (int i = 0; i < DQ / 4; ++i) x[j][i] = *reinterpret_cast<const f32x4*>(sl + row * D + d0 + 4 * i);
-      } else {
-        ml[j] = f32x2{-INFINITY, 0.f};
+      for (int k = 0; k < IPT; ++k) {
+        if (c <= cl) {
+          ml[j][k] = *reinterpret_cast<const f32x4*>(sl + 64 * D + 4 * row[k]);
+          xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + col[k]);
+        } else {
+          ml[j][k] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
+          xv[j][k] = u32x2{0u, 0u};
+        }
       }
     }
-    float Mn = M;
 #pragma unroll
-    for (int j = 0; j < MAXP; ++j) Mn = fmaxf(Mn, ml[j][0]);
-    const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    L *= r;
+    for (int k = 0; k < IPT; ++k) {
+      float Mn = M[k];
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) acc[i] *= r;
+      for (int j = 0; j < MAXP; ++j) Mn = fmaxf(Mn, ml[j][k][0]);
+      const float r = (M[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
+      L[k] *= r;
+      acc[k] *= r;
 #pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-      if (ml[j][0] == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f(ml[j][0] - Mn);
-      L += wgt * ml[j][1];
-#pragma unroll
-      for (int i = 0; i < DQ / 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * i + e] += wgt * x[j][i][e];
+      for (int j = 0; j < MAXP; ++j) {
+        if (ml[j][k][0] == -INFINITY) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ml[j][k][0] - Mn);
+        L[k] += wgt * ml[j][k][1];
+        const float wo = wgt * ml[j][k][2];
+        const uint32_t lo = xv[j][k][0], hi = xv[j][k][1];
+        acc[k] += wo * f32x4{static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(lo & 0xffff))),
+                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(lo >> 16))),
+                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi & 0xffff))),
+                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi >> 16)))};
+      }
+      M[k] = Mn;
     }
-    M = Mn;
   }
-  const float inv = 1.f / L;
-  const int head = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-  const int64_t obase = (static_cast<int64_t>(StreamTiles(p).qrow0(p, p.seg0 + v) + tok) * p.Hq + head) * D + d0;
 #pragma unroll
-  for (int i = 0; i < DQ; i += 4)
-    store_out4(out, p.out_bf16, obase + i, f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv});
+  for (int k = 0; k < IPT; ++k)
+    if (live[k]) store_out4(out, p.out_bf16, obase[k], acc[k] * (1.f / L[k]));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1618,14 +1668,28 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
         *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + 4 * c) = *reinterpret_cast<const f32x4*>(src + 4 * c);
       }
     }
-  } else {   // this job's piece of view v: unnormalised O, then (row max M, row sum l)
+  } else {   // this job's piece of view v: unnormalised O scaled per row and rounded to fp16,
+             // then (row max M, row sum l, 1 / scale) (stream_slot)
     float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
-    constexpr int TPR = D / 4;
+    constexpr int TPR = D / 8;   // lanes per row (aligned groups within a wave), 8 values each
     for (int r = tid / TPR; r < 128; r += 512 / TPR) {
       const int c = tid % TPR;
-      *reinterpret_cast<f32x4*>(slot + r * D + 4 * c) = *reinterpret_cast<const f32x4*>(rows + r * (D + 4) + 4 * c);
+      const float* src = rows + r * (D + 4) + 8 * c;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const int sc = partial_row_scale(mx);
+      const float mul = exp2_int(sc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x8[e] *= mul;
+      st16(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c, F16Ops::pack(x8));
+      if (c == 0)
+        *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
     }
-    if (tid < 128) *reinterpret_cast<f32x2*>(slot + 128 * D + 2 * tid) = f32x2{red_m[tid >> 5][tid & 31], red_l[tid >> 5][tid & 31]};
   }
   wg_barrier();   // LDS is reused by the next job (this job's output stores drain meanwhile)
   }   // jobs
@@ -2590,7 +2654,8 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-    hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * grid), dim3(512), 0, st, p, part, out);
+    if (p.V > 1)   // a workgroup per (chunk boundary, D/16 token group, row block)
+      hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (D / 16) * (grid / p.V)), dim3(256), 0, st, p, part, out);
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
