@@ -131,7 +131,8 @@ size_t fd_stream_workspace_bytes(const fd_geom* g) {
   const fd::KParams p = make_params(g, g->n_frames - 1);
   const int n_rb = p.Hkv * p.n_hsub * p.nqb;
   return fd::align256(krot) + fd::stream_qrot_bytes(p.V * p.T, p.Hq, p.D) +
-         fd::stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + fd::stream_partial_bytes(n_rb, p.V, p.D);
+         fd::stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + fd::stream_merge_desc_bytes(p.nqb, p.V) +
+         fd::stream_partial_bytes(n_rb, p.V, p.D);
 }
 
 size_t fd_prefill_workspace_bytes(const fd_geom* g) {

@@ -116,6 +116,9 @@ inline size_t stream_tiles_bytes(int qmode, int P, int T, int V, int F) {
   }
   return align256(n * 8);
 }
+// merge descriptors of a streaming call (after the tile table): an int4 per (32*TBW-token
+// block, chunk boundary)
+inline size_t stream_merge_desc_bytes(int nqb, int V) { return align256(size_t(nqb) * (V > 1 ? V - 1 : 0) * 16); }
 inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
   return size_t(n_rb) * nseg * 2 * stream_partial_words(D) * sizeof(float);
 }

@@ -498,12 +498,105 @@ struct NewFrame {
 };
 __host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
 
+// Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
+// HPW heads x TBW 32-token blocks of one kv head and head subset).  The launch covers nseg
+// query segments (StreamTiles; in a streaming call the views); for each the row block has a
+// tile sequence of view_tiles tiles.  They are laid end to end in the order nseg-1, 0,
+// nseg-2, 1, ... (long and short alternate) and the ntot tiles are cut into nseg chunks,
+// chunk c = [bnd(c), bnd(c+1)).  Every segment has at least one tile, so no chunk is empty.
+// With `whole` set (cold start: many more workgroups than CUs) the order is nseg-1, nseg-2,
+// ..., 0 (longest first) and chunk c is exactly the c-th segment of it: the dispatcher hands
+// the longest jobs out first and the rest fill in, with no split and no merge.
+struct StreamSplit {
+  int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf, whole;
+  __device__ StreamSplit(const KParams& p, int qb) {
+    constexpr int TK = kTileKeys;
+    nP = (p.P + TK - 1) / TK;
+    tps = (p.T + TK - 1) / TK;
+    ndiag = (min(p.qtok, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
+    V = p.nseg;   // segments of this launch: the "views" of a row block
+    F = p.F;
+    seg0 = p.seg0;
+    qmode = p.qmode;
+    vf = p.V * p.F;
+    whole = p.whole;
+    ntot = 0;
+    for (int u = 0; u < V; ++u) ntot += view_tiles(u);
+  }
+  // tiles of segment seg0 + u for this row block (StreamTiles: frame (v, j) of a full window
+  // is segment v*F + j, after v*F + j earlier frames)
+  __device__ int view_tiles(int u) const {
+    const int sg = seg0 + u;
+    if (qmode == 0) return nP + (sg * F + F - 1) * tps + ndiag;
+    return sg < vf ? nP + sg * tps + ndiag : ndiag;
+  }
+  __device__ int order(int oi) const {
+    if (whole) return V - 1 - oi;
+    return (oi & 1) ? oi / 2 : V - 1 - oi / 2;
+  }
+  __device__ int bnd(int c) const {
+    if (whole) {
+      int pos = 0;
+      for (int oi = 0; oi < c; ++oi) pos += view_tiles(order(oi));
+      return pos;
+    }
+    // floor(c*ntot / V) by an fp64 division, exact for c*ntot < 2^53: the quotient is rounded
+    // correctly, and a quotient that is not an integer lies at least 1/V below the next one,
+    // far more than its rounding error (a 64-bit integer division is ~10x the instructions)
+    const int64_t a = static_cast<int64_t>(c) * ntot;
+    return a < (int64_t(1) << 53) ? static_cast<int>(static_cast<double>(a) / V) : static_cast<int>(a / V);
+  }
+  // start of view v in the end-to-end order
+  __device__ int start(int v) const {
+    int pos = 0;
+    for (int oi = 0; oi < V; ++oi) {
+      const int u = order(oi);
+      if (u == v) break;
+      pos += view_tiles(u);
+    }
+    return pos;
+  }
+  // the chunk holding tile x of the end-to-end order
+  __device__ int chunk_of(int x) const {
+    int c = 0;
+    for (int i = 1; i < V; ++i)
+      if (bnd(i) <= x) c = i;
+    return c;
+  }
+};
+
+// Merge descriptor of chunk boundary cb (1 <= cb < nseg) of the row blocks of token block qb,
+// written by the rotation pass: the view that boundary cuts first, if cb is the first boundary
+// inside it (a view longer than a chunk is cut by several; a boundary at a view's start cuts
+// none): x = the view (-1: nothing to merge), y = its first and last chunks cf | cl << 16,
+// z = the slot of its piece in chunk cf (1: that chunk's last job, 0: its only job), w = the
+// view's first output row.
+__device__ inline int4 stream_merge_desc(const KParams& p, int qb, int cb) {
+  const StreamSplit sp(p, qb);
+  const int x = sp.bnd(cb);
+  int v = -1, sv = 0, nv = 0;   // the view holding tile x of the end-to-end order
+  for (int oi = 0, pos = 0; oi < sp.V; ++oi) {
+    const int u = sp.order(oi), n = sp.view_tiles(u);
+    if (x < pos + n) {
+      v = u;
+      sv = pos;
+      nv = n;
+      break;
+    }
+    pos += n;
+  }
+  if (v < 0 || sv == x || sp.chunk_of(sv) != cb - 1) return int4{-1, 0, 0, 0};
+  const int cf = cb - 1, cl = sp.chunk_of(sv + nv - 1);
+  return int4{v, cf | (cl << 16), sv > sp.bnd(cf) ? 1 : 0, StreamTiles(p).qrow0(p, p.seg0 + v)};
+}
+
 template <typename T, int D, bool INS>   // INS: the new frames are inserted by this pass (nf)
 __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const T* __restrict__ kc,
                                                           typename Path<T>::QKT* __restrict__ krot,
                                                           int nkb, const T* __restrict__ q,
                                                           typename Path<T>::QKT* __restrict__ qrot,
-                                                          int2* __restrict__ tiles, const NewFrame<T> nf) {
+                                                          int2* __restrict__ tiles, int4* __restrict__ mdesc,
+                                                          const NewFrame<T> nf) {
 #pragma clang fp contract(off)   // every instantiation rounds a rotated row the same way
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
@@ -521,18 +614,24 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   constexpr int CH = H2 / E;       // threads per row (RoPE chunk pairs)
   constexpr int RPW = 256 / CH;     // key rows per workgroup
   const int tid = threadIdx.x;
-  if (tiles && blockIdx.x == 0) {   // the attention kernel's tile table
-    const StreamTiles tt(p);
+  if (tiles && blockIdx.x == 0) {   // workgroup 0 (with a tile table): the bookkeeping only
+    const StreamTiles tt(p);        // the attention kernel's tile table
     for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
       for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
+    if (mdesc) {   // the merge kernel's descriptors, [nqb][nseg - 1]
+      const int nb = p.nseg - 1;
+      for (int e = tid; e < p.nqb * nb; e += 256) mdesc[e] = stream_merge_desc(p, e / nb, e % nb + 1);
+    }
+    return;
   }
-  if (static_cast<int>(blockIdx.x) >= nkb) {   // query rows (token, head kvh*G + hh)
+  const int bx = static_cast<int>(blockIdx.x) - (tiles ? 1 : 0);   // rotation workgroup
+  if (bx >= nkb) {   // query rows (token, head kvh*G + hh)
     // thread (token tl, RoPE chunk pair c) for the workgroup's GH heads of kv head kvh, which
     // share the token's angles; frequencies loaded first, angles computed while the rows fly.
     // Streaming: the newest frames' tokens [V*T]; full window: every window token [W]
-    const int kvh = (blockIdx.x - nkb) % p.Hkv, tl = tid / CH, c = tid % CH;
+    const int kvh = (bx - nkb) % p.Hkv, tl = tid / CH, c = tid % CH;
     const int G = p.G, GH = rope_q_heads(G), NTOK = p.qmode == 0 ? p.V * p.T : p.W;
-    const int qb = (blockIdx.x - nkb) / p.Hkv, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
+    const int qb = (bx - nkb) / p.Hkv, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
     const int tg = tok0 + tl;
     if (tl >= kRopeQTok || tg >= NTOK) return;
     const float sc = p.sm_scale_log2;
@@ -576,7 +675,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   // that share the row's angles; the thread's frequencies are loaded before its rows, so the
   // angles are computed while the rows are in flight
   const int nhg = (p.Hkv + kRopeHeads - 1) / kRopeHeads;
-  const int rb = blockIdx.x / nhg, hg = blockIdx.x % nhg;
+  const int rb = bx / nhg, hg = bx % nhg;
   const int r = tid / CH, c = tid % CH, x = rb * RPW + r;
   const bool live = x < p.W;
   double fr[E];
@@ -1091,68 +1190,6 @@ struct StageMap {
 };
 static_assert(StageMap<128>::check() && StageMap<64>::check(), "whole-tile staging offsets");
 
-// Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
-// HPW heads x TBW 32-token blocks of one kv head and head subset).  The launch covers nseg
-// query segments (StreamTiles; in a streaming call the views); for each the row block has a
-// tile sequence of view_tiles tiles.  They are laid end to end in the order nseg-1, 0,
-// nseg-2, 1, ... (long and short alternate) and the ntot tiles are cut into nseg chunks,
-// chunk c = [bnd(c), bnd(c+1)).  Every segment has at least one tile, so no chunk is empty.
-// With `whole` set (cold start: many more workgroups than CUs) the order is nseg-1, nseg-2,
-// ..., 0 (longest first) and chunk c is exactly the c-th segment of it: the dispatcher hands
-// the longest jobs out first and the rest fill in, with no split and no merge.
-struct StreamSplit {
-  int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf, whole;
-  __device__ StreamSplit(const KParams& p, int qb) {
-    constexpr int TK = kTileKeys;
-    nP = (p.P + TK - 1) / TK;
-    tps = (p.T + TK - 1) / TK;
-    ndiag = (min(p.qtok, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
-    V = p.nseg;   // segments of this launch: the "views" of a row block
-    F = p.F;
-    seg0 = p.seg0;
-    qmode = p.qmode;
-    vf = p.V * p.F;
-    whole = p.whole;
-    ntot = 0;
-    for (int u = 0; u < V; ++u) ntot += view_tiles(u);
-  }
-  // tiles of segment seg0 + u for this row block (StreamTiles: frame (v, j) of a full window
-  // is segment v*F + j, after v*F + j earlier frames)
-  __device__ int view_tiles(int u) const {
-    const int sg = seg0 + u;
-    if (qmode == 0) return nP + (sg * F + F - 1) * tps + ndiag;
-    return sg < vf ? nP + sg * tps + ndiag : ndiag;
-  }
-  __device__ int order(int oi) const {
-    if (whole) return V - 1 - oi;
-    return (oi & 1) ? oi / 2 : V - 1 - oi / 2;
-  }
-  __device__ int bnd(int c) const {
-    if (whole) {
-      int pos = 0;
-      for (int oi = 0; oi < c; ++oi) pos += view_tiles(order(oi));
-      return pos;
-    }
-    return static_cast<int>((static_cast<int64_t>(c) * ntot) / V);
-  }
-  // start of view v in the end-to-end order
-  __device__ int start(int v) const {
-    int pos = 0;
-    for (int oi = 0; oi < V; ++oi) {
-      const int u = order(oi);
-      if (u == v) break;
-      pos += view_tiles(u);
-    }
-    return pos;
-  }
-  // the chunk holding tile x of the end-to-end order
-  __device__ int chunk_of(int x) const {
-    int c = 0;
-    for (int i = 1; i < V; ++i)
-      if (bnd(i) <= x) c = i;
-    return c;
-  }
-};
 
 // Slot of the partial of a job of view v in chunk c: two per (row block, chunk), 0 for the
 // chunk's first job (which starts at bnd(c)), 1 for its last.  A slot holds the piece's
@@ -1177,11 +1214,13 @@ __device__ inline int partial_row_scale(float mx) {
 // Merge of the segments (views) whose tiles were split between chunks.  Chunk boundary c
 // (between chunks c - 1 and c, c = 1..V-1) cuts at most one view; the workgroups of boundary
 // c merge that view if c is the first boundary inside it (a view longer than a chunk is cut
-// by several).  For its pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
+// by several), as the rotation pass's descriptor for (token block, c) records
+// (stream_merge_desc: the split is worked out once per call, not in every workgroup).  For
+// its pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
 // sum_i 2^(m_i - M) l_i with M = max_i m_i (the online-softmax merge of disjoint key sets),
-// taken in batches of up to 4 pieces whose loads are all in flight together; piece i's O_i
-// is its stored fp16 row times its 2^-s.  Segments held whole by one chunk were written by
-// the attention kernel.
+// taken in batches of 2 pieces whose loads are all in flight together; piece i's O_i is its
+// stored fp16 row times its 2^-s.  Segments held whole by one chunk were written by the
+// attention kernel.
 // Workgroup = 256 threads over kMergeItems / (HPW*D/4) tokens of one row block, all HPW
 // heads; D/16 workgroups cover the row block's tokens.  Item e (thread tid takes e = tid and
 // tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4)) .. +3: a
@@ -1191,9 +1230,9 @@ __device__ inline int partial_row_scale(float mx) {
 // pattern by 512-thread workgroups took ~1.8x as long).
 constexpr int kMergeItems = 512;   // 4-column items per merge workgroup
 template <int D>
-__global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const float* __restrict__ part,
-                                                           void* __restrict__ out) {
-  constexpr int CG = D / 4, NSUB = D / 16, MAXP = 4, IPT = kMergeItems / 256;
+__global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const int4* __restrict__ mdesc,
+                                                           const float* __restrict__ part, void* __restrict__ out) {
+  constexpr int CG = D / 4, NSUB = D / 16, MAXP = 2, IPT = kMergeItems / 256;
   // blockIdx.x = ((((c - 1)*NSUB + sub)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head
   // fastest, as in the attention kernel, so (for Hkv a multiple of 8) a row block's partials
   // are merged on the XCD whose L2 they were written through
@@ -1205,25 +1244,11 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
   const int hsub = bid % p.n_hsub;
   bid /= p.n_hsub;
   const int sub = bid % NSUB, cb = bid / NSUB + 1;   // boundary between chunks cb - 1 and cb
-  const StreamSplit sp(p, qb);
-  const int x = sp.bnd(cb);
-  int v = -1, sv = 0, nv = 0;   // the view holding tile x of the end-to-end order
-  for (int oi = 0, pos = 0; oi < sp.V; ++oi) {
-    const int u = sp.order(oi), n = sp.view_tiles(u);
-    if (x < pos + n) {
-      v = u;
-      sv = pos;
-      nv = n;
-      break;
-    }
-    pos += n;
-  }
-  if (v < 0 || sv == x || sp.chunk_of(sv) != cb - 1) return;
-  const int cf = cb - 1, cl = sp.chunk_of(sv + nv - 1);
-  const int which_cf = sv > sp.bnd(cf) ? 1 : 0;
+  const int4 dsc = mdesc[qb * (p.nseg - 1) + cb - 1];   // stream_merge_desc
+  if (dsc.x < 0) return;
+  const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
   const int per_tok = p.HPW * CG, ntok = kMergeItems / per_tok;
-  const int qrow0 = StreamTiles(p).qrow0(p, p.seg0 + v);
   int row[IPT], col[IPT];
   int64_t obase[IPT];
   bool live[IPT];
@@ -1246,23 +1271,25 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
     acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int c0 = cf; c0 <= cl; c0 += MAXP) {
+    // every load of the batch issued back to back: a chunk past cl re-reads cl's slot and its
+    // piece is dropped below (max -inf), so no branch splits the loads
     f32x4 ml[MAXP][IPT];
     u32x2 xv[MAXP][IPT];
 #pragma unroll
     for (int j = 0; j < MAXP; ++j) {
-      const int c = c0 + j;
-      const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, min(c, cl), c == cf ? which_cf : 0);
+      const int c = min(c0 + j, cl);
+      const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, c, c == cf ? which_cf : 0);
 #pragma unroll
       for (int k = 0; k < IPT; ++k) {
-        if (c <= cl) {
-          ml[j][k] = *reinterpret_cast<const f32x4*>(sl + 64 * D + 4 * row[k]);
-          xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + col[k]);
-        } else {
-          ml[j][k] = f32x4{-INFINITY, 0.f, 0.f, 0.f};
-          xv[j][k] = u32x2{0u, 0u};
-        }
+        ml[j][k] = *reinterpret_cast<const f32x4*>(sl + 64 * D + 4 * row[k]);
+        xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + col[k]);
       }
     }
+#pragma unroll
+    for (int j = 1; j < MAXP; ++j)
+      if (c0 + j > cl)
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) ml[j][k][0] = -INFINITY;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       float Mn = M[k];
@@ -1272,9 +1299,8 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
       L[k] *= r;
       acc[k] *= r;
 #pragma unroll
-      for (int j = 0; j < MAXP; ++j) {
-        if (ml[j][k][0] == -INFINITY) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ml[j][k][0] - Mn);
+      for (int j = 0; j < MAXP; ++j) {   // weight 0 for a dropped piece (no branch: the loads stay put)
+        const float wgt = ml[j][k][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j][k][0] - Mn);
         L[k] += wgt * ml[j][k][1];
         const float wo = wgt * ml[j][k][2];
         const uint32_t lo = xv[j][k][0], hi = xv[j][k][1];
@@ -2635,19 +2661,22 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = b16 ? reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D))
                     : nullptr;
+  int4* mdesc = b16 && p.V > 1 ? reinterpret_cast<int4*>(reinterpret_cast<unsigned char*>(tiles) +
+                                                          stream_tiles_bytes(0, p.P, p.T, p.V, p.F))
+                               : nullptr;
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D) +
-                                         stream_tiles_bytes(0, p.P, p.T, p.V, p.F));
+                                         stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + stream_merge_desc_bytes(p.nqb, p.V));
   const int nkb = rope_key_workgroups<T, D>(p);
   const int nqk = b16 ? ceil_div(p.V * p.T, kRopeQTok) * (p.G / rope_q_heads(p.G)) : 0;
   const NewFrame<T> nf{static_cast<const T*>(kn), static_cast<const T*>(vn),
                        kn ? const_cast<T*>(static_cast<const T*>(kc)) : nullptr,
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
   if (kn)
-    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, nf);
+    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, nf);
   else
-    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, nf);
+    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, nf);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
@@ -2655,7 +2684,8 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
     if (p.V > 1)   // a workgroup per (chunk boundary, D/16 token group, row block)
-      hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (D / 16) * (grid / p.V)), dim3(256), 0, st, p, part, out);
+      hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (D / 16) * (grid / p.V)), dim3(256), 0, st, p, mdesc,
+                         part, out);
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
@@ -2676,8 +2706,8 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
   const int nkb = rope_key_workgroups<bf16, D>(p), nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
-  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles,
+  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(1 + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+                     static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles, nullptr,
                      NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr});
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   KParams pf = p;   // the frame segments
@@ -2738,7 +2768,7 @@ int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStr
   const int nkb = rope_key_workgroups<T, D>(p);
   hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb), dim3(256), 0, st, p, static_cast<const T*>(kc),
                      static_cast<typename Path<T>::QKT*>(kview), nkb, static_cast<const T*>(nullptr),
-                     static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr),
+                     static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr), nullptr,
                      NewFrame<T>{nullptr, nullptr, nullptr, nullptr});
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }

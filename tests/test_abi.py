@@ -109,14 +109,15 @@ def test_call_errors():
     # rotated keys (fp16), then for bf16 inputs the rotated, scaled queries (fp16, V*T*Hq*D) and
     # two partial slots (fp16 O[128][D], then fp32 (m, l, 1/scale, 0) per row) per (row block,
     # chunk); a row block is 128 query rows: min(G, 4) heads x (4 / min(G, 4)) 32-token blocks
-    # -> G=2: 2 heads, 64 tokens, one block per kv head; between queries and partials, the attention kernel's tile table
-    # (8 bytes per tile of each view's key sequence: view 0 prefix + 3 frames + diagonal,
-    # view 1 prefix + 7 frames + diagonal)
+    # -> G=2: 2 heads, 64 tokens, one block per kv head; between queries and partials, the
+    # attention kernel's tile table (8 bytes per tile of each view's key sequence: view 0 prefix
+    # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal) and the merge descriptors (16
+    # bytes per token block and chunk boundary: one here)
     krot = g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
     qrot = 2 * 16 * 4 * 64 * 2
     n_rb = g.n_kv_heads * 1 * 1
     align = lambda x: (x + 255) // 256 * 256
-    assert sws == align(krot) + align(qrot) + align((5 + 9) * 8) + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16)
+    assert sws == align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16)
     assert L.fd_stream_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 4
     assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
     assert L.fd_stream_attn(gp, None, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
