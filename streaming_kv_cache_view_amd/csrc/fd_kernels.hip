@@ -2574,7 +2574,7 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
 template <int D>
 __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, const float* __restrict__ part,
                                                                void* __restrict__ out) {
-  constexpr int MAXF = 8;                     // slots folded per thread per pass
+  constexpr int MAXF = 4;                     // slots folded per thread per pass
   constexpr int CPR = D / 4;                  // 4-float chunks per row
   constexpr int SG = 256 / CPR;               // slot groups
   const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;
@@ -2593,34 +2593,33 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   float M = -INFINITY, L = 0.f;
   f32x4 acc = f32x4{};
   for (int s0 = sg; s0 < n_used; s0 += SG * MAXF) {
+    // every load of the batch issued back to back: a slot past n_used re-reads the last one
+    // and is dropped below (max -inf, weight 0), so no branch splits the loads
     float mm[MAXF], ll[MAXF];
     f32x4 ov[MAXF];
 #pragma unroll
     for (int jj = 0; jj < MAXF; ++jj) {
-      const int sl = s0 + jj * SG;
-      mm[jj] = -INFINITY;
-      ll[jj] = 0.f;
-      ov[jj] = f32x4{};
-      if (sl < n_used) {
-        const float* ps = base + sl * pw;
-        mm[jj] = ps[32 * D + q];
-        ll[jj] = ps[32 * D + 32 + q];
-        ov[jj] = *reinterpret_cast<const f32x4*>(ps + ooff);
-      }
+      const float* ps = base + min(s0 + jj * SG, n_used - 1) * pw;
+      mm[jj] = ps[32 * D + q];
+      ll[jj] = ps[32 * D + 32 + q];
+      ov[jj] = *reinterpret_cast<const f32x4*>(ps + ooff);
     }
+    float Mn = M;
 #pragma unroll
     for (int jj = 0; jj < MAXF; ++jj) {
-      if (mm[jj] == -INFINITY) continue;
-      if (mm[jj] > M) {
-        const float f = __builtin_amdgcn_exp2f(M - mm[jj]);
-        acc *= f;
-        L *= f;
-        M = mm[jj];
-      }
-      const float wgt = __builtin_amdgcn_exp2f(mm[jj] - M);
+      if (s0 + jj * SG >= n_used) mm[jj] = -INFINITY;
+      Mn = fmaxf(Mn, mm[jj]);
+    }
+    const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    acc *= r;
+    L *= r;
+#pragma unroll
+    for (int jj = 0; jj < MAXF; ++jj) {
+      const float wgt = mm[jj] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[jj] - Mn);
       acc += wgt * ov[jj];
       L += wgt * ll[jj];
     }
+    M = Mn;
   }
   __shared__ float sM[256], sL[256];
   __shared__ f32x4 sA[256];
