@@ -192,6 +192,40 @@ int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new
                           void* k_cache, void* v_cache, int64_t newest_frame, void* out, void* ws,
                           size_t ws_bytes, void* hip_stream);
 
+/* Streaming-prefill attention with a persistent rotated-key view (Positional Encoding
+ * passage: keys cached pre-RoPE and re-encoded at their shifted positions every window).  The
+ * scores depend on query and key positions only through their difference (rotary encoding:
+ * R(a)^T R(b) = R(b - a)), so rotating every key and query of a window at its position plus one
+ * common offset gives the attention of the shifted positions exactly, up to rounding.  With the
+ * offset (newest_frame mod n) * T (n = max(1, 2^24 / T) frames, fd_view_shift), a frame's keys
+ * keep their rotated value from the call that brings the frame in until the offset wraps:
+ * their position falls by T per window while the offset grows by T.  A call then rotates only
+ * the prefix rows (whose positions do not move) and the new frames, instead of the whole window.
+ *   k_view     : caller-owned [Hkv][N][D] rotated keys (fp16 for bf16 inputs, fp32 for fp32),
+ *                cache-row order, kept per layer across calls; row x holds cache row x rotated
+ *                at fd_key_position(row x) + fd_view_shift(newest_frame).
+ *   view_frame : the newest_frame of the last call that updated this k_view (or -1).  If it is
+ *                newest_frame - 1 or newest_frame and the offset has not wrapped in between,
+ *                only the prefix and the newest slot of every view are rotated into k_view;
+ *                otherwise every window row is.  The caller must not have changed any other
+ *                key row of the window since that call (the library does not check).  Pass
+ *                newest_frame as view_frame to the next call.
+ *   Other arguments, results and errors as for fd_stream_attn (fd_stream_attn_view) and
+ *   fd_stream_attn_insert (fd_stream_attn_insert_view); the workspace's first Hkv*N*D
+ *   elements are not used.  FD_ERR_GEOM if pos_base + fd_view_shift(newest_frame) >= 2^31.
+ *   On return k_view serves fd_verify_attn_batched as its k_view for the same newest_frame
+ *   when the verify's geometry has pos_base raised by fd_view_shift(g, newest_frame) (every
+ *   position moves by the same amount, so the verify's scores are unchanged).           */
+int fd_stream_attn_view(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,
+                        int64_t newest_frame, void* k_view, int64_t view_frame, void* out, void* ws,
+                        size_t ws_bytes, void* hip_stream);
+int fd_stream_attn_insert_view(const fd_geom* g, const void* k_new, const void* v_new, const void* q_new,
+                               void* k_cache, void* v_cache, int64_t newest_frame, void* k_view,
+                               int64_t view_frame, void* out, void* ws, size_t ws_bytes, void* hip_stream);
+/* The common position offset of a persistent key view at newest_frame (above); -1 on invalid
+ * geometry or a negative frame. */
+int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame);
+
 /* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every
  * window row's queries rotated (fp16) and the key-tile table.  0 on invalid geometry or
  * fp32 inputs.  The size depends on the geometry only.                              */

@@ -65,6 +65,39 @@ fd::KParams make_params(const fd_geom* g, int64_t t) {
 
 int esize(const fd_geom* g) { return g->in_dtype == FD_BF16 ? 2 : 4; }
 
+// Persistent key view: frames of the stream are grouped in periods of 2^24 / T frames; at newest
+// frame t the view holds every window row rotated at its position + (t mod period) * T.  A frame
+// row keeps that value from the call that inserted it to the end of the period (its position
+// falls by T per frame while the offset grows by T), so within a period a call rotates only the
+// prefix rows and the new frames; the offset stays below 2^24 positions.
+int64_t view_period(const fd_geom* g) {
+  const int64_t n = (int64_t(1) << 24) / g->tok_per_frame;
+  return n > 1 ? n : 1;
+}
+int64_t view_shift(const fd_geom* g, int64_t t) { return (t % view_period(g)) * g->tok_per_frame; }
+
+// Shared by fd_stream_attn_view and fd_stream_attn_insert_view (k_new, v_new null: no insert).
+int stream_view_call(const fd_geom* g, const void* k_new, const void* v_new, const void* q_new, void* k_cache,
+                     void* v_cache, int64_t t, void* k_view, int64_t view_frame, void* out, void* ws,
+                     size_t ws_bytes, void* hip_stream) {
+  int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (!q_new || !k_cache || !v_cache || !out || !k_view) return FD_ERR_NULL;
+  if (t < g->n_frames - 1) return FD_ERR_FRAME;
+  if (g->pos_base + view_shift(g, t) >= (int64_t(1) << 31)) return FD_ERR_GEOM;
+  if (!ws || ws_bytes < fd_stream_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  if ((k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) || !aligned16(q_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(ws) || !aligned16(k_view))
+    return FD_ERR_ALIGN;
+  fd::KParams p = make_params(g, t);
+  p.pos_base += view_shift(g, t);
+  const int64_t per = view_period(g);
+  p.rot_new = (view_frame >= g->n_frames - 1 && (t == view_frame || t == view_frame + 1) &&
+               t / per == view_frame / per) ? 1 : 0;
+  return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream, k_new, v_new,
+                           k_view);
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +218,26 @@ int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new
   fd::KParams p = make_params(g, newest_frame);
   return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream, k_new,
                            v_new);
+}
+
+int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame) {
+  if (check_geom(g) != FD_OK || newest_frame < 0) return -1;
+  return view_shift(g, newest_frame);
+}
+
+int fd_stream_attn_view(const fd_geom* g, const void* q_new, const void* k_cache, const void* v_cache,
+                        int64_t newest_frame, void* k_view, int64_t view_frame, void* out, void* ws,
+                        size_t ws_bytes, void* hip_stream) {
+  return stream_view_call(g, nullptr, nullptr, q_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                          newest_frame, k_view, view_frame, out, ws, ws_bytes, hip_stream);
+}
+
+int fd_stream_attn_insert_view(const fd_geom* g, const void* k_new, const void* v_new, const void* q_new,
+                               void* k_cache, void* v_cache, int64_t newest_frame, void* k_view,
+                               int64_t view_frame, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (!k_new || !v_new) return FD_ERR_NULL;
+  return stream_view_call(g, k_new, v_new, q_new, k_cache, v_cache, newest_frame, k_view, view_frame, out, ws,
+                          ws_bytes, hip_stream);
 }
 
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {

@@ -42,6 +42,9 @@ struct KParams {
                       // 1: chunk c is segment nseg-1-c whole (no split, no merge)
   // verify.  A call verifies n_drafts draft blocks of B tokens over one window; draft d's
   // reasoning rows and block rows sit in cache rows W + d*tail_stride + [0, n_tails[d] + B).
+  int32_t rot_new;    // rotation pass: 1 -> only the prefix rows and the newest slot of every view
+                      //   (a persistent key view whose older frames were rotated by earlier calls)
+  int32_t pad0;
   int32_t n_tail, B, nblk, n_split;   // n_tail: draft 0's; nblk: key blocks of the longest key list;
                                       // n_split: partial slots per (kv head, row block)
   int32_t n_ws, n_ts;   // bf16 path: units over the window's blocks, and per draft over its tail
@@ -134,8 +137,12 @@ int launch_insert(const KParams& p, int esize, void* kc, void* vc, const void* k
                   int slot, void* stream);
 // kn / vn non-null: the new frames' K and V ([V][T][Hkv][D]) are inserted into ring slot
 // s_new by the same launch sequence (the rotation pass), before the attention reads them
+// kview non-null: the rotated keys go to (and are read from) the caller's persistent view
+// [Hkv][W][D] instead of the workspace; with p.rot_new only the prefix and the newest slot's rows
+// are rotated into it, the older frames' rows being kept from earlier calls
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc,
-                  void* out, void* ws, void* stream, const void* kn = nullptr, const void* vn = nullptr);
+                  void* out, void* ws, void* stream, const void* kn = nullptr, const void* vn = nullptr,
+                  void* kview = nullptr);
 int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                    void* stream);
 int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, const void* w, void* kc, void* vc,

@@ -477,12 +477,21 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
 
 constexpr int kRopeQTok = 32;   // tokens per query workgroup of the rotation pass
 constexpr int kRopeHeads = 4;   // kv heads per key workgroup of the rotation pass (sharing angles)
+// key rows of the rotation pass: every window row, or with rot_new only the prefix and the newest
+// ring slot of every view (rope_row)
+__host__ __device__ inline int rope_rows(const KParams& p) { return p.rot_new ? p.P + p.V * p.T : p.W; }
+// window row of entry i of that list
+__device__ inline int rope_row(const KParams& p, int i) {
+  if (!p.rot_new || i < p.P) return i;
+  const int k = i - p.P, v = k / p.T;
+  return p.P + (v * p.F + p.s_new) * p.T + (k - v * p.T);
+}
 // key workgroups of the rotation pass: RPW = 256 / (D/2 / E) rows (E elements per 16-byte chunk of
 // the input type) times ceil(Hkv / kRopeHeads) head groups
 template <typename T, int D>
 inline int rope_key_workgroups(const KParams& p) {
   constexpr int RPW = 256 / (D / 2 / (16 / static_cast<int>(sizeof(T))));
-  return ceil_div(p.W, RPW) * ceil_div(p.Hkv, kRopeHeads);
+  return ceil_div(rope_rows(p), RPW) * ceil_div(p.Hkv, kRopeHeads);
 }
 
 // The new frames to insert in the same pass (kn == nullptr: none).  Rows of ring slot s_new
@@ -676,15 +685,20 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   // angles are computed while the rows are in flight
   const int nhg = (p.Hkv + kRopeHeads - 1) / kRopeHeads;
   const int rb = bx / nhg, hg = bx % nhg;
-  const int r = tid / CH, c = tid % CH, x = rb * RPW + r;
-  const bool live = x < p.W;
+  const int r = tid / CH, c = tid % CH, xi = rb * RPW + r;
+  const bool live = xi < rope_rows(p);
+  const int x = live ? rope_row(p, xi) : 0;   // window row
   double fr[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) fr[e] = p.inv_freq[E * c + e];
   int64_t nrow = -1;   // INS: the row's index in k_new / v_new ([V*T] rows) if it is a new-frame row
   if (INS && live && x >= p.P) {
-    const int xr = x - p.P, v = xr / (p.F * p.T), sl = (xr / p.T) % p.F, i = xr % p.T;
-    if (sl == p.s_new) nrow = v * p.T + i;
+    if (p.rot_new) {
+      nrow = xi - p.P;   // every listed row past the prefix is in the newest slot
+    } else {
+      const int xr = x - p.P, v = xr / (p.F * p.T), sl = (xr / p.T) % p.F, i = xr % p.T;
+      if (sl == p.s_new) nrow = v * p.T + i;
+    }
   }
   u32x4 raw[kRopeHeads][2], vraw[kRopeHeads][2];
 #pragma unroll
@@ -2651,9 +2665,9 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
 
 template <typename T, int D>
 int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
-                    hipStream_t st, const void* kn, const void* vn) {
+                    hipStream_t st, const void* kn, const void* vn, void* kview) {
   using QKT = typename Path<T>::QKT;
-  QKT* krot = static_cast<QKT*>(ws);
+  QKT* krot = static_cast<QKT*>(kview ? kview : ws);   // the rotated keys: the caller's view, or the workspace
   // bf16 path: rotated, scaled queries, the tile table and the partial slots of split views
   // after the keys
   const bool b16 = std::is_same<T, bf16>::value;
@@ -2822,14 +2836,14 @@ int launch_kv_project(const KParams& p, int hidden, int slot, const void* x, con
 }
 
 int launch_stream(const KParams& p, int in_bf16, const void* q, const void* kc, const void* vc, void* out,
-                  void* ws, void* stream, const void* kn, const void* vn) {
+                  void* ws, void* stream, const void* kn, const void* vn, void* kview) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_bf16) {
-    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, ws, st, kn, vn)
-                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, ws, st, kn, vn);
+    return p.D == 128 ? launch_stream_t<bf16, 128>(p, q, kc, vc, out, ws, st, kn, vn, kview)
+                      : launch_stream_t<bf16, 64>(p, q, kc, vc, out, ws, st, kn, vn, kview);
   }
-  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st, kn, vn)
-                    : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st, kn, vn);
+  return p.D == 128 ? launch_stream_t<float, 128>(p, q, kc, vc, out, ws, st, kn, vn, kview)
+                    : launch_stream_t<float, 64>(p, q, kc, vc, out, ws, st, kn, vn, kview);
 }
 
 int launch_prefill(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,

@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.fd_stream_attn.restype = ctypes.c_int
         L.fd_stream_attn_insert.argtypes = [G, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn_insert.restype = ctypes.c_int
+        L.fd_stream_attn_view.argtypes = [G, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp]
+        L.fd_stream_attn_view.restype = ctypes.c_int
+        L.fd_stream_attn_insert_view.argtypes = [G, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp]
+        L.fd_stream_attn_insert_view.restype = ctypes.c_int
+        L.fd_view_shift.argtypes, L.fd_view_shift.restype = [G, i64], i64
         L.fd_prefill_workspace_bytes.argtypes, L.fd_prefill_workspace_bytes.restype = [G], sz
         L.fd_prefill_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_prefill_attn.restype = ctypes.c_int
@@ -78,7 +83,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
-           "fd_stream_attn", "fd_stream_attn_insert", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
+           "fd_stream_attn", "fd_stream_attn_insert", "fd_stream_attn_view", "fd_stream_attn_insert_view",
+           "fd_view_shift", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
            "fd_verify_attn", "fd_verify_batched_workspace_bytes", "fd_verify_attn_batched", "fd_rotate_window",
            "fd_verify_attn_noalloc", "fd_status_str")
 
@@ -165,6 +171,32 @@ def stream_attn_insert(g, k_new, v_new, q_new, k_cache, v_cache, newest_frame: i
     _check("fd_stream_attn_insert", lib().fd_stream_attn_insert(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(k_new), _ptr(v_new), _ptr(q_new), _ptr(k_cache),
         _ptr(v_cache), int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def stream_attn_view(g, q_new, k_cache, v_cache, newest_frame: int, k_view, view_frame: int, out, ws,
+                     ws_bytes: int | None = None, out_dtype: str = "f32", stream=None):
+    """stream_attn with the rotated keys kept in the caller's persistent k_view [Hkv][N][D]:
+    view_frame is the newest_frame of the last call that updated k_view (-1: none)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("fd_stream_attn_view", lib().fd_stream_attn_view(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(q_new), _ptr(k_cache), _ptr(v_cache), int(newest_frame),
+        _ptr(k_view), int(view_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def stream_attn_insert_view(g, k_new, v_new, q_new, k_cache, v_cache, newest_frame: int, k_view, view_frame: int,
+                            out, ws, ws_bytes: int | None = None, out_dtype: str = "f32", stream=None):
+    """stream_attn_insert with the caller's persistent k_view (as stream_attn_view)."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check("fd_stream_attn_insert_view", lib().fd_stream_attn_insert_view(
+        ctypes.byref(make_geom(g, out_dtype)), _ptr(k_new), _ptr(v_new), _ptr(q_new), _ptr(k_cache), _ptr(v_cache),
+        int(newest_frame), _ptr(k_view), int(view_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def view_shift(g, newest_frame: int) -> int:
+    """The common position offset of a persistent key view at newest_frame."""
+    return int(lib().fd_view_shift(ctypes.byref(make_geom(g)), int(newest_frame)))
 
 
 def prefill_workspace_bytes(g) -> int:

@@ -160,6 +160,41 @@ def test_call_errors():
         assert fd.lib().fd_status_str(code).decode() != "unknown status"
 
 
+def test_stream_view_call_errors_and_shift():
+    """The persistent-view calls: the same checks as fd_stream_attn(_insert) plus the view; the
+    common position offset (newest_frame mod n) * T with n = 2^24 / T frames, and FD_ERR_GEOM when
+    pos_base plus that offset reaches 2^31."""
+    L = fd.lib()
+    g = _g()
+    gp = ctypes.byref(g)
+    sws = L.fd_stream_workspace_bytes(gp)
+    per = (1 << 24) // g.tok_per_frame
+    assert L.fd_view_shift(gp, 0) == 0 and L.fd_view_shift(gp, 5) == 5 * 16
+    assert L.fd_view_shift(gp, per - 1) == (per - 1) * 16 and L.fd_view_shift(gp, per) == 0
+    assert L.fd_view_shift(gp, 3 * per + 7) == 7 * 16
+    assert L.fd_view_shift(gp, -1) == -1 and L.fd_view_shift(None, 5) == -1
+    big_t = _g(n_views=1, n_frames=1, tok_per_frame=1 << 24, prefix_len=0, n_q_heads=1, n_kv_heads=1, tail_cap=0)
+    assert L.fd_view_shift(ctypes.byref(big_t), 9) == 0   # T = 2^24: one frame per period
+    V = L.fd_stream_attn_view
+    assert V(None, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws, None) == -1
+    assert V(gp, FAKE, FAKE, FAKE, 5, None, 4, FAKE, FAKE, sws, None) == -1          # no view
+    assert V(gp, None, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws, None) == -1
+    assert V(gp, FAKE, FAKE, FAKE, 2, FAKE, 1, FAKE, FAKE, sws, None) == -4          # window not full
+    assert V(gp, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws - 1, None) == -7
+    assert V(gp, FAKE, FAKE, FAKE, 5, MISALIGNED, 4, FAKE, FAKE, sws, None) == -5    # misaligned view
+    assert V(gp, FAKE, FAKE, FAKE, 5, FAKE, 4, MISALIGNED, FAKE, sws, None) == -5
+    hi = _g(pos_base=(1 << 31) - 100)
+    assert V(ctypes.byref(hi), FAKE, FAKE, FAKE, 7, FAKE, 6, FAKE, FAKE, sws, None) == -2   # + 7 * 16 >= 2^31
+    S = L.fd_stream_attn_insert_view
+    assert S(gp, None, FAKE, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws, None) == -1  # no k_new
+    assert S(gp, FAKE, None, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws, None) == -1  # no v_new
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 5, None, 4, FAKE, FAKE, sws, None) == -1  # no view
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, 1, FAKE, FAKE, sws, None) == -4
+    assert S(gp, MISALIGNED, FAKE, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws, None) == -5
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 5, MISALIGNED, 4, FAKE, FAKE, sws, None) == -5
+    assert S(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 5, FAKE, 4, FAKE, FAKE, sws - 1, None) == -7
+
+
 def test_verify_noalloc_call_errors():
     """The allocation-free verify: the same argument checks as fd_verify_attn, and a problem
     whose workspace exceeds the static array is refused with FD_ERR_SCRATCH before any HIP call."""

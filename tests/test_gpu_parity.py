@@ -615,6 +615,92 @@ def test_stream_insert_fused_edge_geometries(w):
     check_stream_insert(w, 0, w.first_t + w.geom.n_frames)   # a later ring phase
 
 
+# ---------------------------------------------------------------------------- persistent key view
+def _key_view(g):
+    return torch.empty((g.n_kv_heads, g.window, g.head_dim),
+                       dtype=torch.float16 if g.dtype == synth.BF16 else torch.float32, device=H.DEV)
+
+
+@pytest.mark.parametrize("cid,n_win", [(1, 6), (2, 9), (5, 12)])
+def test_stream_view_rolling(cid, n_win):
+    """fd_stream_attn_insert_view over consecutive windows with the view kept between calls (after
+    the first only the prefix and the new frames are rotated; the ring wraps), every row against the
+    oracle.  Alongside, on a copy of the cache: the frames inserted separately and
+    fd_stream_attn_view, and fd_stream_attn_insert_view rebuilding the whole view every window
+    (view_frame -1).  Positions are integers, so a frame row's rotated value is the same whether
+    it was rotated when the frame came in or again now: all three outputs are bit-identical."""
+    w = synth.CONFIGS[cid]
+    g = w.geom
+    ts = list(range(w.first_t, w.first_t + n_win))
+    want = oracle_outputs(w, 0, ts)
+    kc, vc = H.new_cache(g)
+    H.write_prefix(w, 0, kc, vc)
+    for t in range(ts[0]):
+        H.insert(w, 0, kc, vc, t)
+    kc2, vc2, kc3, vc3 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    views = [_key_view(g) for _ in range(3)]
+    ws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    outs = [torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV) for _ in range(3)]
+    vf = -1
+    for t in ts:
+        H.say(f"  cfg {cid} window t={t} (view of t={vf})")
+        k, v, _ = synth.new_frames(w, 0, t)
+        kn, vn, q = H.dev(k, g), H.dev(v, g), H.q_new(w, 0, t)
+        fd.stream_attn_insert_view(g, kn, vn, q, kc, vc, t, views[0], vf, outs[0], ws)
+        fd.kv_insert_frame(g, kc2, vc2, kn, vn, t)
+        fd.stream_attn_view(g, q, kc2, vc2, t, views[1], vf, outs[1], ws)
+        fd.stream_attn_insert_view(g, kn, vn, q, kc3, vc3, t, views[2], -1, outs[2], ws)
+        vf = t
+        torch.cuda.synchronize()
+        assert torch.equal(kc, kc2) and torch.equal(vc, vc2) and torch.equal(kc, kc3), "cache images differ"
+        assert torch.equal(views[0], views[1]) and torch.equal(views[0], views[2]), "views differ"
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), "outputs differ"
+        err = H.check_out(outs[0].cpu().numpy().astype(np.float64), want[t], g, "f32", ("view", w.name, t))
+        H.say(f"    max-abs vs oracle {err:.3e}")
+
+
+def test_stream_view_offset_wrap():
+    """Around the end of an offset period (n = 2^24 / T frames): the window at n-1 (view of n-2),
+    at n (the offset wraps to 0: the whole view is rebuilt) and at n+1 (view of n), each against
+    the oracle on the window's F frames and bit-identical to a rebuild of the whole view."""
+    w = synth.CONFIGS[2]
+    g = w.geom
+    per = max(1, (1 << 24) // g.tok_per_frame)
+    assert fd.view_shift(g, per) == 0 and fd.view_shift(g, per - 1) == (per - 1) * g.tok_per_frame
+    t0 = per - 2
+    pk, pv = synth.prefix_kv(w, 0)
+    win = fd_oracle.StreamWindow(g, pk, pv)
+    kc, vc = H.new_cache(g)
+    H.write_prefix(w, 0, kc, vc)
+    for t in range(t0 - g.n_frames + 1, t0 + 1):   # the ring holds the last F frames
+        k, v, _ = synth.new_frames(w, 0, t)
+        for vi in range(g.n_views):
+            win.push(vi, t, k[vi], v[vi])
+        H.insert(w, 0, kc, vc, t)
+    ws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    view, full = _key_view(g), _key_view(g)
+    out, ref = (torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV) for _ in range(2))
+    q0 = H.q_new(w, 0, t0)
+    fd.stream_attn_view(g, q0, kc, vc, t0, view, -1, out, ws)   # the view of t0
+    vf = t0
+    qpos = fd_oracle.new_query_positions(g)
+    for t in (per - 1, per, per + 1):
+        k, v, q = synth.new_frames(w, 0, t)
+        for vi in range(g.n_views):
+            win.push(vi, t, k[vi], v[vi])
+        kc2, vc2 = kc.clone(), vc.clone()
+        kn, vn, qd = H.dev(k, g), H.dev(v, g), H.dev(q, g)
+        fd.stream_attn_insert_view(g, kn, vn, qd, kc, vc, t, view, vf, out, ws)
+        fd.stream_attn_insert_view(g, kn, vn, qd, kc2, vc2, t, full, -1, ref, ws)
+        vf = t
+        torch.cuda.synchronize()
+        assert torch.equal(view, full) and torch.equal(out, ref), t
+        kw, vw = win.kv()
+        wnt = fd_oracle.attend(q, kw, vw, qpos, fd_oracle.window_positions(g, kw.shape[0]), g.rope_theta)
+        err = H.check_out(out.cpu().numpy().astype(np.float64), wnt, g, "f32", ("view wrap", t))
+        H.say(f"  t={t} (offset {fd.view_shift(g, t)}): max-abs vs oracle {err:.3e}")
+
+
 # ---------------------------------------------------------------------------- fp16 operand range
 # For bf16 inputs the rotated keys, and the rotated queries scaled by log2(e)/sqrt(D), are
 # rounded to fp16 for the Q K^T matrix cores.  A rotated element is x cos - y sin (or
