@@ -3,7 +3,9 @@
 One step = one window of the 36-layer backbone, for every layer:
     insert               new frame of 4 views -> ring slot
     streaming prefill    1,024 new-frame queries over 4,608 keys      (config 3)
-        (the two through fd_stream_attn_insert, which copies the frame in the rotation pass)
+        (the two through fd_stream_attn_insert_view, which copies the frame in the rotation pass
+        and keeps the layer's keys rotated in a persistent view: after the first window only the
+        prefix and the new frames are rotated)
     fd_verify_attn       8-token block over 4,608 + 200 + 8 keys      (config 4)
 with 36 independent per-layer caches (717 MB of K/V, beyond the 256 MB Infinity Cache),
 the ring advancing one frame per step.  Inputs are synthetic, seeded, resident in HBM.
@@ -218,21 +220,47 @@ def rolling_windows(g, n_windows, gen, host_ahead):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n_windows * 1e3
 
+    kview = torch.empty(g.n_kv_heads, g.window, g.head_dim, dtype=torch.float16, device=dev)
+
+    def sweep_view(fused):
+        # the persistent key view carried from window to window (the first one builds it whole)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        host_ahead()
+        e0.record()
+        for w in range(n_windows):
+            t = t0 + w
+            if fused:
+                fd.stream_attn_insert_view(g, kn[w % n_in], vn[w % n_in], qn[w % n_in], kc, vc, t, kview, t - 1,
+                                           out, sws)
+            else:
+                fd.stream_attn_view(g, qn[w % n_in], kc, vc, t, kview, t - 1, out, sws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n_windows * 1e3
+
     sweep(True)   # warm-up
     fused_us = min(sweep(True) for _ in range(2))
     att_us = min(sweep(False) for _ in range(2))
+    fd.stream_attn_view(g, qn[0], kc, vc, t0 - 1, kview, -1, out, sws)   # the view of the window before
+    sweep_view(True)
+    fused_view_us = min(sweep_view(True) for _ in range(2))
+    att_view_us = min(sweep_view(False) for _ in range(2))
     flops = 4 * g.head_dim * g.n_q_heads * stream_pairs(g)
-    tf = flops / (att_us * 1e-6) / 1e12
+    tf = flops / (att_view_us * 1e-6) / 1e12
     return {
         "windows": n_windows,
+        "stream_view_us_per_window": round(att_view_us, 2),
+        "stream_insert_view_us_per_window": round(fused_view_us, 2),
         "stream_us_per_window": round(att_us, 2),
         "stream_insert_us_per_window": round(fused_us, 2),
         "gflop_per_window": round(flops / 1e9, 2),
         "achieved_tflops": round(tf, 2),
         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
         "note": "100 rolling windows of one layer at 8,704 keys (V=4, F=8, T=256, P=512, 32/8 heads, D=128); "
-                "fd_stream_attn per window (the attention alone, rate and frac) and fd_stream_attn_insert "
-                "(the window step with its insert); HIP events around each 100-window sweep; timing inputs "
+                "fd_stream_attn_view per window with the persistent key view carried between windows (the "
+                "attention alone, rate and frac) and fd_stream_attn_insert_view (the window step with its "
+                "insert); beside them the same without a view (fd_stream_attn, fd_stream_attn_insert: the "
+                "whole window rotated every call); HIP events around each 100-window sweep; timing inputs "
                 "N(0,1) bf16",
     }
 
@@ -285,6 +313,8 @@ def main():
     vout = [torch.empty(blk, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
     ws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=dev)
     sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=dev)   # shared by layers
+    kview = [torch.empty(g.n_kv_heads, g.window, g.head_dim, dtype=torch.float16, device=dev) for _ in range(L)]
+    vframe = [-1] * L   # the frame each layer's key view reflects (-1: none yet)
     torch.cuda.synchronize()
 
     frame = [g.n_frames]   # newest frame index; the window starts full
@@ -296,13 +326,33 @@ def main():
         torch.cuda._sleep(12_000_000)
 
     def step():
-        """One window: per layer the new frames' insert fused with the streaming-prefill call, then
-        the verify."""
+        """One window: per layer the new frames' insert fused with the streaming-prefill call over
+        the layer's persistent key view (after the first window only the prefix and the new frames
+        are rotated), then the verify."""
+        t = frame[0]
+        for l in range(L):
+            fd.stream_attn_insert_view(g, kn[l], vn[l], qn[l], kc[l], vc[l], t, kview[l], vframe[l], out[l], sws)
+            vframe[l] = t
+            fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
+        frame[0] += 1
+
+    def step_plain():
+        """The same window without a key view: every call rotates the whole window."""
         t = frame[0]
         for l in range(L):
             fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t, out[l], sws)
             fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
         frame[0] += 1
+
+    def timed_steps(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(args.warmup):
         step()
@@ -310,13 +360,13 @@ def main():
     # whole-step timing
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step()
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = timed_steps(step, args.steps)
+    plain_ms_per_step = None
+    if not args.core_only:
+        step_plain()
+        plain_ms_per_step = timed_steps(step_plain, max(2, args.steps // 2))
+        for l in range(L):
+            vframe[l] = -1   # the plain steps left the views behind
 
     # per-call timing: each call type swept over the layers back to back behind a queued GPU spin,
     # two HIP events (on the stream the kernels are launched on) around each sweep, so a figure is
@@ -338,13 +388,24 @@ def main():
     t_pc = frame[0]
     reps = max(2, args.steps // 4)
     ins_ms = sweep(lambda l: fd.kv_insert_frame(g, kc[l], vc[l], kn[l], vn[l], t_pc), reps)
-    att_ms = sweep(lambda l: fd.stream_attn(g, qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
+    plain = not args.core_only   # core-only (profiled runs): the view calls only, so that every
+    # rotation-pass launch in a trace covers the same rows
+    att_ms = sweep(lambda l: fd.stream_attn(g, qn[l], kc[l], vc[l], t_pc, out[l], sws), reps) if plain else None
     ver_ms = sweep(lambda l: fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t_pc, n_tail, blk, vout[l], ws),
                    reps)
-    si_ms = sweep(lambda l: fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
+    si_ms = (sweep(lambda l: fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
+             if plain else None)
+    for l in range(L):   # each layer's view of t_pc (the insert sweeps above put frame t_pc in the cache)
+        fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], -1, out[l], sws)
+    # with the view of t_pc: a call rotates the prefix and the newest slot, as one from the view of t_pc - 1
+    attv_ms = sweep(lambda l: fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], t_pc, out[l], sws), reps)
+    siv_ms = sweep(lambda l: fd.stream_attn_insert_view(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, kview[l], t_pc,
+                                                        out[l], sws), reps)
     mean = lambda a: sum(a) / len(a)
     med = lambda a: sorted(a)[len(a) // 2]
-    att_us, ver_us, ins_us = mean(att_ms) * 1e3, mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
+    att_us = mean(att_ms) * 1e3 if plain else None
+    ver_us, ins_us = mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
+    attv_us = mean(attv_ms) * 1e3
 
     v16_us = graph_ms_per_step = prefill_us = kvproj_us = c5 = vgraph_us = batched = None
     esz_in = 2
@@ -451,7 +512,7 @@ def main():
                 gr = torch.cuda.CUDAGraph()
                 frame[0] = g.n_frames + i
                 with torch.cuda.graph(gr, stream=side):
-                    step()
+                    step_plain()   # a graph fixes the view offset, which moves with the frame index
                 graphs[(g.n_frames + i) % F] = gr
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
@@ -473,7 +534,8 @@ def main():
     v16bytes_layer = verify_bytes(g, n_tail, b16, esz)
     ibytes_layer = 2 * 2 * g.n_views * g.tok_per_frame * g.n_kv_heads * g.head_dim * esz
     value = flops_layer * L / (ms_per_step * 1e-3) / 1e12
-    att_tflops = flops_layer / (att_us * 1e-6) / 1e12
+    att_tflops = flops_layer / (attv_us * 1e-6) / 1e12
+    att_plain_tflops = flops_layer / (att_us * 1e-6) / 1e12 if plain else None
     ver_gbs = vbytes_layer / (ver_us * 1e-6) / 1e9
 
     res = {
@@ -491,14 +553,14 @@ def main():
         "data": "synthetic (seeded N(0,1), bf16, resident in HBM)",
         "config": {
             "workload": f"backbone window step: {L} layers x (insert 4x256-token frame + streaming-prefill "
-                        f"attention, 1024 queries over 4608 keys, 32/8 heads, D=128 + 8-token verify over "
-                        f"4608+{n_tail}+{blk} keys)",
+                        f"attention over the layer's persistent key view, 1024 queries over 4608 keys, 32/8 "
+                        f"heads, D=128 + 8-token verify over 4608+{n_tail}+{blk} keys)",
             "layers": L, "views": g.n_views, "frames": g.n_frames, "tok_per_frame": g.tok_per_frame,
             "prefix": g.prefix_len, "heads_q_kv": [g.n_q_heads, g.n_kv_heads], "head_dim": g.head_dim,
             "parallelism": "1 GPU",
         },
         "roofline": {
-            "kernel": "fd_stream_attn (rope_window_kernel + stream_pp_kernel + stream_merge_kernel)",
+            "kernel": "fd_stream_attn_view (rope_window_kernel + stream_pp_kernel + stream_merge_kernel)",
             "bound": "mfma",
             "achieved": round(att_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -515,13 +577,21 @@ def main():
             "frac": round(ver_gbs / PEAK_HBM_GBS, 4),
             "traffic": committed_traffic("verify_attn_config4_traffic.md"),
         },
-        "per_call_us": {"insert": round(ins_us, 2), "stream_attn": round(att_us, 2),
-                        "verify_attn": round(ver_us, 2), "stream_attn_insert": round(mean(si_ms) * 1e3, 2)},
+        "per_call_us": {"insert": round(ins_us, 2), "stream_attn_view": round(attv_us, 2),
+                        "stream_attn_insert_view": round(mean(siv_ms) * 1e3, 2), "verify_attn": round(ver_us, 2),
+                        "stream_attn": plain and round(att_us, 2),
+                        "stream_attn_insert": plain and round(mean(si_ms) * 1e3, 2)},
+        "stream_attn_plain_tflops": plain and round(att_plain_tflops, 2),
         "per_call_us_median": {k: round(med(x) * 1e3, 2) for k, x in
-                               (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
+                               (("insert", ins_ms), ("stream_attn_view", attv_ms), ("stream_attn", att_ms),
+                                ("verify_attn", ver_ms)) if x},
         "per_call_us_min": {k: round(min(x) * 1e3, 2) for k, x in
-                            (("insert", ins_ms), ("stream_attn", att_ms), ("verify_attn", ver_ms))},
-        "per_call_note": "each call type swept over the 36 layers back to back; HIP events around each sweep",
+                            (("insert", ins_ms), ("stream_attn_view", attv_ms), ("stream_attn", att_ms),
+                             ("verify_attn", ver_ms)) if x},
+        "per_call_note": "each call type swept over the 36 layers back to back; HIP events around each sweep; "
+                         "_view: with the layer's persistent key view (the prefix and the new frames rotated), "
+                         "without: the whole window rotated every call",
+        "plain_ms_per_step": None if plain_ms_per_step is None else round(plain_ms_per_step, 4),
         "verify_graph": None if vgraph_us is None else {
             "us_per_call": round(vgraph_us, 2),
             "gbs": round(vbytes_layer / (vgraph_us * 1e-6) / 1e9, 1),
@@ -552,9 +622,11 @@ def main():
             "note": "fd_kv_project_insert: 1,024 tokens x hidden 4,096 -> K and V (8 heads x 128), "
                     "written into the ring slot"},
         "graph": None if graph_ms_per_step is None else {
-            "ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": round(ms_per_step, 4),
+            "ms_per_step": round(graph_ms_per_step, 4), "eager_ms_per_step": plain_ms_per_step and round(plain_ms_per_step, 4),
             "graphs": F, "launches_per_step": L * 5,
-            "note": "the same step replayed from one HIP graph per ring phase (t mod F)"},
+            "note": "the step without key views (fd_stream_attn_insert + fd_verify_attn per layer) replayed from "
+                    "one HIP graph per ring phase (t mod F), beside the same step run eagerly; a key view's "
+                    "offset follows the frame index, which a replayed graph cannot"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

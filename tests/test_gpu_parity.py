@@ -5,6 +5,8 @@ accumulation; cache insertion and the verify tail copy are compared bit for bit.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -304,8 +306,9 @@ def check_verify_batched(w, layer, t, n_tails, stride, blk, view=None, out_dtype
     """S draft blocks over one window in one call: draft d's reasoning rows (seeded per draft)
     at cache rows N + d*stride, its block after them; every draft against oracle_verify with its
     own tail and block, block rows copied bit-exactly, other tail rows untouched.  view: None
-    (keys rotated in the kernel), "rotate" (fd_rotate_window) or "stream" (a streaming call's
-    workspace start)."""
+    (keys rotated in the kernel), "rotate" (fd_rotate_window), "stream" (a streaming call's
+    workspace start) or "persistent" (fd_stream_attn_view's key view, the verify's pos_base
+    raised by fd_view_shift)."""
     g = w.geom
     S = len(n_tails)
     H.say(f"batched verify cfg {w.cfg_id} layer {layer} t {t} drafts {S} tails {n_tails} stride {stride} "
@@ -331,10 +334,22 @@ def check_verify_batched(w, layer, t, n_tails, stride, blk, view=None, out_dtype
         o = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
         fd.stream_attn(g, H.q_new(w, layer, t), kc, vc, t, o, sws)
         kview = sws
+    gv = g
+    if view == "persistent":   # a persistent view updated at t from the view of t-1, and the
+        # verify's positions raised by the view's offset
+        kc1, vc1 = H.window_caches(w, layer, t - 1)
+        sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+        o = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
+        kview = torch.empty((g.n_kv_heads, g.window, g.head_dim), dtype=torch.float16, device=H.DEV)
+        fd.stream_attn_view(g, H.q_new(w, layer, t - 1), kc1, vc1, t - 1, kview, -1, o, sws)
+        H.insert(w, layer, kc1, vc1, t)
+        fd.stream_attn_view(g, H.q_new(w, layer, t), kc1, vc1, t, kview, t - 1, o, sws)
+        gv = dataclasses.replace(g, pos_base=g.pos_base + fd.view_shift(g, t))
+        H.say(f"  persistent view, verify pos_base {gv.pos_base}")
     out = torch.empty((S, blk, g.n_q_heads, g.head_dim),
                       dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=H.DEV)
     ws = torch.full((fd.verify_batched_workspace_bytes(g, S, blk),), 0xAB, dtype=torch.uint8, device=H.DEV)
-    fd.verify_attn_batched(g, q, k, v, kc, vc, t, n_tails, stride, blk, out, ws, k_view=kview,
+    fd.verify_attn_batched(gv, q, k, v, kc, vc, t, n_tails, stride, blk, out, ws, k_view=kview,
                            out_dtype=out_dtype)
     got = out.float().cpu().numpy()
     win = fd_oracle.StreamWindow(g, *synth.prefix_kv(w, layer))
@@ -356,7 +371,8 @@ def check_verify_batched(w, layer, t, n_tails, stride, blk, view=None, out_dtype
 
 @pytest.mark.parametrize("cid,n_tails,stride,view", [
     (4, [100, 37], 128, None), (4, [0, 5, 17, 33, 12, 30], 42, None), (4, [200], 0, "rotate"),
-    (4, [0, 5, 17, 33, 12, 30], 42, "stream"), (2, [20, 3], 32, None), (2, [0, 1, 2, 0, 1, 2], 10, "rotate")])
+    (4, [0, 5, 17, 33, 12, 30], 42, "stream"), (2, [20, 3], 32, None), (2, [0, 1, 2, 0, 1, 2], 10, "rotate"),
+    (4, [200], 0, "persistent"), (2, [20, 3], 32, "persistent")])
 def test_verify_batched(cid, n_tails, stride, view):
     w = synth.CONFIGS[cid]
     check_verify_batched(w, 0, w.first_t + 1, n_tails, stride, 8, view)
