@@ -311,7 +311,8 @@ def main():
     kb = [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
     vb = [rnd(blk, g.n_kv_heads, g.head_dim) for _ in range(L)]
     vout = [torch.empty(blk, g.n_q_heads, g.head_dim, device=dev) for _ in range(L)]
-    ws = torch.empty(fd.verify_workspace_bytes(g, blk), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(fd.verify_workspace_bytes(g, blk), fd.verify_batched_workspace_bytes(g, 1, blk)),
+                     dtype=torch.uint8, device=dev)
     sws = torch.empty(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=dev)   # shared by layers
     kview = [torch.empty(g.n_kv_heads, g.window, g.head_dim, dtype=torch.float16, device=dev) for _ in range(L)]
     vframe = [-1] * L   # the frame each layer's key view reflects (-1: none yet)
@@ -325,15 +326,22 @@ def main():
         pair brackets one call's kernels, not the host's time to issue the next call."""
         torch.cuda._sleep(12_000_000)
 
+    def view_geom(t):
+        """The geometry whose positions carry the key views' offset at frame t: a verify over a
+        view reads its window keys from it and rotates its own rows at these positions."""
+        return g.replace(pos_base=g.pos_base + fd.view_shift(g, t))
+
     def step():
         """One window: per layer the new frames' insert fused with the streaming-prefill call over
         the layer's persistent key view (after the first window only the prefix and the new frames
-        are rotated), then the verify."""
+        are rotated), then the verify with its window keys read from that view."""
         t = frame[0]
+        gv = view_geom(t)
         for l in range(L):
             fd.stream_attn_insert_view(g, kn[l], vn[l], qn[l], kc[l], vc[l], t, kview[l], vframe[l], out[l], sws)
             vframe[l] = t
-            fd.verify_attn(g, qb[l], kb[l], vb[l], kc[l], vc[l], t, n_tail, blk, vout[l], ws)
+            fd.verify_attn_batched(gv, qb[l], kb[l], vb[l], kc[l], vc[l], t, [n_tail], 0, blk, vout[l], ws,
+                                   k_view=kview[l])
         frame[0] += 1
 
     def step_plain():
@@ -401,11 +409,14 @@ def main():
     attv_ms = sweep(lambda l: fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], t_pc, out[l], sws), reps)
     siv_ms = sweep(lambda l: fd.stream_attn_insert_view(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, kview[l], t_pc,
                                                         out[l], sws), reps)
+    gv_pc = view_geom(t_pc)
+    verv_ms = sweep(lambda l: fd.verify_attn_batched(gv_pc, qb[l], kb[l], vb[l], kc[l], vc[l], t_pc, [n_tail], 0, blk,
+                                                     vout[l], ws, k_view=kview[l]), reps)
     mean = lambda a: sum(a) / len(a)
     med = lambda a: sorted(a)[len(a) // 2]
     att_us = mean(att_ms) * 1e3 if plain else None
     ver_us, ins_us = mean(ver_ms) * 1e3, mean(ins_ms) * 1e3
-    attv_us = mean(attv_ms) * 1e3
+    attv_us, verv_us = mean(attv_ms) * 1e3, mean(verv_ms) * 1e3
 
     v16_us = graph_ms_per_step = prefill_us = kvproj_us = c5 = vgraph_us = batched = None
     esz_in = 2
@@ -536,7 +547,8 @@ def main():
     value = flops_layer * L / (ms_per_step * 1e-3) / 1e12
     att_tflops = flops_layer / (attv_us * 1e-6) / 1e12
     att_plain_tflops = flops_layer / (att_us * 1e-6) / 1e12 if plain else None
-    ver_gbs = vbytes_layer / (ver_us * 1e-6) / 1e9
+    ver_gbs = vbytes_layer / (verv_us * 1e-6) / 1e9
+    ver_plain_gbs = vbytes_layer / (ver_us * 1e-6) / 1e9
 
     res = {
         "metric": METRIC,
@@ -569,7 +581,8 @@ def main():
             "traffic": committed_traffic("stream_attn_config3_traffic.md"),
         },
         "roofline_verify": {
-            "kernel": "fd_verify_attn (verify_dma_kernel + verify_merge_dma_kernel)",
+            "kernel": "fd_verify_attn_batched, one draft, window keys from the key view (verify_dma_kernel + "
+                      "verify_merge_dma_kernel)",
             "bound": "hbm",
             "achieved": round(ver_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -578,16 +591,18 @@ def main():
             "traffic": committed_traffic("verify_attn_config4_traffic.md"),
         },
         "per_call_us": {"insert": round(ins_us, 2), "stream_attn_view": round(attv_us, 2),
-                        "stream_attn_insert_view": round(mean(siv_ms) * 1e3, 2), "verify_attn": round(ver_us, 2),
+                        "stream_attn_insert_view": round(mean(siv_ms) * 1e3, 2),
+                        "verify_attn_view": round(verv_us, 2), "verify_attn": round(ver_us, 2),
                         "stream_attn": plain and round(att_us, 2),
                         "stream_attn_insert": plain and round(mean(si_ms) * 1e3, 2)},
         "stream_attn_plain_tflops": plain and round(att_plain_tflops, 2),
+        "verify_attn_plain_gbs": round(ver_plain_gbs, 1),
         "per_call_us_median": {k: round(med(x) * 1e3, 2) for k, x in
                                (("insert", ins_ms), ("stream_attn_view", attv_ms), ("stream_attn", att_ms),
-                                ("verify_attn", ver_ms)) if x},
+                                ("verify_attn_view", verv_ms), ("verify_attn", ver_ms)) if x},
         "per_call_us_min": {k: round(min(x) * 1e3, 2) for k, x in
                             (("insert", ins_ms), ("stream_attn_view", attv_ms), ("stream_attn", att_ms),
-                             ("verify_attn", ver_ms)) if x},
+                             ("verify_attn_view", verv_ms), ("verify_attn", ver_ms)) if x},
         "per_call_note": "each call type swept over the 36 layers back to back; HIP events around each sweep; "
                          "_view: with the layer's persistent key view (the prefix and the new frames rotated), "
                          "without: the whole window rotated every call",

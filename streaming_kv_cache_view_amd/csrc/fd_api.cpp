@@ -252,8 +252,9 @@ size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len) {
                     : fd::verify_splits(fd::verify_blocks(g->prefix_len, g->n_views, g->n_frames,
                                                           g->tok_per_frame, g->tail_cap),
                                         fd::kVerifyWaves * fd::kVerifyBlocksPerWave);
-  return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * fd::verify_row_blocks(G, blk_len) * S *
-                                                   fd::verify_partial_words(g->head_dim) * sizeof(float);
+  const size_t pw = g->in_dtype == FD_BF16 ? fd::verify_dma_partial_words(g->head_dim)
+                                           : fd::verify_partial_words(g->head_dim);
+  return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * fd::verify_row_blocks(G, blk_len) * S * pw * sizeof(float);
 }
 
 size_t fd_verify_batched_workspace_bytes(const fd_geom* g, int32_t n_drafts, int32_t blk_len) {
@@ -265,7 +266,7 @@ size_t fd_verify_batched_workspace_bytes(const fd_geom* g, int32_t n_drafts, int
   // every draft's tail fits in tail_cap: its slots are at most those of a tail_cap-row tail
   const int S = fd::verify_dma_slots(g->prefix_len, g->n_views, g->n_frames, g->tok_per_frame, g->tail_cap);
   return fd::kVerifyWsHeader + size_t(g->n_kv_heads) * n_drafts * fd::verify_row_blocks(G, blk_len) *
-                                                   S * fd::verify_partial_words(g->head_dim) * sizeof(float);
+                                                   S * fd::verify_dma_partial_words(g->head_dim) * sizeof(float);
 }
 
 namespace {

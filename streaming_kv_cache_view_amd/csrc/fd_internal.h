@@ -77,6 +77,9 @@ inline int verify_blocks(int P, int V, int F, int T, int tail_rows) {
 inline int verify_splits(int nblk, int blocks_per_wg) { return ceil_div(nblk, blocks_per_wg); }
 // fp32 words of one (kv head, split) partial: O[32][D], m[32], l[32]
 constexpr size_t verify_partial_words(int D) { return (size_t)32 * D + 64; }
+// bf16 path: O^T in fp16 (32*D halves, the split kernel's accumulator order), each (row, 32-wide
+// d slice) scaled by a power of two; then fp32 (m, l)[32] and the inverse scales [D/32][32]
+constexpr size_t verify_dma_partial_words(int D) { return (size_t)16 * D + 64 + D; }
 // bf16 path: key blocks per workgroup ("unit"); units over the window's blocks; units over one
 // draft's tail of tail_rows rows (reasoning rows + block rows); partial slots per (kv head, row
 // block) with tails up to tail_rows: one per unit

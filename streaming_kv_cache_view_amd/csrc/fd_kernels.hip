@@ -2395,7 +2395,7 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
     const int cb2 = (32 * sl + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     return key0 * ROWB + ((((cb2 >> 4) ^ vswz(key0)) << 4) | (cb2 & 15));
   }();
-  const size_t pw = verify_partial_words(D);
+  const size_t pw = verify_dma_partial_words(D);
   for (int rc = rb_lo; rc < rb_hi; rc += QR) {
   const int nr = min(QR, rb_hi - rc);
   if (rc > rb_lo) {   // the next row blocks' queries, once every wave is done with qbuf
@@ -2484,17 +2484,29 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
         }
       }
     }
-    if (w < NS) {
+    if (w < NS) {   // the partial (verify_dma_partial_words): O^T slice sl of row l32 in fp16, scaled
+      // by a power of two that brings the slice's largest magnitude (this lane's 16 values and
+      // its partner's in the other half) into [2^14, 2^15); then (m, l) pairs and 1/scale in fp32
       float L = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) L += red_l[ww][l32];
       float* dst = part + ((static_cast<int64_t>(kvh) * p.n_rb + rb) * p.n_split + slot) * pw;
+      float mxo = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(dst + ((sl * 4 + j) * 64 + lane) * 4) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-      if (sl == 0 && lane < 32) {
-        dst[32 * D + l32] = M;
-        dst[32 * D + 32 + l32] = L;
+      for (int i = 0; i < 16; ++i) mxo = fmaxf(mxo, fabsf(o[i]));
+      const int sc = partial_row_scale(xhalf_max(mxo));
+      const float mul = exp2_int(sc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f16x4 hv = f16x4{static_cast<_Float16>(o[4 * j] * mul), static_cast<_Float16>(o[4 * j + 1] * mul),
+                               static_cast<_Float16>(o[4 * j + 2] * mul), static_cast<_Float16>(o[4 * j + 3] * mul)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<_Float16*>(dst) + ((sl * 4 + j) * 64 + lane) * 4) =
+            __builtin_bit_cast(u32x2, hv);
+      }
+      if (lane < 32) {
+        dst[16 * D + 64 + 32 * sl + l32] = exp2_int(-sc);
+        if (sl == 0) *reinterpret_cast<f32x2*>(dst + 16 * D + 2 * l32) = f32x2{M, L};
       }
     }
   }
@@ -2581,8 +2593,9 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
 
 // Verify merge for the bf16 split kernel: fixed-order log-sum-exp combination, per (kv head, query
 // row), of the partials of the row's draft: the window units' and that draft's tail units', NH
-// key groups each.  O is stored in the accumulator order of the split kernel: element (row q,
-// d = 32s + 8j + 4h + e) at ((s*4 + j)*64 + q + 32h)*4 + e.  One workgroup per (kv head, row),
+// key groups each.  O is stored in fp16 in the accumulator order of the split kernel: element
+// (row q, d = 32s + 8j + 4h + e) at half ((s*4 + j)*64 + q + 32h)*4 + e, times the scale of
+// (row q, slice s) whose inverse follows the rows' (m, l) pairs.  One workgroup per (kv head, row),
 // kv head = blockIdx % Hkv as in the split kernel (the partials' XCD); thread (slot group sg,
 // 4 consecutive d).
 template <int D>
@@ -2598,25 +2611,27 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   if (hh >= p.G) return;
   const int sg = threadIdx.x / CPR, c = threadIdx.x % CPR;
   const int s = c / 8, j = (c % 8) / 2, hf = c % 2;
-  const int ooff = ((s * 4 + j) * 64 + q + 32 * hf) * 4;
+  const int ooff = ((s * 4 + j) * 64 + q + 32 * hf) * 4;   // (halves) 4 consecutive d of row q
   // slots of this draft: the window units', then its own tail units'
   const int ntb = ceil_div(p.n_tails[dft] + p.B, kVerifyBlock);
   const int n_used = p.n_ws + ceil_div(ntb, kVerifyUnitBlocks);
-  const size_t pw = verify_partial_words(D);
+  const size_t pw = verify_dma_partial_words(D);
   const float* base = part + (static_cast<size_t>(kvh) * p.n_rb + rb) * p.n_split * pw;
   float M = -INFINITY, L = 0.f;
   f32x4 acc = f32x4{};
   for (int s0 = sg; s0 < n_used; s0 += SG * MAXF) {
     // every load of the batch issued back to back: a slot past n_used re-reads the last one
     // and is dropped below (max -inf, weight 0), so no branch splits the loads
-    float mm[MAXF], ll[MAXF];
-    f32x4 ov[MAXF];
+    float mm[MAXF], ll[MAXF], os[MAXF];
+    u32x2 ov[MAXF];
 #pragma unroll
     for (int jj = 0; jj < MAXF; ++jj) {
       const float* ps = base + min(s0 + jj * SG, n_used - 1) * pw;
-      mm[jj] = ps[32 * D + q];
-      ll[jj] = ps[32 * D + 32 + q];
-      ov[jj] = *reinterpret_cast<const f32x4*>(ps + ooff);
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(ps + 16 * D + 2 * q);
+      mm[jj] = ml[0];
+      ll[jj] = ml[1];
+      os[jj] = ps[16 * D + 64 + 32 * s + q];
+      ov[jj] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(ps) + ooff);
     }
     float Mn = M;
 #pragma unroll
@@ -2630,7 +2645,10 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
 #pragma unroll
     for (int jj = 0; jj < MAXF; ++jj) {
       const float wgt = mm[jj] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[jj] - Mn);
-      acc += wgt * ov[jj];
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+      const f16x4 hv = __builtin_bit_cast(f16x4, ov[jj]);
+      acc += (wgt * os[jj]) * f32x4{static_cast<float>(hv[0]), static_cast<float>(hv[1]), static_cast<float>(hv[2]),
+                                    static_cast<float>(hv[3])};
       L += wgt * ll[jj];
     }
     M = Mn;

@@ -260,24 +260,27 @@ def test_kv_project_call_errors():
 
 
 def test_workspace_size_covers_largest_block():
-    """bf16: one partial per (kv head, row block, unit); units of 8 key blocks over the window,
-    then over a draft's tail (its longest: tail_cap rows).  fp32: one per (kv head, row block,
-    4-block split) of the whole key list."""
+    """bf16: one partial per (kv head, row block, unit); units of 5 key blocks over the window,
+    then over a draft's tail (its longest: tail_cap rows); a partial is O^T in fp16 (32*D
+    halves), m and l (32 floats each) and the inverse scales of its D/32 slices (32 floats each).
+    fp32: one fp32 partial (O 32*D, m, l) per (kv head, row block, 4-block split) of the whole
+    key list.  Each size is a 256-byte header plus the slots."""
     g = synth.CONFIGS[4].geom
-    pw = (32 * g.head_dim + 64) * 4
+    pw16 = lambda d: (16 * d + 64 + d) * 4
+    pw32 = (32 * g.head_dim + 64) * 4
     wblk = -(-g.prefix_len // 32) + g.n_views * g.n_frames * -(-g.tok_per_frame // 32)
-    units = -(-wblk // 8) + -(-(-(-g.tail_cap // 32)) // 8)
-    assert units == 18 + 1
-    assert fd.verify_workspace_bytes(g, 8) >= g.n_kv_heads * units * pw
+    units = -(-wblk // 5) + -(-(-(-g.tail_cap // 32)) // 5)
+    assert units == 29 + 2
+    assert fd.verify_workspace_bytes(g, 8) == 256 + g.n_kv_heads * units * pw16(g.head_dim)
     # 16-token blocks: G*16 = 64 query rows per kv head, two 32-row blocks
-    assert fd.verify_workspace_bytes(g, 16) >= 2 * g.n_kv_heads * units * pw
+    assert fd.verify_workspace_bytes(g, 16) == 256 + 2 * g.n_kv_heads * units * pw16(g.head_dim)
     g64 = g.replace(head_dim=64)
-    assert fd.verify_workspace_bytes(g64, 8) >= g.n_kv_heads * units * (32 * 64 + 64) * 4
+    assert fd.verify_workspace_bytes(g64, 8) == 256 + g.n_kv_heads * units * pw16(64)
     g32 = g.replace(dtype=synth.F32)
     splits = -(-(wblk + -(-g.tail_cap // 32)) // 4)
-    assert fd.verify_workspace_bytes(g32, 8) >= g.n_kv_heads * splits * pw
+    assert fd.verify_workspace_bytes(g32, 8) == 256 + g.n_kv_heads * splits * pw32
     # batched: every draft's row blocks
-    assert fd.verify_batched_workspace_bytes(g, 6, 8) >= 6 * g.n_kv_heads * units * pw
+    assert fd.verify_batched_workspace_bytes(g, 6, 8) == 256 + 6 * g.n_kv_heads * units * pw16(g.head_dim)
 
 
 def test_verify_batched_call_errors():
