@@ -403,8 +403,10 @@ def main():
                    reps)
     si_ms = (sweep(lambda l: fd.stream_attn_insert(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, out[l], sws), reps)
              if plain else None)
-    for l in range(L):   # each layer's view of t_pc (the insert sweeps above put frame t_pc in the cache)
-        fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], -1, out[l], sws)
+    for l in range(L):   # each layer's view of t_pc (the insert sweeps above put frame t_pc in the cache):
+        # from the view of the last step (t_pc - 1), or rebuilt whole after the plain steps
+        fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], vframe[l], out[l], sws)
+        vframe[l] = t_pc
     # with the view of t_pc: a call rotates the prefix and the newest slot, as one from the view of t_pc - 1
     attv_ms = sweep(lambda l: fd.stream_attn_view(g, qn[l], kc[l], vc[l], t_pc, kview[l], t_pc, out[l], sws), reps)
     siv_ms = sweep(lambda l: fd.stream_attn_insert_view(g, kn[l], vn[l], qn[l], kc[l], vc[l], t_pc, kview[l], t_pc,
