@@ -637,15 +637,14 @@ def _key_view(g):
                        dtype=torch.float16 if g.dtype == synth.BF16 else torch.float32, device=H.DEV)
 
 
-@pytest.mark.parametrize("cid,n_win", [(1, 6), (2, 9), (5, 12)])
-def test_stream_view_rolling(cid, n_win):
+def check_view_rolling(w, n_win):
     """fd_stream_attn_insert_view over consecutive windows with the view kept between calls (after
     the first only the prefix and the new frames are rotated; the ring wraps), every row against the
     oracle.  Alongside, on a copy of the cache: the frames inserted separately and
     fd_stream_attn_view, and fd_stream_attn_insert_view rebuilding the whole view every window
     (view_frame -1).  Positions are integers, so a frame row's rotated value is the same whether
     it was rotated when the frame came in or again now: all three outputs are bit-identical."""
-    w = synth.CONFIGS[cid]
+    cid = w.cfg_id
     g = w.geom
     ts = list(range(w.first_t, w.first_t + n_win))
     want = oracle_outputs(w, 0, ts)
@@ -673,6 +672,16 @@ def test_stream_view_rolling(cid, n_win):
         assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), "outputs differ"
         err = H.check_out(outs[0].cpu().numpy().astype(np.float64), want[t], g, "f32", ("view", w.name, t))
         H.say(f"    max-abs vs oracle {err:.3e}")
+
+
+@pytest.mark.parametrize("cid,n_win", [(1, 6), (2, 9), (5, 12)])
+def test_stream_view_rolling(cid, n_win):
+    check_view_rolling(synth.CONFIGS[cid], n_win)
+
+
+@pytest.mark.parametrize("w", EXTRA, ids=lambda w: w.name)
+def test_stream_view_edge_geometries(w):
+    check_view_rolling(w, w.geom.n_frames + 2)
 
 
 def test_stream_view_offset_wrap():
