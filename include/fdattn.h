@@ -148,9 +148,10 @@ int fd_kv_project_insert(const fd_geom* g, const void* x_new, const void* w_kv, 
 /* Bytes of workspace fd_stream_attn needs: the window's keys rotated at their current
  * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); for bf16 inputs
  * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements), a
- * table of the attention kernel's key tiles (8 bytes per 64-key tile) and fp32 partial
- * results of views whose key range is split between workgroups (about 2*V*D*4*128 bytes per
- * block of 128 query rows).  0 on invalid geometry.
+ * table of the attention kernel's key tiles (8 bytes per 64-key tile), the merge kernel's
+ * descriptors (16 bytes per query-token block and chunk boundary) and the partial results of
+ * views whose key range is split between workgroups (fp16 O with a per-row scale and fp32
+ * (m, l): about 2*V*(2*D + 16)*128 bytes per block of 128 query rows).  0 on invalid geometry.
  * The size depends on the geometry only, so one workspace serves every layer.            */
 size_t fd_stream_workspace_bytes(const fd_geom* g);
 
@@ -253,8 +254,9 @@ int fd_prefill_attn(const fd_geom* g, const void* q_win,
                     void* hip_stream);
 
 /* Bytes of workspace fd_verify_attn needs for blocks of up to blk_len tokens
- * (any n_tail with n_tail + blk_len <= tail_cap): fp32 (m, l, O) partials per (kv head,
- * 32-row block of query rows, key split); 0 on invalid arguments.                  */
+ * (any n_tail with n_tail + blk_len <= tail_cap): (m, l, O) partials per (kv head,
+ * 32-row block of query rows, key split) -- for bf16 inputs O in fp16 with a per-(row, 32-wide
+ * slice) scale, for fp32 inputs all fp32; 0 on invalid arguments.                  */
 size_t fd_verify_workspace_bytes(const fd_geom* g, int32_t blk_len);
 
 /* Speculative-verify attention of a draft block of blk_len tokens (README technique
