@@ -1,5 +1,6 @@
 // C ABI: argument validation on the host, then a launch on the caller's stream.
 // Every check runs before any HIP call, so every error code is reachable without a GPU.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -32,8 +33,14 @@ int check_geom(const fd_geom* g) {
   return FD_OK;
 }
 
+// Polls of the ready flag of a view cut once, process-wide (fd_merge_wait).  16 polls of ~1,000
+// cycles each (~8 us at 2 GHz): the second piece is the first job of its workgroup, so its flag is
+// normally set long before the first piece (the last job of another workgroup) finishes.
+std::atomic<int32_t> g_merge_polls{16};
+
 fd::KParams make_params(const fd_geom* g, int64_t t) {
   fd::KParams p{};
+  p.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
   p.V = g->n_views;
   p.F = g->n_frames;
   p.T = g->tok_per_frame;
@@ -165,7 +172,7 @@ size_t fd_stream_workspace_bytes(const fd_geom* g) {
   const int n_rb = p.Hkv * p.n_hsub * p.nqb;
   return fd::align256(krot) + fd::stream_qrot_bytes(p.V * p.T, p.Hq, p.D) +
          fd::stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + fd::stream_merge_desc_bytes(p.nqb, p.V) +
-         fd::stream_partial_bytes(n_rb, p.V, p.D);
+         fd::stream_flags_bytes(n_rb, p.V) + fd::stream_partial_bytes(n_rb, p.V, p.D);
 }
 
 size_t fd_prefill_workspace_bytes(const fd_geom* g) {
@@ -218,6 +225,11 @@ int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new
   fd::KParams p = make_params(g, newest_frame);
   return fd::launch_stream(p, g->in_dtype == FD_BF16, q_new, k_cache, v_cache, out, ws, hip_stream, k_new,
                            v_new);
+}
+
+int32_t fd_merge_wait(int32_t polls) {
+  if (polls < 0 || polls > 1024) return g_merge_polls.load(std::memory_order_relaxed);
+  return g_merge_polls.exchange(polls, std::memory_order_relaxed);
 }
 
 int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame) {

@@ -605,7 +605,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
                                                           int nkb, const T* __restrict__ q,
                                                           typename Path<T>::QKT* __restrict__ qrot,
                                                           int2* __restrict__ tiles, int4* __restrict__ mdesc,
-                                                          const NewFrame<T> nf) {
+                                                          unsigned* __restrict__ flags, const NewFrame<T> nf) {
 #pragma clang fp contract(off)   // every instantiation rounds a rotated row the same way
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
@@ -631,6 +631,8 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       const int nb = p.nseg - 1;
       for (int e = tid; e < p.nqb * nb; e += 256) mdesc[e] = stream_merge_desc(p, e / nb, e % nb + 1);
     }
+    if (flags)   // the attention kernel's merge flags, cleared for this call
+      for (int e = tid; e < 2 * p.Hkv * p.n_hsub * p.nqb * p.nseg; e += 256) flags[e] = 0u;
     return;
   }
   const int bx = static_cast<int>(blockIdx.x) - (tiles ? 1 : 0);   // rotation workgroup
@@ -1235,34 +1237,59 @@ __device__ inline int partial_row_scale(float mx) {
 // taken in batches of 2 pieces whose loads are all in flight together; piece i's O_i is its
 // stored fp16 row times its 2^-s.  Segments held whole by one chunk were written by the
 // attention kernel.
-// Workgroup = 256 threads over kMergeItems / (HPW*D/4) tokens of one row block, all HPW
-// heads; D/16 workgroups cover the row block's tokens.  Item e (thread tid takes e = tid and
-// tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4)) .. +3: a
-// token's heads are adjacent rows of the output, so each store instruction of a wave writes
-// 1 KB (fp32) of contiguous output, and the many small workgroups spread the writes over
-// the whole output at once (the same bytes written as 16-byte pieces of a 16 KB-strided
-// pattern by 512-thread workgroups took ~1.8x as long).
+// Workgroup = 256 threads over one (boundary, row block), which takes the row block's D/16
+// groups of kMergeItems / (HPW*D/4) tokens (all HPW heads) in turn.  Item e (thread tid takes
+// e = tid and tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4))
+// .. +3: a token's heads are adjacent rows of the output, so each store instruction of a wave
+// writes 1 KB (fp32) of contiguous output.  A view cut once is normally merged by the attention
+// kernel (its flag set): the workgroup then only reads the flag, so the launch stays small.
 constexpr int kMergeItems = 512;   // 4-column items per merge workgroup
+// 4 fp16 values (as stored) to fp32
+__device__ inline f32x4 f16x4_to_f32(u32x2 x) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const f16x4 h = __builtin_bit_cast(f16x4, x);
+  return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]), static_cast<float>(h[3])};
+}
+// The merge of the two pieces of a view cut once, for 4 consecutive columns of a row: piece i's
+// (row max m_i, row sum l_i, inverse scale s_i) and its 4 stored fp16 values x_i give
+// sum_i 2^(m_i - M) s_i x_i / sum_i 2^(m_i - M) l_i, M = max(m_0, m_1).  The merge kernel and the
+// attention kernel's own merge both call it on the same stored values, so they give the same bits.
+__device__ __forceinline__ f32x4 merge_two(float m0, float l0, float s0, u32x2 x0, float m1, float l1, float s1,
+                                           u32x2 x1) {
+  const float M = fmaxf(m0, m1);
+  const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+  const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+  const float inv = 1.f / __builtin_fmaf(w1, l1, w0 * l0);
+  const float a0 = w0 * s0, a1 = w1 * s1;
+  const f32x4 h0 = f16x4_to_f32(x0), h1 = f16x4_to_f32(x1);
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = __builtin_fmaf(a1, h1[e], a0 * h0[e]) * inv;
+  return r;
+}
 template <int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const int4* __restrict__ mdesc,
+                                                           const unsigned* __restrict__ flags,
                                                            const float* __restrict__ part, void* __restrict__ out) {
   constexpr int CG = D / 4, NSUB = D / 16, MAXP = 2, IPT = kMergeItems / 256;
-  // blockIdx.x = ((((c - 1)*NSUB + sub)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head
-  // fastest, as in the attention kernel, so (for Hkv a multiple of 8) a row block's partials
-  // are merged on the XCD whose L2 they were written through
+  // blockIdx.x = (((c - 1)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head fastest, as in the
+  // attention kernel, so (for Hkv a multiple of 8) a row block's partials are merged on the XCD
+  // whose L2 they were written through
   int bid = blockIdx.x;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
   const int qb = bid % p.nqb;
   bid /= p.nqb;
   const int hsub = bid % p.n_hsub;
-  bid /= p.n_hsub;
-  const int sub = bid % NSUB, cb = bid / NSUB + 1;   // boundary between chunks cb - 1 and cb
-  const int4 dsc = mdesc[qb * (p.nseg - 1) + cb - 1];   // stream_merge_desc
-  if (dsc.x < 0) return;
-  const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;
+  const int cb = bid / p.n_hsub + 1;   // boundary between chunks cb - 1 and cb
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
+  const unsigned merged = flags[n_rb * p.nseg + rbi * p.nseg + cb];   // merged by the attention kernel
+  const int4 dsc = mdesc[qb * (p.nseg - 1) + cb - 1];   // stream_merge_desc
+  if (dsc.x < 0 || merged != 0) return;
+  const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;
   const int per_tok = p.HPW * CG, ntok = kMergeItems / per_tok;
+  for (int sub = 0; sub < NSUB; ++sub) {   // the row block's token groups in turn
   int row[IPT], col[IPT];
   int64_t obase[IPT];
   bool live[IPT];
@@ -1275,6 +1302,25 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
     const int tok = qb * 32 * p.TBW + tr;
     live[k] = tok < p.qtok;
     obase[k] = (static_cast<int64_t>(qrow0 + tok) * p.Hq + kvh * p.G + hsub * p.HPW + hl) * D + col[k];
+  }
+  if (cl == cf + 1) {   // a view cut once: merge_two, as the attention kernel's own merge
+    const float* s0 = stream_slot<D>(const_cast<float*>(part), p, rbi, cf, which_cf);
+    const float* s1 = stream_slot<D>(const_cast<float*>(part), p, rbi, cl, 0);
+    f32x4 ml0[IPT], ml1[IPT];
+    u32x2 x0[IPT], x1[IPT];
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      ml0[k] = *reinterpret_cast<const f32x4*>(s0 + 64 * D + 4 * row[k]);
+      x0[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s0) + row[k] * D + col[k]);
+      ml1[k] = *reinterpret_cast<const f32x4*>(s1 + 64 * D + 4 * row[k]);
+      x1[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s1) + row[k] * D + col[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k)
+      if (live[k])
+        store_out4(out, p.out_bf16, obase[k],
+                   merge_two(ml0[k][0], ml0[k][1], ml0[k][2], x0[k], ml1[k][0], ml1[k][1], ml1[k][2], x1[k]));
+    continue;
   }
   float M[IPT], L[IPT];
   f32x4 acc[IPT];
@@ -1329,6 +1375,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
 #pragma unroll
   for (int k = 0; k < IPT; ++k)
     if (live[k]) store_out4(out, p.out_bf16, obase[k], acc[k] * (1.f / L[k]));
+  }   // token groups
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1351,7 +1398,8 @@ template <int D>
 __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
                                                         const _Float16* __restrict__ krot,
                                                         const bf16* __restrict__ vc, void* __restrict__ out,
-                                                        float* __restrict__ part, const int2* __restrict__ tiles) {
+                                                        float* __restrict__ part, const int2* __restrict__ tiles,
+                                                        const int4* __restrict__ mdesc, unsigned* __restrict__ flags) {
   using QK = F16Ops;
   using PV = BF16Ops;
   constexpr int E = 8;                           // 16-bit elements per 16-byte chunk
@@ -1378,6 +1426,7 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
 
   __shared__ float red_m[4][32], red_l[4][32];
   __shared__ __attribute__((aligned(16))) unsigned char buf[BUFB];
+  __shared__ int s_ready;
 
   const int tid0 = threadIdx.x;
   // wave-uniform values in scalar registers (the index arithmetic of staging and masking)
@@ -1688,10 +1737,80 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS only: the prefetched loads stay in flight
   wg_barrier();
+  // ---- a view cut once (two pieces, stream_merge_desc): its second piece (this chunk's first
+  // job) publishes its partial with device-scope stores and then a ready flag; its first piece
+  // (this chunk's last job, on a workgroup that finishes early) waits a bounded time for that
+  // flag and merges the view here (merge_two), writing its rows; without the flag in time it
+  // leaves its partial for the merge kernel as a split piece does.
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
+  int role = 0;   // 1: first piece of a view cut once, 2: its second piece
+  if (!whole && mdesc) {
+    if (jb < nv) {
+      const int4 d = mdesc[qb * (p.nseg - 1) + chunk];   // boundary chunk + 1
+      role = (d.x == v && (d.y >> 16) == chunk + 1) ? 1 : 0;
+    } else {
+      const int4 d = mdesc[qb * (p.nseg - 1) + chunk - 1];   // boundary chunk (ja > 0 here)
+      role = (d.x == v && (d.y & 0xffff) == chunk - 1 && (d.y >> 16) == chunk) ? 2 : 0;
+    }
+  }
+  bool merge_here = false;
+  if (role == 1) {
+    if (tid == 0) {
+      int rdy = 0;
+      for (int i = 0; i < p.merge_polls && !rdy; ++i) {   // each poll then s_sleep 16 (~1,000 cycles)
+        rdy = __hip_atomic_load(&flags[rbi * p.nseg + chunk + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        if (!rdy) __builtin_amdgcn_s_sleep(16);
+      }
+      s_ready = rdy;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();
+    merge_here = s_ready != 0;
+  }
   // ---- rows out, 16 bytes per lane and whole rows per group of lanes.  Row r of the block
   // is token tok0 + 32*((r/32)/HPW) + r%32 of query head kvh*G + hsub*HPW + (r/32)%HPW.
   const float* rows = reinterpret_cast<const float*>(buf);
-  if (whole) {
+  if (merge_here) {   // this piece quantised exactly as its partial would be stored, then merge_two
+    // with the second piece's stored partial (slot 0 of chunk + 1), read with device-scope loads
+    const float* slot_b = stream_slot<D>(part, p, rbi, chunk + 1, 0);
+    constexpr int TPR = D / 8;
+    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
+      const int c = tid % TPR;
+      const float* src = rows + r * (D + 4) + 8 * c;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const int sc = partial_row_scale(mx);
+      const float mul = exp2_int(sc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x8[e] *= mul;
+      const u32x4 a16 = F16Ops::pack(x8);
+      const uint64_t* bsrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(slot_b) + r * D + 8 * c);
+      const uint64_t* bml = reinterpret_cast<const uint64_t*>(slot_b + 64 * D + 4 * r);
+      const uint64_t b0 = __hip_atomic_load(bsrc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t b1 = __hip_atomic_load(bsrc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t bm = __hip_atomic_load(bml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t bs = __hip_atomic_load(bml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float ma = red_m[r >> 5][r & 31], la = red_l[r >> 5][r & 31], sa = exp2_int(-sc);
+      const float mb2 = __uint_as_float(static_cast<uint32_t>(bm)), lb = __uint_as_float(static_cast<uint32_t>(bm >> 32));
+      const float sb = __uint_as_float(static_cast<uint32_t>(bs));
+      const f32x4 r0 = merge_two(ma, la, sa, u32x2{a16[0], a16[1]}, mb2, lb, sb,
+                                 u32x2{static_cast<uint32_t>(b0), static_cast<uint32_t>(b0 >> 32)});
+      const f32x4 r1 = merge_two(ma, la, sa, u32x2{a16[2], a16[3]}, mb2, lb, sb,
+                                 u32x2{static_cast<uint32_t>(b1), static_cast<uint32_t>(b1 >> 32)});
+      const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
+      if (tk >= p.qtok) continue;
+      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+      const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
+      store_out4(out, p.out_bf16, obase, r0);
+      store_out4(out, p.out_bf16, obase + 4, r1);
+    }
+    if (tid == 0) flags[n_rb * p.nseg + rbi * p.nseg + chunk + 1] = 1u;   // read by the merge kernel
+  } else if (whole) {
     const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
     for (int r = tid / TPR; r < 128; r += 512 / TPR) {
       const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
@@ -1726,9 +1845,29 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
       const float mul = exp2_int(sc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x8[e] *= mul;
-      st16(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c, F16Ops::pack(x8));
-      if (c == 0)
-        *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
+      const u32x4 pk = F16Ops::pack(x8);
+      const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
+      if (role == 2) {   // read by the first piece's workgroup within this launch: device scope
+        uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c);
+        __hip_atomic_store(dst, (static_cast<uint64_t>(pk[1]) << 32) | pk[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, (static_cast<uint64_t>(pk[3]) << 32) | pk[2], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (c == 0) {
+          uint64_t* mdst = reinterpret_cast<uint64_t*>(slot + 64 * D + 4 * r);
+          __hip_atomic_store(mdst, (static_cast<uint64_t>(__float_as_uint(mlv[1])) << 32) | __float_as_uint(mlv[0]),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(mdst + 1, static_cast<uint64_t>(__float_as_uint(mlv[2])), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        st16(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c, pk);
+        if (c == 0) *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = mlv;
+      }
+    }
+    if (role == 2) {   // every lane's stores complete, then the ready flag
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      wg_barrier();
+      if (tid == 0) __hip_atomic_store(&flags[rbi * p.nseg + chunk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   wg_barrier();   // LDS is reused by the next job (this job's output stores drain meanwhile)
@@ -2695,8 +2834,13 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   int4* mdesc = b16 && p.V > 1 ? reinterpret_cast<int4*>(reinterpret_cast<unsigned char*>(tiles) +
                                                           stream_tiles_bytes(0, p.P, p.T, p.V, p.F))
                                : nullptr;
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
+  unsigned* flags = mdesc ? reinterpret_cast<unsigned*>(reinterpret_cast<unsigned char*>(mdesc) +
+                                                        stream_merge_desc_bytes(p.nqb, p.V))
+                          : nullptr;
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.V * p.T, p.Hq, D) +
-                                         stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + stream_merge_desc_bytes(p.nqb, p.V));
+                                         stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + stream_merge_desc_bytes(p.nqb, p.V) +
+                                         stream_flags_bytes(n_rb, p.V));
   const int nkb = rope_key_workgroups<T, D>(p);
   const int nqk = b16 ? ceil_div(p.V * p.T, kRopeQTok) * (p.G / rope_q_heads(p.G)) : 0;
   const NewFrame<T> nf{static_cast<const T*>(kn), static_cast<const T*>(vn),
@@ -2704,19 +2848,19 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
   if (kn)
     hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, nf);
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf);
   else
     hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, nf);
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
-                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles);
+                       static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles, mdesc, flags);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-    if (p.V > 1)   // a workgroup per (chunk boundary, D/16 token group, row block)
-      hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (D / 16) * (grid / p.V)), dim3(256), 0, st, p, mdesc,
-                         part, out);
+    if (p.V > 1)   // a workgroup per (chunk boundary, row block)
+      hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (grid / p.V)), dim3(256), 0, st, p, mdesc,
+                         flags, part, out);
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);
@@ -2738,7 +2882,7 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
   const int nkb = rope_key_workgroups<bf16, D>(p), nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
   hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(1 + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                     static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles, nullptr,
+                     static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles, nullptr, nullptr,
                      NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr});
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   KParams pf = p;   // the frame segments
@@ -2749,7 +2893,7 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   pf.whole = 1;
   const int grid = pf.Hkv * pf.n_hsub * pf.nqb * pf.nseg;
   hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pf, static_cast<const QKT*>(qrot),
-                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, nullptr, tiles);
+                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, nullptr, tiles, nullptr, nullptr);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   if (p.P > 0) {
     KParams pp = p;   // the prefix segment
@@ -2760,7 +2904,7 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
     pp.whole = 1;
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(pp.Hkv * pp.n_hsub * pp.nqb), dim3(512), 0, st, pp,
                        static_cast<const QKT*>(qrot), static_cast<const QKT*>(krot), static_cast<const bf16*>(vc),
-                       out, nullptr, tiles);
+                       out, nullptr, tiles, nullptr, nullptr);
   }
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
@@ -2799,7 +2943,7 @@ int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStr
   const int nkb = rope_key_workgroups<T, D>(p);
   hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb), dim3(256), 0, st, p, static_cast<const T*>(kc),
                      static_cast<typename Path<T>::QKT*>(kview), nkb, static_cast<const T*>(nullptr),
-                     static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr), nullptr,
+                     static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr), nullptr, nullptr,
                      NewFrame<T>{nullptr, nullptr, nullptr, nullptr});
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }

@@ -111,13 +111,15 @@ def test_call_errors():
     # chunk); a row block is 128 query rows: min(G, 4) heads x (4 / min(G, 4)) 32-token blocks
     # -> G=2: 2 heads, 64 tokens, one block per kv head; between queries and partials, the
     # attention kernel's tile table (8 bytes per tile of each view's key sequence: view 0 prefix
-    # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal) and the merge descriptors (16
-    # bytes per token block and chunk boundary: one here)
+    # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal), the merge descriptors (16
+    # bytes per token block and chunk boundary: one here) and the merge flags (two 4-byte flags
+    # per row block and chunk)
     krot = g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
     qrot = 2 * 16 * 4 * 64 * 2
     n_rb = g.n_kv_heads * 1 * 1
     align = lambda x: (x + 255) // 256 * 256
-    assert sws == align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16)
+    assert sws == (align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + align(2 * n_rb * 2 * 4)
+                   + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16))
     assert L.fd_stream_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 4
     assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
     assert L.fd_stream_attn(gp, None, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
@@ -158,6 +160,16 @@ def test_call_errors():
     assert L.fd_verify_attn(gp, None, *args[1:], 5, 0, 8, FAKE, FAKE, ws, None) == -1
     for code in range(-9, 1):
         assert fd.lib().fd_status_str(code).decode() != "unknown status"
+
+
+def test_merge_wait_setting():
+    """fd_merge_wait: default 16 polls; 0..1024 sets and returns the previous count; anything else
+    reads the count and changes nothing."""
+    L = fd.lib()
+    assert L.fd_merge_wait(-1) == 16
+    assert L.fd_merge_wait(0) == 16 and L.fd_merge_wait(-1) == 0
+    assert L.fd_merge_wait(1025) == 0 and L.fd_merge_wait(1024) == 0 and L.fd_merge_wait(-5) == 1024
+    assert L.fd_merge_wait(16) == 1024 and fd.merge_wait() == 16
 
 
 def test_stream_view_call_errors_and_shift():

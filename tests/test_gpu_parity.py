@@ -238,6 +238,29 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_merge_in_kernel_or_merge_kernel_same_bits(cid):
+    """A view that two workgroups share is merged by its first piece's workgroup when the second
+    piece's ready flag comes in time, else by the merge kernel: with the wait at 0 polls every
+    such view goes to the merge kernel, and the outputs must be the same bits (and match the
+    oracle) as with the default wait."""
+    w = synth.CONFIGS[cid]
+    t = w.first_t + 1
+    kc, vc = H.window_caches(w, 0, t)
+    q = H.q_new(w, 0, t)
+    a = H.stream_out(w, 0, kc, vc, t, q=q)
+    prev = fd.merge_wait(0)
+    try:
+        assert fd.merge_wait() == 0
+        b = H.stream_out(w, 0, kc, vc, t, q=q)
+        check_stream(w, 0, [t])
+    finally:
+        fd.merge_wait(prev)
+    assert fd.merge_wait() == prev
+    H.say(f"cfg {cid} t {t}: in-kernel and merge-kernel outputs equal: {torch.equal(a, b)}")
+    assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------------------------- verify
 def check_verify(w, layer, t, n_tail, blk_len, out_dtype="f32"):
     g = w.geom
