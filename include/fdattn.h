@@ -231,7 +231,8 @@ int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame);
 /* Merge wait of the bf16 streaming calls (fd_stream_attn and its insert / view forms), for tests
  * and tuning.  A view whose key range two workgroups share is merged by the workgroup of its
  * first piece when the second piece's ready flag is set within `polls` polls (~1,000 shader
- * cycles each), else by a merge kernel; both give the same bits.  Sets the poll count, process-
+ * cycles each), else by a merge kernel; both give the same bits.  A launch with more attention
+ * workgroups than the device has compute units does not wait (0 polls).  Sets the poll count, process-
  * wide, for calls made after it when 0 <= polls <= 1024 (0: every such view goes to the merge
  * kernel) and returns the count in force before the call; any other polls (say -1) changes
  * nothing and returns the present count.  Default 16.                                      */

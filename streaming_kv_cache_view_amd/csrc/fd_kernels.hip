@@ -37,6 +37,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -2820,6 +2821,18 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   }
 }
 
+// Compute units of the current device (cached per device; 0 when the runtime cannot say)
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cus[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? n : 0;
+}
+
 template <typename T, int D>
 int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                     hipStream_t st, const void* kn, const void* vn, void* kview) {
@@ -2855,7 +2868,11 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
-    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
+    // A first piece waits for its second piece only when every workgroup can be resident at once
+    // (one per CU): with more, the second piece's workgroup may not start until others end.
+    KParams pa = p;
+    if (grid > device_cus()) pa.merge_polls = 0;
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pa, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles, mdesc, flags);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
     if (p.V > 1)   // a workgroup per (chunk boundary, row block)

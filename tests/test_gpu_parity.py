@@ -238,13 +238,20 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5])
-def test_merge_in_kernel_or_merge_kernel_same_bits(cid):
+# 512 attention workgroups (8 kv heads x 16 token blocks x 4 views), more than the GPU's CUs: the
+# first pieces do not wait for their second pieces there and every split view is merged by the
+# merge kernel
+MANY_WG = Workload(208, "512 workgroups", Geometry(4, 2, 512, 64, 32, 8, 128, 16, 1e6, dtype=synth.BF16), first_t=2)
+
+
+@pytest.mark.parametrize("w", [synth.CONFIGS[2], synth.CONFIGS[3], synth.CONFIGS[5], MANY_WG],
+                         ids=lambda w: w.name)
+def test_merge_in_kernel_or_merge_kernel_same_bits(w):
     """A view that two workgroups share is merged by its first piece's workgroup when the second
     piece's ready flag comes in time, else by the merge kernel: with the wait at 0 polls every
     such view goes to the merge kernel, and the outputs must be the same bits (and match the
     oracle) as with the default wait."""
-    w = synth.CONFIGS[cid]
+    cid = w.cfg_id
     t = w.first_t + 1
     kc, vc = H.window_caches(w, 0, t)
     q = H.q_new(w, 0, t)
