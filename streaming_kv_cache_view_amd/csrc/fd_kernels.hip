@@ -2735,21 +2735,24 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(const KParams p, cons
 // row), of the partials of the row's draft: the window units' and that draft's tail units', NH
 // key groups each.  O is stored in fp16 in the accumulator order of the split kernel: element
 // (row q, d = 32s + 8j + 4h + e) at half ((s*4 + j)*64 + q + 32h)*4 + e, times the scale of
-// (row q, slice s) whose inverse follows the rows' (m, l) pairs.  One workgroup per (kv head, row),
-// kv head = blockIdx % Hkv as in the split kernel (the partials' XCD); thread (slot group sg,
-// 4 consecutive d).
+// (row q, slice s) whose inverse follows the rows' (m, l) pairs.  One workgroup per (kv head,
+// 32-row block, 4-column chunk c = (s, j, h)), kv head = blockIdx % Hkv as in the split kernel (the
+// partials' XCD); thread (slot group sg, row q).  The 32 rows of a chunk are 256 contiguous bytes
+// of a slot, and a row's (m, l) pair and slice scale are contiguous over the rows too, so every
+// load of a wave reads whole lines (with one workgroup per row, each lane's 8 bytes sat in a
+// line of its own and every line was fetched by 16 workgroups).
 template <int D>
 __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, const float* __restrict__ part,
                                                                void* __restrict__ out) {
   constexpr int MAXF = 4;                     // slots folded per thread per pass
-  constexpr int CPR = D / 4;                  // 4-float chunks per row
-  constexpr int SG = 256 / CPR;               // slot groups
+  constexpr int CPR = D / 4;                  // 4-column chunks per row
+  constexpr int SG = 256 / 32;                // slot groups
   const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;
-  const int q = r % 32, rb = r / 32;
-  const int dft = rb / p.nrb_d, rl = r - 32 * p.nrb_d * dft;   // draft, row within the draft
+  const int c = r % CPR, rb = r / CPR;
+  const int dft = rb / p.nrb_d;               // draft
+  const int sg = threadIdx.x / 32, q = threadIdx.x % 32;
+  const int rl = 32 * (rb - p.nrb_d * dft) + q;   // row within the draft
   const int hh = rl / p.B, b = rl % p.B;
-  if (hh >= p.G) return;
-  const int sg = threadIdx.x / CPR, c = threadIdx.x % CPR;
   const int s = c / 8, j = (c % 8) / 2, hf = c % 2;
   const int ooff = ((s * 4 + j) * 64 + q + 32 * hf) * 4;   // (halves) 4 consecutive d of row q
   // slots of this draft: the window units', then its own tail units'
@@ -2799,20 +2802,20 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   sL[threadIdx.x] = L;
   sA[threadIdx.x] = acc;
   __syncthreads();
-  if (sg != 0) return;
+  if (sg != 0 || hh >= p.G) return;
   float Mt = -INFINITY;
-  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, sM[g * CPR + c]);
+  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, sM[g * 32 + q]);
   float Lt = 0.f;
   f32x4 At = f32x4{};
   for (int g = 0; g < SG; ++g) {
-    const float mg = sM[g * CPR + c];
+    const float mg = sM[g * 32 + q];
     if (mg == -INFINITY) continue;
     const float f = __builtin_amdgcn_exp2f(mg - Mt);
-    Lt += f * sL[g * CPR + c];
-    At += f * sA[g * CPR + c];
+    Lt += f * sL[g * 32 + q];
+    At += f * sA[g * 32 + q];
   }
   const f32x4 res = At * (1.f / Lt);
-  const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * D + 4 * c;
+  const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
   if (p.out_bf16) {
     bf16 b4[4] = {static_cast<bf16>(res[0]), static_cast<bf16>(res[1]), static_cast<bf16>(res[2]), static_cast<bf16>(res[3])};
     *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + oidx) = *reinterpret_cast<const u32x2*>(b4);
@@ -2941,7 +2944,7 @@ int launch_verify_t(const KParams& p, const void* qb, const void* kb, const void
                          static_cast<const T*>(kb), static_cast<const T*>(vb), static_cast<T*>(kc), static_cast<T*>(vc),
                          static_cast<const _Float16*>(nullptr), part);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-    hipLaunchKernelGGL((verify_merge_dma_kernel<D>), dim3(p.Hkv * p.n_rb * 32), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((verify_merge_dma_kernel<D>), dim3(p.Hkv * p.n_rb * (D / 4)), dim3(256), 0, st, p,
                        static_cast<const float*>(part), out);
   } else {
     hipLaunchKernelGGL((verify_split_kernel<T, D>), dim3(p.Hkv * p.n_rb * p.n_split), dim3(256), 0, st, p,
