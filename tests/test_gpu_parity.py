@@ -256,16 +256,19 @@ def test_merge_in_kernel_or_merge_kernel_same_bits(w):
     kc, vc = H.window_caches(w, 0, t)
     q = H.q_new(w, 0, t)
     a = H.stream_out(w, 0, kc, vc, t, q=q)
+    a16 = H.stream_out(w, 0, kc, vc, t, out_dtype="bf16", q=q)
     prev = fd.merge_wait(0)
     try:
         assert fd.merge_wait() == 0
         b = H.stream_out(w, 0, kc, vc, t, q=q)
+        b16 = H.stream_out(w, 0, kc, vc, t, out_dtype="bf16", q=q)
         check_stream(w, 0, [t])
     finally:
         fd.merge_wait(prev)
     assert fd.merge_wait() == prev
-    H.say(f"cfg {cid} t {t}: in-kernel and merge-kernel outputs equal: {torch.equal(a, b)}")
-    assert torch.equal(a, b)
+    H.say(f"cfg {cid} t {t}: in-kernel and merge-kernel outputs equal: fp32 {torch.equal(a, b)}, "
+          f"bf16 {torch.equal(a16, b16)}")
+    assert torch.equal(a, b) and torch.equal(a16, b16)
 
 
 # ---------------------------------------------------------------------------- verify
