@@ -574,7 +574,7 @@ def main():
             "parallelism": "1 GPU",
         },
         "roofline": {
-            "kernel": "fd_stream_attn_view (rope_window_kernel + stream_pp_kernel + stream_merge_kernel)",
+            "kernel": "fd_stream_attn_view (rope_window_kernel + stream_pp_kernel; at this geometry no view is cut twice, so no merge launch)",
             "bound": "mfma",
             "achieved": round(att_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -149,7 +149,7 @@ int fd_kv_project_insert(const fd_geom* g, const void* x_new, const void* w_kv, 
  * positions, Hkv*N*D elements of fp16 (bf16 inputs) or fp32 (fp32 inputs); for bf16 inputs
  * also the new frames' queries rotated at their positions (fp16, V*T*Hq*D elements), a
  * table of the attention kernel's key tiles (8 bytes per 64-key tile), the merge kernel's
- * descriptors (16 bytes per query-token block and chunk boundary), two 4-byte merge flags per
+ * descriptors (16 bytes per query-token block and chunk boundary), a 4-byte merge ticket per
  * (block of 128 query rows, chunk), cleared by every call, and the partial results of
  * views whose key range is split between workgroups (fp16 O with a per-row scale and fp32
  * (m, l): about 2*V*(2*D + 16)*128 bytes per block of 128 query rows).  0 on invalid geometry.
@@ -228,15 +228,16 @@ int fd_stream_attn_insert_view(const fd_geom* g, const void* k_new, const void* 
  * geometry or a negative frame. */
 int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame);
 
-/* Merge wait of the bf16 streaming calls (fd_stream_attn and its insert / view forms), for tests
- * and tuning.  A view whose key range two workgroups share is merged by the workgroup of its
- * first piece when the second piece's ready flag is set within `polls` polls (~1,000 shader
- * cycles each), else by a merge kernel; both give the same bits.  A launch with more attention
- * workgroups than the device has compute units does not wait (0 polls).  Sets the poll count, process-
- * wide, for calls made after it when 0 <= polls <= 1024 (0: every such view goes to the merge
- * kernel) and returns the count in force before the call; any other polls (say -1) changes
- * nothing and returns the present count.  Default 16.                                      */
-int32_t fd_merge_wait(int32_t polls);
+/* How the bf16 streaming calls (fd_stream_attn and its insert / view forms) merge a view whose
+ * key range two workgroups share, for tests and tuning.  1 (default): by the workgroup of
+ * whichever piece finishes second (both pieces store their partials and take a ticket; no
+ * workgroup waits for another); 0: by a separate merge kernel; 2: as 1, with the second piece's
+ * workgroup waiting a bounded time for the first piece's ticket so that it is the second piece
+ * that merges (tests).  Every mode gives the same bits.  Views cut more than once always go to
+ * the merge kernel.  Sets the mode, process-wide, for calls made after it when 0 <= mode <= 2
+ * and returns the mode in force before the call; any other value (say -1) changes nothing and
+ * returns the present mode.                                                                  */
+int32_t fd_stream_merge_mode(int32_t mode);
 
 /* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every
  * window row's queries rotated (fp16) and the key-tile table.  0 on invalid geometry or

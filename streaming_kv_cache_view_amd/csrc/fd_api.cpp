@@ -33,14 +33,12 @@ int check_geom(const fd_geom* g) {
   return FD_OK;
 }
 
-// Polls of the ready flag of a view cut once, process-wide (fd_merge_wait).  16 polls of ~1,000
-// cycles each (~8 us at 2 GHz): the second piece is the first job of its workgroup, so its flag is
-// normally set long before the first piece (the last job of another workgroup) finishes.
-std::atomic<int32_t> g_merge_polls{16};
+// How the streaming calls merge a view cut once, process-wide (fd_stream_merge_mode)
+std::atomic<int32_t> g_merge_mode{1};
 
 fd::KParams make_params(const fd_geom* g, int64_t t) {
   fd::KParams p{};
-  p.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
+  p.merge_mode = g_merge_mode.load(std::memory_order_relaxed);
   p.V = g->n_views;
   p.F = g->n_frames;
   p.T = g->tok_per_frame;
@@ -227,9 +225,9 @@ int fd_stream_attn_insert(const fd_geom* g, const void* k_new, const void* v_new
                            v_new);
 }
 
-int32_t fd_merge_wait(int32_t polls) {
-  if (polls < 0 || polls > 1024) return g_merge_polls.load(std::memory_order_relaxed);
-  return g_merge_polls.exchange(polls, std::memory_order_relaxed);
+int32_t fd_stream_merge_mode(int32_t mode) {
+  if (mode < 0 || mode > 2) return g_merge_mode.load(std::memory_order_relaxed);
+  return g_merge_mode.exchange(mode, std::memory_order_relaxed);
 }
 
 int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame) {

@@ -44,8 +44,9 @@ struct KParams {
   // reasoning rows and block rows sit in cache rows W + d*tail_stride + [0, n_tails[d] + B).
   int32_t rot_new;    // rotation pass: 1 -> only the prefix rows and the newest slot of every view
                       //   (a persistent key view whose older frames were rotated by earlier calls)
-  int32_t merge_polls;   // streaming attention: polls of a ready flag before the first piece of a view
-                         //   cut once leaves the merge to the merge kernel (0: always leaves it)
+  int32_t merge_mode;   // streaming attention, a view cut once (split between two workgroups): 1 ->
+                        //   merged by whichever piece finishes second; 0 -> by the merge kernel;
+                        //   2 -> as 1 with the second piece made to finish second (tests)
   int32_t n_tail, B, nblk, n_split;   // n_tail: draft 0's; nblk: key blocks of the longest key list;
                                       // n_split: partial slots per (kv head, row block)
   int32_t n_ws, n_ts;   // bf16 path: units over the window's blocks, and per draft over its tail
@@ -126,10 +127,9 @@ inline size_t stream_tiles_bytes(int qmode, int P, int T, int V, int F) {
 // merge descriptors of a streaming call (after the tile table): an int4 per (32*TBW-token
 // block, chunk boundary)
 inline size_t stream_merge_desc_bytes(int nqb, int V) { return align256(size_t(nqb) * (V > 1 ? V - 1 : 0) * 16); }
-// merge flags of a streaming call (after the descriptors): per (row block, chunk) the ready flag
-// of the chunk's first piece, then per (row block, boundary) whether the attention kernel merged
-// the view that boundary cuts
-inline size_t stream_flags_bytes(int n_rb, int V) { return V > 1 ? align256(size_t(2) * n_rb * V * 4) : 0; }
+// merge tickets of a streaming call (after the descriptors): a counter per (row block, chunk
+// boundary) taken by the two pieces of the view the boundary cuts once
+inline size_t stream_flags_bytes(int n_rb, int V) { return V > 1 ? align256(size_t(n_rb) * V * 4) : 0; }
 inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
   return size_t(n_rb) * nseg * 2 * stream_partial_words(D) * sizeof(float);
 }

@@ -519,11 +519,12 @@ __host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
 // the longest jobs out first and the rest fill in, with no split and no merge.
 struct StreamSplit {
   int nP, tps, ndiag, V, F, ntot, seg0, qmode, vf, whole;
-  __device__ StreamSplit(const KParams& p, int qb) {
+  __host__ __device__ StreamSplit(const KParams& p, int qb) {
     constexpr int TK = kTileKeys;
     nP = (p.P + TK - 1) / TK;
     tps = (p.T + TK - 1) / TK;
-    ndiag = (min(p.qtok, (qb + 1) * 32 * p.TBW) + TK - 1) / TK;
+    const int qend = (qb + 1) * 32 * p.TBW;
+    ndiag = ((p.qtok < qend ? p.qtok : qend) + TK - 1) / TK;
     V = p.nseg;   // segments of this launch: the "views" of a row block
     F = p.F;
     seg0 = p.seg0;
@@ -535,16 +536,16 @@ struct StreamSplit {
   }
   // tiles of segment seg0 + u for this row block (StreamTiles: frame (v, j) of a full window
   // is segment v*F + j, after v*F + j earlier frames)
-  __device__ int view_tiles(int u) const {
+  __host__ __device__ int view_tiles(int u) const {
     const int sg = seg0 + u;
     if (qmode == 0) return nP + (sg * F + F - 1) * tps + ndiag;
     return sg < vf ? nP + sg * tps + ndiag : ndiag;
   }
-  __device__ int order(int oi) const {
+  __host__ __device__ int order(int oi) const {
     if (whole) return V - 1 - oi;
     return (oi & 1) ? oi / 2 : V - 1 - oi / 2;
   }
-  __device__ int bnd(int c) const {
+  __host__ __device__ int bnd(int c) const {
     if (whole) {
       int pos = 0;
       for (int oi = 0; oi < c; ++oi) pos += view_tiles(order(oi));
@@ -557,7 +558,7 @@ struct StreamSplit {
     return a < (int64_t(1) << 53) ? static_cast<int>(static_cast<double>(a) / V) : static_cast<int>(a / V);
   }
   // start of view v in the end-to-end order
-  __device__ int start(int v) const {
+  __host__ __device__ int start(int v) const {
     int pos = 0;
     for (int oi = 0; oi < V; ++oi) {
       const int u = order(oi);
@@ -567,7 +568,7 @@ struct StreamSplit {
     return pos;
   }
   // the chunk holding tile x of the end-to-end order
-  __device__ int chunk_of(int x) const {
+  __host__ __device__ int chunk_of(int x) const {
     int c = 0;
     for (int i = 1; i < V; ++i)
       if (bnd(i) <= x) c = i;
@@ -581,8 +582,9 @@ struct StreamSplit {
 // none): x = the view (-1: nothing to merge), y = its first and last chunks cf | cl << 16,
 // z = the slot of its piece in chunk cf (1: that chunk's last job, 0: its only job), w = the
 // view's first output row.
-__device__ inline int4 stream_merge_desc(const KParams& p, int qb, int cb) {
-  const StreamSplit sp(p, qb);
+// The cut behind it, on the host too: x = the view (-1: none), y = its first chunk, z = its last,
+// w = its first tile in the end-to-end order.
+__host__ __device__ inline int4 stream_cut(const KParams& p, const StreamSplit& sp, int cb) {
   const int x = sp.bnd(cb);
   int v = -1, sv = 0, nv = 0;   // the view holding tile x of the end-to-end order
   for (int oi = 0, pos = 0; oi < sp.V; ++oi) {
@@ -596,8 +598,25 @@ __device__ inline int4 stream_merge_desc(const KParams& p, int qb, int cb) {
     pos += n;
   }
   if (v < 0 || sv == x || sp.chunk_of(sv) != cb - 1) return int4{-1, 0, 0, 0};
-  const int cf = cb - 1, cl = sp.chunk_of(sv + nv - 1);
-  return int4{v, cf | (cl << 16), sv > sp.bnd(cf) ? 1 : 0, StreamTiles(p).qrow0(p, p.seg0 + v)};
+  return int4{v, cb - 1, sp.chunk_of(sv + nv - 1), sv};
+}
+__device__ inline int4 stream_merge_desc(const KParams& p, int qb, int cb) {
+  const StreamSplit sp(p, qb);
+  const int4 c = stream_cut(p, sp, cb);
+  if (c.x < 0) return c;
+  return int4{c.x, c.y | (c.z << 16), c.w > sp.bnd(c.y) ? 1 : 0, StreamTiles(p).qrow0(p, p.seg0 + c.x)};
+}
+// Whether a view of a streaming launch is cut by two or more chunk boundaries: its pieces then go
+// to the merge kernel (a view cut once is merged by the attention kernel).
+inline bool stream_view_cut_twice(const KParams& p) {
+  for (int qb = 0; qb < p.nqb; ++qb) {
+    const StreamSplit sp(p, qb);
+    for (int cb = 1; cb < p.nseg; ++cb) {
+      const int4 c = stream_cut(p, sp, cb);
+      if (c.x >= 0 && c.z > c.y + 1) return true;
+    }
+  }
+  return false;
 }
 
 template <typename T, int D, bool INS>   // INS: the new frames are inserted by this pass (nf)
@@ -632,8 +651,8 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       const int nb = p.nseg - 1;
       for (int e = tid; e < p.nqb * nb; e += 256) mdesc[e] = stream_merge_desc(p, e / nb, e % nb + 1);
     }
-    if (flags)   // the attention kernel's merge flags, cleared for this call
-      for (int e = tid; e < 2 * p.Hkv * p.n_hsub * p.nqb * p.nseg; e += 256) flags[e] = 0u;
+    if (flags)   // the attention kernel's merge tickets, cleared for this call
+      for (int e = tid; e < p.Hkv * p.n_hsub * p.nqb * p.nseg; e += 256) flags[e] = 0u;
     return;
   }
   const int bx = static_cast<int>(blockIdx.x) - (tiles ? 1 : 0);   // rotation workgroup
@@ -1242,9 +1261,13 @@ __device__ inline int partial_row_scale(float mx) {
 // groups of kMergeItems / (HPW*D/4) tokens (all HPW heads) in turn.  Item e (thread tid takes
 // e = tid and tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4))
 // .. +3: a token's heads are adjacent rows of the output, so each store instruction of a wave
-// writes 1 KB (fp32) of contiguous output.  A view cut once is normally merged by the attention
-// kernel (its flag set): the workgroup then only reads the flag, so the launch stays small.
+// writes 1 KB (fp32) of contiguous output.  A view cut once is merged by the attention kernel
+// unless merge_mode is 0; the kernel is launched only when some view is cut more than once or in
+// that mode.
 constexpr int kMergeItems = 512;   // 4-column items per merge workgroup
+// Polls (each then s_sleep 16, ~1,000 cycles) for which the second piece of a view cut once waits
+// for the first piece's ticket in the test mode that makes the second piece merge (merge_mode 2)
+constexpr int kMergeTestPolls = 4096;
 // 4 fp16 values (as stored) to fp32
 __device__ inline f32x4 f16x4_to_f32(u32x2 x) {
   typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -1270,7 +1293,6 @@ __device__ __forceinline__ f32x4 merge_two(float m0, float l0, float s0, u32x2 x
 }
 template <int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const int4* __restrict__ mdesc,
-                                                           const unsigned* __restrict__ flags,
                                                            const float* __restrict__ part, void* __restrict__ out) {
   constexpr int CG = D / 4, NSUB = D / 16, MAXP = 2, IPT = kMergeItems / 256;
   // blockIdx.x = (((c - 1)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head fastest, as in the
@@ -1284,11 +1306,10 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
   const int hsub = bid % p.n_hsub;
   const int cb = bid / p.n_hsub + 1;   // boundary between chunks cb - 1 and cb
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
-  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
-  const unsigned merged = flags[n_rb * p.nseg + rbi * p.nseg + cb];   // merged by the attention kernel
   const int4 dsc = mdesc[qb * (p.nseg - 1) + cb - 1];   // stream_merge_desc
-  if (dsc.x < 0 || merged != 0) return;
+  if (dsc.x < 0) return;
   const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;
+  if (cl == cf + 1 && p.merge_mode != 0) return;   // a view cut once: merged by the attention kernel
   const int per_tok = p.HPW * CG, ntok = kMergeItems / per_tok;
   for (int sub = 0; sub < NSUB; ++sub) {   // the row block's token groups in turn
   int row[IPT], col[IPT];
@@ -1738,80 +1759,48 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS only: the prefetched loads stay in flight
   wg_barrier();
-  // ---- a view cut once (two pieces, stream_merge_desc): its second piece (this chunk's first
-  // job) publishes its partial with device-scope stores and then a ready flag; its first piece
-  // (this chunk's last job, on a workgroup that finishes early) waits a bounded time for that
-  // flag and merges the view here (merge_two), writing its rows; without the flag in time it
-  // leaves its partial for the merge kernel as a split piece does.
-  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
-  int role = 0;   // 1: first piece of a view cut once, 2: its second piece
-  if (!whole && mdesc) {
+  // ---- a view cut once (two pieces, stream_merge_desc) is merged here by whichever of its
+  // pieces finishes second.  Both pieces store their partials with device-scope stores, wait for
+  // them, and take a ticket on the boundary's counter (device-scope atomic add).  The piece that
+  // draws ticket 1 reads the other's stored partial with device-scope loads, quantises its own
+  // rows exactly as it stored them, and merges (merge_two, the first piece's values first), so
+  // the result has the same bits whichever piece merges.  No piece waits for another.  The
+  // second piece is its chunk's first job and the first piece its chunk's last, so it is
+  // normally the first piece, on a workgroup that finishes early, that merges.
+  int role = 0;      // 1: first piece of a view cut once, 2: its second piece
+  int which_a = 0;   // role 2: the first piece's slot in its chunk
+  if (!whole && mdesc && p.merge_mode != 0) {
     if (jb < nv) {
       const int4 d = mdesc[qb * (p.nseg - 1) + chunk];   // boundary chunk + 1
       role = (d.x == v && (d.y >> 16) == chunk + 1) ? 1 : 0;
     } else {
       const int4 d = mdesc[qb * (p.nseg - 1) + chunk - 1];   // boundary chunk (ja > 0 here)
       role = (d.x == v && (d.y & 0xffff) == chunk - 1 && (d.y >> 16) == chunk) ? 2 : 0;
+      which_a = d.z;
     }
-  }
-  bool merge_here = false;
-  if (role == 1) {
-    if (tid == 0) {
-      int rdy = 0;
-      for (int i = 0; i < p.merge_polls && !rdy; ++i) {   // each poll then s_sleep 16 (~1,000 cycles)
-        rdy = __hip_atomic_load(&flags[rbi * p.nseg + chunk + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-        if (!rdy) __builtin_amdgcn_s_sleep(16);
-      }
-      s_ready = rdy;
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    wg_barrier();
-    merge_here = s_ready != 0;
   }
   // ---- rows out, 16 bytes per lane and whole rows per group of lanes.  Row r of the block
   // is token tok0 + 32*((r/32)/HPW) + r%32 of query head kvh*G + hsub*HPW + (r/32)%HPW.
   const float* rows = reinterpret_cast<const float*>(buf);
-  if (merge_here) {   // this piece quantised exactly as its partial would be stored, then merge_two
-    // with the second piece's stored partial (slot 0 of chunk + 1), read with device-scope loads
-    const float* slot_b = stream_slot<D>(part, p, rbi, chunk + 1, 0);
-    constexpr int TPR = D / 8;
-    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
-      const int c = tid % TPR;
-      const float* src = rows + r * (D + 4) + 8 * c;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
-      float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      float mx = 0.f;
+  constexpr int TPQ = D / 8;   // lanes per row of a partial (aligned groups within a wave), 8 values each
+  // row r's 8 values from lane c of its group, scaled by its row's power of two 2^sc (the
+  // largest magnitude over the row's lanes) and rounded to fp16: the stored partial's values
+  auto quant_row = [&](int r, int c, int& sc) -> u32x4 {
+    const float* src = rows + r * (D + 4) + 8 * c;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
+    float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    float mx = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
 #pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const int sc = partial_row_scale(mx);
-      const float mul = exp2_int(sc);
+    for (int o = 1; o < TPQ; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    sc = partial_row_scale(mx);
+    const float mul = exp2_int(sc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x8[e] *= mul;
-      const u32x4 a16 = F16Ops::pack(x8);
-      const uint64_t* bsrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(slot_b) + r * D + 8 * c);
-      const uint64_t* bml = reinterpret_cast<const uint64_t*>(slot_b + 64 * D + 4 * r);
-      const uint64_t b0 = __hip_atomic_load(bsrc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t b1 = __hip_atomic_load(bsrc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t bm = __hip_atomic_load(bml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t bs = __hip_atomic_load(bml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float ma = red_m[r >> 5][r & 31], la = red_l[r >> 5][r & 31], sa = exp2_int(-sc);
-      const float mb2 = __uint_as_float(static_cast<uint32_t>(bm)), lb = __uint_as_float(static_cast<uint32_t>(bm >> 32));
-      const float sb = __uint_as_float(static_cast<uint32_t>(bs));
-      const f32x4 r0 = merge_two(ma, la, sa, u32x2{a16[0], a16[1]}, mb2, lb, sb,
-                                 u32x2{static_cast<uint32_t>(b0), static_cast<uint32_t>(b0 >> 32)});
-      const f32x4 r1 = merge_two(ma, la, sa, u32x2{a16[2], a16[3]}, mb2, lb, sb,
-                                 u32x2{static_cast<uint32_t>(b1), static_cast<uint32_t>(b1 >> 32)});
-      const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-      if (tk >= p.qtok) continue;
-      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-      const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
-      store_out4(out, p.out_bf16, obase, r0);
-      store_out4(out, p.out_bf16, obase + 4, r1);
-    }
-    if (tid == 0) flags[n_rb * p.nseg + rbi * p.nseg + chunk + 1] = 1u;   // read by the merge kernel
-  } else if (whole) {
+    for (int e = 0; e < 8; ++e) x8[e] *= mul;
+    return F16Ops::pack(x8);
+  };
+  if (whole) {
     const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
     for (int r = tid / TPR; r < 128; r += 512 / TPR) {
       const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
@@ -1831,24 +1820,12 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   } else {   // this job's piece of view v: unnormalised O scaled per row and rounded to fp16,
              // then (row max M, row sum l, 1 / scale) (stream_slot)
     float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
-    constexpr int TPR = D / 8;   // lanes per row (aligned groups within a wave), 8 values each
-    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
-      const int c = tid % TPR;
-      const float* src = rows + r * (D + 4) + 8 * c;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
-      float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      float mx = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const int sc = partial_row_scale(mx);
-      const float mul = exp2_int(sc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x8[e] *= mul;
-      const u32x4 pk = F16Ops::pack(x8);
+    for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
+      const int c = tid % TPQ;
+      int sc;
+      const u32x4 pk = quant_row(r, c, sc);
       const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
-      if (role == 2) {   // read by the first piece's workgroup within this launch: device scope
+      if (role != 0) {   // read by the other piece's workgroup within this launch: device scope
         uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c);
         __hip_atomic_store(dst, (static_cast<uint64_t>(pk[1]) << 32) | pk[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(dst + 1, (static_cast<uint64_t>(pk[3]) << 32) | pk[2], __ATOMIC_RELAXED,
@@ -1865,10 +1842,49 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
         if (c == 0) *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = mlv;
       }
     }
-    if (role == 2) {   // every lane's stores complete, then the ready flag
+    if (role != 0) {   // every lane's stores complete, then the ticket
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       wg_barrier();
-      if (tid == 0) __hip_atomic_store(&flags[rbi * p.nseg + chunk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned* cnt = flags + rbi * p.nseg + (role == 1 ? chunk + 1 : chunk);
+      if (tid == 0) {
+        if (role == 2 && p.merge_mode == 2)   // test mode: the second piece lets the first take ticket 0
+          for (int i = 0; i < kMergeTestPolls && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++i)
+            __builtin_amdgcn_s_sleep(16);
+        s_ready = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      wg_barrier();
+      if (s_ready == 1) {   // the other piece's partial is stored: merge the view here
+        const float* other = role == 1 ? stream_slot<D>(part, p, rbi, chunk + 1, 0)
+                                       : stream_slot<D>(part, p, rbi, chunk - 1, which_a);
+        for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
+          const int c = tid % TPQ;
+          int sc;
+          const u32x4 own = quant_row(r, c, sc);
+          const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D + 8 * c);
+          const uint64_t* oml = reinterpret_cast<const uint64_t*>(other + 64 * D + 4 * r);
+          const uint64_t o0 = __hip_atomic_load(osrc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t o1 = __hip_atomic_load(osrc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t om = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t os = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float m_o = __uint_as_float(static_cast<uint32_t>(om)), l_o = __uint_as_float(static_cast<uint32_t>(om >> 32));
+          const float s_o = __uint_as_float(static_cast<uint32_t>(os));
+          const float m_s = red_m[r >> 5][r & 31], l_s = red_l[r >> 5][r & 31], s_s = exp2_int(-sc);
+          const u32x2 x_o0{static_cast<uint32_t>(o0), static_cast<uint32_t>(o0 >> 32)};
+          const u32x2 x_o1{static_cast<uint32_t>(o1), static_cast<uint32_t>(o1 >> 32)};
+          const u32x2 x_s0{own[0], own[1]}, x_s1{own[2], own[3]};
+          const f32x4 r0 = role == 1 ? merge_two(m_s, l_s, s_s, x_s0, m_o, l_o, s_o, x_o0)
+                                     : merge_two(m_o, l_o, s_o, x_o0, m_s, l_s, s_s, x_s0);
+          const f32x4 r1 = role == 1 ? merge_two(m_s, l_s, s_s, x_s1, m_o, l_o, s_o, x_o1)
+                                     : merge_two(m_o, l_o, s_o, x_o1, m_s, l_s, s_s, x_s1);
+          const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
+          if (tk >= p.qtok) continue;
+          const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+          const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
+          store_out4(out, p.out_bf16, obase, r0);
+          store_out4(out, p.out_bf16, obase + 4, r1);
+        }
+      }
     }
   }
   wg_barrier();   // LDS is reused by the next job (this job's output stores drain meanwhile)
@@ -2824,18 +2840,6 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   }
 }
 
-// Compute units of the current device (cached per device; 0 when the runtime cannot say)
-int device_cus() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cus[kMaxDevices] = {};
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    cus[dev].store(n, std::memory_order_relaxed);
-  return n > 0 ? n : 0;
-}
-
 template <typename T, int D>
 int launch_stream_t(const KParams& p, const void* q, const void* kc, const void* vc, void* out, void* ws,
                     hipStream_t st, const void* kn, const void* vn, void* kview) {
@@ -2871,16 +2875,12 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
-    // A first piece waits for its second piece only when every workgroup can be resident at once
-    // (one per CU): with more, the second piece's workgroup may not start until others end.
-    KParams pa = p;
-    if (grid > device_cus()) pa.merge_polls = 0;
-    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pa, static_cast<const QKT*>(qrot),
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles, mdesc, flags);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-    if (p.V > 1)   // a workgroup per (chunk boundary, row block)
+    if (p.V > 1 && (p.merge_mode == 0 || stream_view_cut_twice(p)))   // a workgroup per (chunk boundary, row block)
       hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (grid / p.V)), dim3(256), 0, st, p, mdesc,
-                         flags, part, out);
+                         part, out);
   } else {
     hipLaunchKernelGGL((stream_attn_kernel<T, D>), dim3(grid), dim3(512), 0, st, p, static_cast<const T*>(q),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out);

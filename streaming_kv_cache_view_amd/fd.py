@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.fd_stream_attn_insert_view.argtypes = [G, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp, sz, vp]
         L.fd_stream_attn_insert_view.restype = ctypes.c_int
         L.fd_view_shift.argtypes, L.fd_view_shift.restype = [G, i64], i64
-        L.fd_merge_wait.argtypes, L.fd_merge_wait.restype = [i32], i32
+        L.fd_stream_merge_mode.argtypes, L.fd_stream_merge_mode.restype = [i32], i32
         L.fd_prefill_workspace_bytes.argtypes, L.fd_prefill_workspace_bytes.restype = [G], sz
         L.fd_prefill_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_prefill_attn.restype = ctypes.c_int
@@ -85,7 +85,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_project_insert", "fd_stream_workspace_bytes",
            "fd_stream_attn", "fd_stream_attn_insert", "fd_stream_attn_view", "fd_stream_attn_insert_view",
-           "fd_view_shift", "fd_merge_wait", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
+           "fd_view_shift", "fd_stream_merge_mode", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
            "fd_verify_attn", "fd_verify_batched_workspace_bytes", "fd_verify_attn_batched", "fd_rotate_window",
            "fd_verify_attn_noalloc", "fd_status_str")
 
@@ -200,9 +200,11 @@ def view_shift(g, newest_frame: int) -> int:
     return int(lib().fd_view_shift(ctypes.byref(make_geom(g)), int(newest_frame)))
 
 
-def merge_wait(polls: int = -1) -> int:
-    """Set the streaming calls' merge wait (0..1024 polls) and return the previous count; -1 reads it."""
-    return int(lib().fd_merge_wait(int(polls)))
+def stream_merge_mode(mode: int = -1) -> int:
+    """Set how the streaming calls merge a view split between two workgroups (1: in the attention
+    kernel, 0: merge kernel, 2: in the attention kernel by the second piece) and return the previous
+    mode; -1 reads it."""
+    return int(lib().fd_stream_merge_mode(int(mode)))
 
 
 def prefill_workspace_bytes(g) -> int:

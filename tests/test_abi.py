@@ -112,13 +112,13 @@ def test_call_errors():
     # -> G=2: 2 heads, 64 tokens, one block per kv head; between queries and partials, the
     # attention kernel's tile table (8 bytes per tile of each view's key sequence: view 0 prefix
     # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal), the merge descriptors (16
-    # bytes per token block and chunk boundary: one here) and the merge flags (two 4-byte flags
+    # bytes per token block and chunk boundary: one here) and the merge tickets (a 4-byte counter
     # per row block and chunk)
     krot = g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
     qrot = 2 * 16 * 4 * 64 * 2
     n_rb = g.n_kv_heads * 1 * 1
     align = lambda x: (x + 255) // 256 * 256
-    assert sws == (align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + align(2 * n_rb * 2 * 4)
+    assert sws == (align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + align(n_rb * 2 * 4)
                    + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16))
     assert L.fd_stream_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 4
     assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
@@ -162,14 +162,14 @@ def test_call_errors():
         assert fd.lib().fd_status_str(code).decode() != "unknown status"
 
 
-def test_merge_wait_setting():
-    """fd_merge_wait: default 16 polls; 0..1024 sets and returns the previous count; anything else
-    reads the count and changes nothing."""
+def test_stream_merge_mode_setting():
+    """fd_stream_merge_mode: default 1; 0..2 sets and returns the previous mode; anything else reads
+    the mode and changes nothing."""
     L = fd.lib()
-    assert L.fd_merge_wait(-1) == 16
-    assert L.fd_merge_wait(0) == 16 and L.fd_merge_wait(-1) == 0
-    assert L.fd_merge_wait(1025) == 0 and L.fd_merge_wait(1024) == 0 and L.fd_merge_wait(-5) == 1024
-    assert L.fd_merge_wait(16) == 1024 and fd.merge_wait() == 16
+    assert L.fd_stream_merge_mode(-1) == 1
+    assert L.fd_stream_merge_mode(0) == 1 and L.fd_stream_merge_mode(-1) == 0
+    assert L.fd_stream_merge_mode(3) == 0 and L.fd_stream_merge_mode(2) == 0 and L.fd_stream_merge_mode(-5) == 2
+    assert L.fd_stream_merge_mode(1) == 2 and fd.stream_merge_mode() == 1
 
 
 def test_stream_view_call_errors_and_shift():

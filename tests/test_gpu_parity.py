@@ -238,37 +238,36 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
-# 512 attention workgroups (8 kv heads x 16 token blocks x 4 views), more than the GPU's CUs: the
-# first pieces do not wait for their second pieces there and every split view is merged by the
-# merge kernel
+# 512 attention workgroups (8 kv heads x 16 token blocks x 4 views), more than the GPU's CUs
 MANY_WG = Workload(208, "512 workgroups", Geometry(4, 2, 512, 64, 32, 8, 128, 16, 1e6, dtype=synth.BF16), first_t=2)
 
 
 @pytest.mark.parametrize("w", [synth.CONFIGS[2], synth.CONFIGS[3], synth.CONFIGS[5], MANY_WG],
                          ids=lambda w: w.name)
-def test_merge_in_kernel_or_merge_kernel_same_bits(w):
-    """A view that two workgroups share is merged by its first piece's workgroup when the second
-    piece's ready flag comes in time, else by the merge kernel: with the wait at 0 polls every
-    such view goes to the merge kernel, and the outputs must be the same bits (and match the
-    oracle) as with the default wait."""
+def test_merge_modes_same_bits(w):
+    """A view that two workgroups share is merged in the attention kernel by whichever piece
+    finishes second (mode 1, the default), by the second piece (mode 2, which makes it finish
+    second) or by the merge kernel (mode 0): fp32 and bf16 outputs must be the same bits in every
+    mode, and match the oracle."""
     cid = w.cfg_id
     t = w.first_t + 1
     kc, vc = H.window_caches(w, 0, t)
     q = H.q_new(w, 0, t)
-    a = H.stream_out(w, 0, kc, vc, t, q=q)
-    a16 = H.stream_out(w, 0, kc, vc, t, out_dtype="bf16", q=q)
-    prev = fd.merge_wait(0)
+    got = {}
+    prev = fd.stream_merge_mode()
     try:
-        assert fd.merge_wait() == 0
-        b = H.stream_out(w, 0, kc, vc, t, q=q)
-        b16 = H.stream_out(w, 0, kc, vc, t, out_dtype="bf16", q=q)
-        check_stream(w, 0, [t])
+        for mode in (1, 0, 2):
+            assert fd.stream_merge_mode(mode) in (0, 1, 2) and fd.stream_merge_mode() == mode
+            got[mode] = (H.stream_out(w, 0, kc, vc, t, q=q), H.stream_out(w, 0, kc, vc, t, out_dtype="bf16", q=q))
+            if mode != 1:
+                check_stream(w, 0, [t])
     finally:
-        fd.merge_wait(prev)
-    assert fd.merge_wait() == prev
-    H.say(f"cfg {cid} t {t}: in-kernel and merge-kernel outputs equal: fp32 {torch.equal(a, b)}, "
-          f"bf16 {torch.equal(a16, b16)}")
-    assert torch.equal(a, b) and torch.equal(a16, b16)
+        fd.stream_merge_mode(prev)
+    assert fd.stream_merge_mode() == prev
+    for mode in (0, 2):
+        same = torch.equal(got[1][0], got[mode][0]) and torch.equal(got[1][1], got[mode][1])
+        H.say(f"cfg {cid} t {t}: mode {mode} outputs equal to mode 1 (fp32 and bf16): {same}")
+        assert same
 
 
 # ---------------------------------------------------------------------------- verify
