@@ -1233,6 +1233,18 @@ static_assert(StageMap<128>::check() && StageMap<64>::check(), "whole-tile stagi
 // largest magnitude into [2^14, 2^15) (so no row overflows or leaves the normal range, and
 // each value keeps fp16's 11 significant bits), then per row the fp32 (row max m, row sum l,
 // 2^-s, 0).
+// Half offset, within a row of a stored streaming partial, of its 4 values at columns col .. col+3
+// (col a multiple of 4).  The 8 values of lane c of a row's D/8 lanes go out as two 8-byte units,
+// columns 8c .. 8c+3 at unit c and 8c+4 .. 8c+7 at unit D/8 + c, so that each store instruction of
+// a wave writes whole runs of a row (device-scope stores are 8 bytes wide, and a lane's two halves
+// side by side would leave every run half written per instruction).
+template <int D>
+__host__ __device__ constexpr int partial_col(int col) {
+  return 4 * (((col >> 2) & 1) ? D / 8 + (col >> 3) : (col >> 3));
+}
+static_assert(partial_col<128>(0) == 0 && partial_col<128>(4) == 64 && partial_col<128>(8) == 4 &&
+                  partial_col<128>(124) == 124 && partial_col<64>(60) == 60,
+              "partial row layout");
 template <int D>
 __device__ inline float* stream_slot(float* part, const KParams& p, int rbi, int c, int which) {
   return part + (static_cast<int64_t>(rbi * p.nseg + c) * 2 + which) * stream_partial_words(D);
@@ -1333,9 +1345,9 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       ml0[k] = *reinterpret_cast<const f32x4*>(s0 + 64 * D + 4 * row[k]);
-      x0[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s0) + row[k] * D + col[k]);
+      x0[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s0) + row[k] * D + partial_col<D>(col[k]));
       ml1[k] = *reinterpret_cast<const f32x4*>(s1 + 64 * D + 4 * row[k]);
-      x1[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s1) + row[k] * D + col[k]);
+      x1[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(s1) + row[k] * D + partial_col<D>(col[k]));
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k)
@@ -1364,7 +1376,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
 #pragma unroll
       for (int k = 0; k < IPT; ++k) {
         ml[j][k] = *reinterpret_cast<const f32x4*>(sl + 64 * D + 4 * row[k]);
-        xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + col[k]);
+        xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + partial_col<D>(col[k]));
       }
     }
 #pragma unroll
@@ -1825,11 +1837,11 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
       int sc;
       const u32x4 pk = quant_row(r, c, sc);
       const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
+      uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D);   // partial_col
+      const uint64_t lo = (static_cast<uint64_t>(pk[1]) << 32) | pk[0], hi = (static_cast<uint64_t>(pk[3]) << 32) | pk[2];
       if (role != 0) {   // read by the other piece's workgroup within this launch: device scope
-        uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c);
-        __hip_atomic_store(dst, (static_cast<uint64_t>(pk[1]) << 32) | pk[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 1, (static_cast<uint64_t>(pk[3]) << 32) | pk[2], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + c, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + TPQ + c, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (c == 0) {
           uint64_t* mdst = reinterpret_cast<uint64_t*>(slot + 64 * D + 4 * r);
           __hip_atomic_store(mdst, (static_cast<uint64_t>(__float_as_uint(mlv[1])) << 32) | __float_as_uint(mlv[0]),
@@ -1838,7 +1850,8 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
                              __HIP_MEMORY_SCOPE_AGENT);
         }
       } else {
-        st16(reinterpret_cast<_Float16*>(slot) + r * D + 8 * c, pk);
+        dst[c] = lo;
+        dst[TPQ + c] = hi;
         if (c == 0) *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = mlv;
       }
     }
@@ -1861,10 +1874,10 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
           const int c = tid % TPQ;
           int sc;
           const u32x4 own = quant_row(r, c, sc);
-          const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D + 8 * c);
+          const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D);
           const uint64_t* oml = reinterpret_cast<const uint64_t*>(other + 64 * D + 4 * r);
-          const uint64_t o0 = __hip_atomic_load(osrc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t o1 = __hip_atomic_load(osrc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t o0 = __hip_atomic_load(osrc + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // partial_col
+          const uint64_t o1 = __hip_atomic_load(osrc + TPQ + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const uint64_t om = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const uint64_t os = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const float m_o = __uint_as_float(static_cast<uint32_t>(om)), l_o = __uint_as_float(static_cast<uint32_t>(om >> 32));
