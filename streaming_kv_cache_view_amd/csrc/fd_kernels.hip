@@ -11,8 +11,11 @@
 //  stream_pp_kernel    (bf16) attention of the new frame's tokens over the view-major window,
 //                      two wave groups in MFMA / softmax ping-pong; the streaming mask is
 //                      generated from the view / slot / token indices, never loaded.  The
-//                      views of a block of query rows are balanced across workgroups.
-//  stream_merge_kernel (bf16) fixed-order merge of the views split between workgroups.
+//                      views of a block of query rows are balanced across workgroups, and
+//                      a view split between two of them is merged by the one that
+//                      finishes second.  stream_pp2_kernel runs a cold start's frame and
+//                      prefix segments in one launch.
+//  stream_merge_kernel (bf16) fixed-order merge of views split more than once.
 //  stream_attn_kernel  (fp32) the same attention, both groups in the same phase.
 //  kv_project_kernel   (bf16) K/V projection of the new frames (MFMA GEMM) whose epilogue
 //                      writes them, pre-RoPE, into the ring slot (Technical Summary,
@@ -1429,11 +1432,11 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
 // piece goes to its partial slot for stream_merge_kernel.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
-                                                        const _Float16* __restrict__ krot,
-                                                        const bf16* __restrict__ vc, void* __restrict__ out,
-                                                        float* __restrict__ part, const int2* __restrict__ tiles,
-                                                        const int4* __restrict__ mdesc, unsigned* __restrict__ flags) {
+__device__ __forceinline__ void stream_pp_body(const KParams& p, const int block, const _Float16* __restrict__ qrot,
+                                               const _Float16* __restrict__ krot, const bf16* __restrict__ vc,
+                                               void* __restrict__ out, float* __restrict__ part,
+                                               const int2* __restrict__ tiles, const int4* __restrict__ mdesc,
+                                               unsigned* __restrict__ flags) {
   using QK = F16Ops;
   using PV = BF16Ops;
   constexpr int E = 8;                           // 16-bit elements per 16-byte chunk
@@ -1465,7 +1468,7 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   const int tid0 = threadIdx.x;
   // wave-uniform values in scalar registers (the index arithmetic of staging and masking)
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-  int bid = blockIdx.x;
+  int bid = block;
   const int kvh = bid % p.Hkv;
   bid /= p.Hkv;
   const int hsub = bid % p.n_hsub;
@@ -1902,6 +1905,34 @@ __global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _
   }
   wg_barrier();   // LDS is reused by the next job (this job's output stores drain meanwhile)
   }   // jobs
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void stream_pp_kernel(const KParams p, const _Float16* __restrict__ qrot,
+                                                        const _Float16* __restrict__ krot,
+                                                        const bf16* __restrict__ vc, void* __restrict__ out,
+                                                        float* __restrict__ part, const int2* __restrict__ tiles,
+                                                        const int4* __restrict__ mdesc, unsigned* __restrict__ flags) {
+  stream_pp_body<D>(p, blockIdx.x, qrot, krot, vc, out, part, tiles, mdesc, flags);
+}
+
+// Two launches of the attention kernel in one, for a cold start: workgroups [0, n0) run the frame
+// segments (p0), the rest the prefix segment (p1).  The prefix's short jobs come last, after the
+// frames' longest-first order (and longest first among themselves), and fill the tail of that
+// launch instead of a launch of their own on half the CUs.
+template <int D>
+__global__ __launch_bounds__(512) void stream_pp2_kernel(const KParams p0, const KParams p1, const int n0,
+                                                         const _Float16* __restrict__ qrot,
+                                                         const _Float16* __restrict__ krot,
+                                                         const bf16* __restrict__ vc, void* __restrict__ out,
+                                                         const int2* __restrict__ tiles) {
+  const int b = blockIdx.x;
+  if (b < n0) {
+    stream_pp_body<D>(p0, b, qrot, krot, vc, out, nullptr, tiles, nullptr, nullptr);
+  } else {   // the prefix's row blocks last token block first: the longest key ranges start first
+    const int hb = p1.Hkv * p1.n_hsub, bp = b - n0;
+    stream_pp_body<D>(p1, (p1.nqb - 1 - bp / hb) * hb + bp % hb, qrot, krot, vc, out, nullptr, tiles, nullptr, nullptr);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -2925,19 +2956,19 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   pf.nqb = ceil_div(p.T, 32 * p.TBW);
   pf.whole = 1;
   const int grid = pf.Hkv * pf.n_hsub * pf.nqb * pf.nseg;
-  hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pf, static_cast<const QKT*>(qrot),
-                     static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, nullptr, tiles, nullptr, nullptr);
-  if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   if (p.P > 0) {
-    KParams pp = p;   // the prefix segment
+    KParams pp = p;   // the prefix segment, in the same launch after the frames
     pp.seg0 = p.V * p.F;
     pp.nseg = 1;
     pp.qtok = p.P;
     pp.nqb = ceil_div(p.P, 32 * p.TBW);
     pp.whole = 1;
-    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(pp.Hkv * pp.n_hsub * pp.nqb), dim3(512), 0, st, pp,
-                       static_cast<const QKT*>(qrot), static_cast<const QKT*>(krot), static_cast<const bf16*>(vc),
-                       out, nullptr, tiles, nullptr, nullptr);
+    hipLaunchKernelGGL((stream_pp2_kernel<D>), dim3(grid + pp.Hkv * pp.n_hsub * pp.nqb), dim3(512), 0, st, pf, pp, grid,
+                       static_cast<const QKT*>(qrot), static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out,
+                       tiles);
+  } else {
+    hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, pf, static_cast<const QKT*>(qrot),
+                       static_cast<const QKT*>(krot), static_cast<const bf16*>(vc), out, nullptr, tiles, nullptr, nullptr);
   }
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
