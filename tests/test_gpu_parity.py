@@ -270,6 +270,30 @@ def test_merge_modes_same_bits(w):
         assert same
 
 
+def test_merge_in_kernel_repeat_bit_identical():
+    """The in-kernel merge of split views over many calls: 12 config-3 layers (two ring phases each)
+    and 6 config-5 windows, every output of the default mode the same bits as the merge kernel's
+    (mode 0) on the same inputs."""
+    prev = fd.stream_merge_mode()
+    n = 0
+    try:
+        for cid, layers, ts in ((3, range(12), (4, 5)), (5, range(2), (8, 9, 10))):
+            w = synth.CONFIGS[cid]
+            for layer in layers:
+                for t in ts:
+                    kc, vc = H.window_caches(w, layer, t)
+                    q = H.q_new(w, layer, t)
+                    fd.stream_merge_mode(1)
+                    a = H.stream_out(w, layer, kc, vc, t, q=q)
+                    fd.stream_merge_mode(0)
+                    b = H.stream_out(w, layer, kc, vc, t, q=q)
+                    assert torch.equal(a, b), (cid, layer, t)
+                    n += 1
+    finally:
+        fd.stream_merge_mode(prev)
+    H.say(f"{n} calls: in-kernel merge bit-identical to the merge kernel")
+
+
 # ---------------------------------------------------------------------------- verify
 def check_verify(w, layer, t, n_tail, blk_len, out_dtype="f32"):
     g = w.geom
