@@ -480,7 +480,7 @@ __device__ inline int64_t row_pos(const KParams& p, int x) {
 }
 
 constexpr int kRopeQTok = 32;   // tokens per query workgroup of the rotation pass
-constexpr int kRopeHeads = 4;   // kv heads per key workgroup of the rotation pass (sharing angles)
+constexpr int kRopeHeads = 2;   // kv heads per key workgroup of the rotation pass (sharing angles)
 // key rows of the rotation pass: every window row, or with rot_new only the prefix and the newest
 // ring slot of every view (rope_row)
 __host__ __device__ inline int rope_rows(const KParams& p) { return p.rot_new ? p.P + p.V * p.T : p.W; }
