@@ -1781,7 +1781,9 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
   // rows exactly as it stored them, and merges (merge_two, the first piece's values first), so
   // the result has the same bits whichever piece merges.  No piece waits for another.  The
   // second piece is its chunk's first job and the first piece its chunk's last, so it is
-  // normally the first piece, on a workgroup that finishes early, that merges.
+  // normally the first piece, on a workgroup that finishes early, that merges; it reads the
+  // counter first, and when the second piece's ticket is already there it merges at once
+  // without storing its own partial (nobody would read it).
   int role = 0;      // 1: first piece of a view cut once, 2: its second piece
   int which_a = 0;   // role 2: the first piece's slot in its chunk
   if (!whole && mdesc && p.merge_mode != 0) {
@@ -1834,72 +1836,82 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     }
   } else {   // this job's piece of view v: unnormalised O scaled per row and rounded to fp16,
              // then (row max M, row sum l, 1 / scale) (stream_slot)
-    float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
-    for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
-      const int c = tid % TPQ;
-      int sc;
-      const u32x4 pk = quant_row(r, c, sc);
-      const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
-      uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D);   // partial_col
-      const uint64_t lo = (static_cast<uint64_t>(pk[1]) << 32) | pk[0], hi = (static_cast<uint64_t>(pk[3]) << 32) | pk[2];
-      if (role != 0) {   // read by the other piece's workgroup within this launch: device scope
-        __hip_atomic_store(dst + c, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + TPQ + c, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (c == 0) {
-          uint64_t* mdst = reinterpret_cast<uint64_t*>(slot + 64 * D + 4 * r);
-          __hip_atomic_store(mdst, (static_cast<uint64_t>(__float_as_uint(mlv[1])) << 32) | __float_as_uint(mlv[0]),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(mdst + 1, static_cast<uint64_t>(__float_as_uint(mlv[2])), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else {
-        dst[c] = lo;
-        dst[TPQ + c] = hi;
-        if (c == 0) *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = mlv;
-      }
-    }
-    if (role != 0) {   // every lane's stores complete, then the ticket
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      wg_barrier();
-      unsigned* cnt = flags + rbi * p.nseg + (role == 1 ? chunk + 1 : chunk);
-      if (tid == 0) {
-        if (role == 2 && p.merge_mode == 2)   // test mode: the second piece lets the first take ticket 0
-          for (int i = 0; i < kMergeTestPolls && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++i)
-            __builtin_amdgcn_s_sleep(16);
-        s_ready = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      }
+    unsigned* const cnt = role != 0 ? flags + rbi * p.nseg + (role == 1 ? chunk + 1 : chunk) : nullptr;
+    bool merge_now = false;   // merge the view here, from this piece's rows and the other's partial
+    if (role == 1) {   // a first piece whose second piece has taken its ticket merges at once, storing nothing
+      if (tid == 0) s_ready = static_cast<int>(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       wg_barrier();
-      if (s_ready == 1) {   // the other piece's partial is stored: merge the view here
-        const float* other = role == 1 ? stream_slot<D>(part, p, rbi, chunk + 1, 0)
-                                       : stream_slot<D>(part, p, rbi, chunk - 1, which_a);
-        for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
-          const int c = tid % TPQ;
-          int sc;
-          const u32x4 own = quant_row(r, c, sc);
-          const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D);
-          const uint64_t* oml = reinterpret_cast<const uint64_t*>(other + 64 * D + 4 * r);
-          const uint64_t o0 = __hip_atomic_load(osrc + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // partial_col
-          const uint64_t o1 = __hip_atomic_load(osrc + TPQ + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t om = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t os = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const float m_o = __uint_as_float(static_cast<uint32_t>(om)), l_o = __uint_as_float(static_cast<uint32_t>(om >> 32));
-          const float s_o = __uint_as_float(static_cast<uint32_t>(os));
-          const float m_s = red_m[r >> 5][r & 31], l_s = red_l[r >> 5][r & 31], s_s = exp2_int(-sc);
-          const u32x2 x_o0{static_cast<uint32_t>(o0), static_cast<uint32_t>(o0 >> 32)};
-          const u32x2 x_o1{static_cast<uint32_t>(o1), static_cast<uint32_t>(o1 >> 32)};
-          const u32x2 x_s0{own[0], own[1]}, x_s1{own[2], own[3]};
-          const f32x4 r0 = role == 1 ? merge_two(m_s, l_s, s_s, x_s0, m_o, l_o, s_o, x_o0)
-                                     : merge_two(m_o, l_o, s_o, x_o0, m_s, l_s, s_s, x_s0);
-          const f32x4 r1 = role == 1 ? merge_two(m_s, l_s, s_s, x_s1, m_o, l_o, s_o, x_o1)
-                                     : merge_two(m_o, l_o, s_o, x_o1, m_s, l_s, s_s, x_s1);
-          const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-          if (tk >= p.qtok) continue;
-          const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-          const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
-          store_out4(out, p.out_bf16, obase, r0);
-          store_out4(out, p.out_bf16, obase + 4, r1);
+      merge_now = s_ready != 0;
+    }
+    if (!merge_now) {
+      float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
+      for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
+        const int c = tid % TPQ;
+        int sc;
+        const u32x4 pk = quant_row(r, c, sc);
+        const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
+        uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D);   // partial_col
+        const uint64_t lo = (static_cast<uint64_t>(pk[1]) << 32) | pk[0], hi = (static_cast<uint64_t>(pk[3]) << 32) | pk[2];
+        if (role != 0) {   // read by the other piece's workgroup within this launch: device scope
+          __hip_atomic_store(dst + c, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(dst + TPQ + c, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (c == 0) {
+            uint64_t* mdst = reinterpret_cast<uint64_t*>(slot + 64 * D + 4 * r);
+            __hip_atomic_store(mdst, (static_cast<uint64_t>(__float_as_uint(mlv[1])) << 32) | __float_as_uint(mlv[0]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mdst + 1, static_cast<uint64_t>(__float_as_uint(mlv[2])), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        } else {
+          dst[c] = lo;
+          dst[TPQ + c] = hi;
+          if (c == 0) *reinterpret_cast<f32x4*>(slot + 64 * D + 4 * r) = mlv;
         }
+      }
+      if (role != 0) {   // every lane's stores complete, then the ticket
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        wg_barrier();
+        if (tid == 0) {
+          if (role == 2 && p.merge_mode == 2)   // test mode: the second piece lets the first take ticket 0
+            for (int i = 0; i < kMergeTestPolls && __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++i)
+              __builtin_amdgcn_s_sleep(16);
+          s_ready = static_cast<int>(__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        wg_barrier();
+        merge_now = s_ready == 1;   // the other piece's partial is stored
+      }
+    }
+    if (merge_now) {
+      const float* other = role == 1 ? stream_slot<D>(part, p, rbi, chunk + 1, 0)
+                                     : stream_slot<D>(part, p, rbi, chunk - 1, which_a);
+      for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
+        const int c = tid % TPQ;
+        int sc;
+        const u32x4 own = quant_row(r, c, sc);
+        const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D);
+        const uint64_t* oml = reinterpret_cast<const uint64_t*>(other + 64 * D + 4 * r);
+        const uint64_t o0 = __hip_atomic_load(osrc + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // partial_col
+        const uint64_t o1 = __hip_atomic_load(osrc + TPQ + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t om = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t os = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float m_o = __uint_as_float(static_cast<uint32_t>(om)), l_o = __uint_as_float(static_cast<uint32_t>(om >> 32));
+        const float s_o = __uint_as_float(static_cast<uint32_t>(os));
+        const float m_s = red_m[r >> 5][r & 31], l_s = red_l[r >> 5][r & 31], s_s = exp2_int(-sc);
+        const u32x2 x_o0{static_cast<uint32_t>(o0), static_cast<uint32_t>(o0 >> 32)};
+        const u32x2 x_o1{static_cast<uint32_t>(o1), static_cast<uint32_t>(o1 >> 32)};
+        const u32x2 x_s0{own[0], own[1]}, x_s1{own[2], own[3]};
+        const f32x4 r0 = role == 1 ? merge_two(m_s, l_s, s_s, x_s0, m_o, l_o, s_o, x_o0)
+                                   : merge_two(m_o, l_o, s_o, x_o0, m_s, l_s, s_s, x_s0);
+        const f32x4 r1 = role == 1 ? merge_two(m_s, l_s, s_s, x_s1, m_o, l_o, s_o, x_o1)
+                                   : merge_two(m_o, l_o, s_o, x_o1, m_s, l_s, s_s, x_s1);
+        const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
+        if (tk >= p.qtok) continue;
+        const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+        const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
+        store_out4(out, p.out_bf16, obase, r0);
+        store_out4(out, p.out_bf16, obase + 4, r1);
       }
     }
   }
