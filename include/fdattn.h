@@ -230,8 +230,9 @@ int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame);
 
 /* How the bf16 streaming calls (fd_stream_attn and its insert / view forms) merge a view whose
  * key range two workgroups share, for tests and tuning.  1 (default): by the workgroup of
- * whichever piece finishes second (both pieces store their partials and take a ticket; no
- * workgroup waits for another); 0: by a separate merge kernel; 2: as 1, with the second piece's
+ * whichever piece finishes second (a piece stores its partial and takes a ticket unless the
+ * other's ticket is already there; no workgroup waits for another); 0: by a separate merge
+ * kernel; 2: as 1, with the second piece's
  * workgroup waiting a bounded time for the first piece's ticket so that it is the second piece
  * that merges (tests).  Every mode gives the same bits.  Views cut more than once always go to
  * the merge kernel.  Sets the mode, process-wide, for calls made after it when 0 <= mode <= 2
