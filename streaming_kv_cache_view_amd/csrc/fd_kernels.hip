@@ -1784,6 +1784,13 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
   // normally the first piece, on a workgroup that finishes early, that merges; it reads the
   // counter first, and when the second piece's ticket is already there it merges at once
   // without storing its own partial (nobody would read it).
+  // Ordering: every access the two workgroups share is a relaxed device-scope atomic (8-byte
+  // stores and loads of the partial, the counter's add and load), which the hardware performs
+  // at device coherence (written through past the XCD's L2, read from there).  A piece takes its
+  // ticket only after s_waitcnt vmcnt(0) on every wave and a barrier, i.e. after all its partial
+  // stores have completed, and the merging piece issues its loads of the other's partial only
+  // after the counter value it read has returned.  So the merger reads complete data without a
+  // release / acquire fence, which at device scope would write back or invalidate the whole L2.
   int role = 0;      // 1: first piece of a view cut once, 2: its second piece
   int which_a = 0;   // role 2: the first piece's slot in its chunk
   if (!whole && mdesc && p.merge_mode != 0) {
