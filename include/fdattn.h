@@ -232,12 +232,11 @@ int64_t fd_view_shift(const fd_geom* g, int64_t newest_frame);
  * key range two workgroups share, for tests and tuning.  1 (default): by the workgroup of
  * whichever piece finishes second (a piece stores its partial and takes a ticket unless the
  * other's ticket is already there; no workgroup waits for another); 0: by a separate merge
- * kernel; 2: as 1, with the second piece's
- * workgroup waiting a bounded time for the first piece's ticket so that it is the second piece
- * that merges (tests).  Every mode gives the same bits.  Views cut more than once always go to
- * the merge kernel.  Sets the mode, process-wide, for calls made after it when 0 <= mode <= 2
- * and returns the mode in force before the call; any other value (say -1) changes nothing and
- * returns the present mode.                                                                  */
+ * kernel; 2: as 1, with the second piece's workgroup waiting a bounded time for the first
+ * piece's ticket so that it is the second piece that merges (tests).  Every mode gives the same
+ * bits (the work split never cuts a view twice).  Sets the mode, process-wide, for calls made
+ * after it when 0 <= mode <= 2 and returns the mode in force before the call; any other value
+ * (say -1) changes nothing and returns the present mode. */
 int32_t fd_stream_merge_mode(int32_t mode);
 
 /* Bytes of workspace fd_prefill_attn needs (bf16 inputs): the window's keys and every

@@ -580,9 +580,9 @@ struct StreamSplit {
 };
 
 // Merge descriptor of chunk boundary cb (1 <= cb < nseg) of the row blocks of token block qb,
-// written by the rotation pass: the view that boundary cuts first, if cb is the first boundary
-// inside it (a view longer than a chunk is cut by several; a boundary at a view's start cuts
-// none): x = the view (-1: nothing to merge), y = its first and last chunks cf | cl << 16,
+// written by the rotation pass: the view that boundary cuts, if cb is the first boundary inside
+// it (a boundary at a view's start cuts none; no view is cut twice, stream_merge_kernel):
+// x = the view (-1: nothing to merge), y = its first and last chunks cf | cl << 16,
 // z = the slot of its piece in chunk cf (1: that chunk's last job, 0: its only job), w = the
 // view's first output row.
 // The cut behind it, on the host too: x = the view (-1: none), y = its first chunk, z = its last,
@@ -609,8 +609,8 @@ __device__ inline int4 stream_merge_desc(const KParams& p, int qb, int cb) {
   if (c.x < 0) return c;
   return int4{c.x, c.y | (c.z << 16), c.w > sp.bnd(c.y) ? 1 : 0, StreamTiles(p).qrow0(p, p.seg0 + c.x)};
 }
-// Whether a view of a streaming launch is cut by two or more chunk boundaries: its pieces then go
-// to the merge kernel (a view cut once is merged by the attention kernel).
+// Whether a view of a streaming launch is cut by two or more chunk boundaries, which the split
+// never does (stream_merge_kernel); a launch that found one would be refused.
 inline bool stream_view_cut_twice(const KParams& p) {
   for (int qb = 0; qb < p.nqb; ++qb) {
     const StreamSplit sp(p, qb);
@@ -1262,23 +1262,21 @@ __device__ inline int partial_row_scale(float mx) {
   return min(max(141 - e_bits, -126), 126);
 }
 
-// Merge of the segments (views) whose tiles were split between chunks.  Chunk boundary c
-// (between chunks c - 1 and c, c = 1..V-1) cuts at most one view; the workgroups of boundary
-// c merge that view if c is the first boundary inside it (a view longer than a chunk is cut
-// by several), as the rotation pass's descriptor for (token block, c) records
-// (stream_merge_desc: the split is worked out once per call, not in every workgroup).  For
-// its pieces in chunks cf..cl (in that order): O = sum_i 2^(m_i - M) O_i /
-// sum_i 2^(m_i - M) l_i with M = max_i m_i (the online-softmax merge of disjoint key sets),
-// taken in batches of 2 pieces whose loads are all in flight together; piece i's O_i is its
-// stored fp16 row times its 2^-s.  Segments held whole by one chunk were written by the
-// attention kernel.
+// Merge of the views whose tiles were split between two chunks, by a separate kernel (merge mode
+// 0; otherwise the attention kernel merges them itself).  No view is cut more than once: for a
+// row block, view u has a + b*u tiles, and the order V-1, 0, V-2, 1, ... pairs views whose tiles
+// sum to exactly two chunks, so a pair starts and ends on chunk boundaries, its long view
+// (longer than one chunk, shorter than two) is cut once and its short view is whole; with V odd
+// the middle view is one chunk exactly.  The host checks this (stream_view_cut_twice) before
+// every streaming launch.  Chunk boundary c (between chunks c - 1 and c) cuts at most one view,
+// as the rotation pass's descriptor for (token block, c) records (stream_merge_desc); its two
+// pieces combine by merge_two, the function the attention kernel's own merge calls, so the two
+// give the same bits.
 // Workgroup = 256 threads over one (boundary, row block), which takes the row block's D/16
 // groups of kMergeItems / (HPW*D/4) tokens (all HPW heads) in turn.  Item e (thread tid takes
 // e = tid and tid + 256) is token e / (HPW*D/4), head (e / (D/4)) % HPW, columns 4*(e % (D/4))
 // .. +3: a token's heads are adjacent rows of the output, so each store instruction of a wave
-// writes 1 KB (fp32) of contiguous output.  A view cut once is merged by the attention kernel
-// unless merge_mode is 0; the kernel is launched only when some view is cut more than once or in
-// that mode.
+// writes 1 KB (fp32) of contiguous output.
 constexpr int kMergeItems = 512;   // 4-column items per merge workgroup
 // Polls (each then s_sleep 16, ~1,000 cycles) for which the second piece of a view cut once waits
 // for the first piece's ticket in the test mode that makes the second piece merge (merge_mode 2)
@@ -1309,7 +1307,7 @@ __device__ __forceinline__ f32x4 merge_two(float m0, float l0, float s0, u32x2 x
 template <int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, const int4* __restrict__ mdesc,
                                                            const float* __restrict__ part, void* __restrict__ out) {
-  constexpr int CG = D / 4, NSUB = D / 16, MAXP = 2, IPT = kMergeItems / 256;
+  constexpr int CG = D / 4, NSUB = D / 16, IPT = kMergeItems / 256;
   // blockIdx.x = (((c - 1)*n_hsub + hsub)*nqb + qb)*Hkv + kvh: the kv head fastest, as in the
   // attention kernel, so (for Hkv a multiple of 8) a row block's partials are merged on the XCD
   // whose L2 they were written through
@@ -1322,9 +1320,8 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
   const int cb = bid / p.n_hsub + 1;   // boundary between chunks cb - 1 and cb
   const int rbi = (kvh * p.n_hsub + hsub) * p.nqb + qb;
   const int4 dsc = mdesc[qb * (p.nseg - 1) + cb - 1];   // stream_merge_desc
-  if (dsc.x < 0) return;
-  const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;
-  if (cl == cf + 1 && p.merge_mode != 0) return;   // a view cut once: merged by the attention kernel
+  if (dsc.x < 0) return;   // the boundary cuts no view
+  const int cf = dsc.y & 0xffff, cl = dsc.y >> 16, which_cf = dsc.z, qrow0 = dsc.w;   // cl == cf + 1
   const int per_tok = p.HPW * CG, ntok = kMergeItems / per_tok;
   for (int sub = 0; sub < NSUB; ++sub) {   // the row block's token groups in turn
   int row[IPT], col[IPT];
@@ -1340,7 +1337,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
     live[k] = tok < p.qtok;
     obase[k] = (static_cast<int64_t>(qrow0 + tok) * p.Hq + kvh * p.G + hsub * p.HPW + hl) * D + col[k];
   }
-  if (cl == cf + 1) {   // a view cut once: merge_two, as the attention kernel's own merge
+  {
     const float* s0 = stream_slot<D>(const_cast<float*>(part), p, rbi, cf, which_cf);
     const float* s1 = stream_slot<D>(const_cast<float*>(part), p, rbi, cl, 0);
     f32x4 ml0[IPT], ml1[IPT];
@@ -1357,61 +1354,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
       if (live[k])
         store_out4(out, p.out_bf16, obase[k],
                    merge_two(ml0[k][0], ml0[k][1], ml0[k][2], x0[k], ml1[k][0], ml1[k][1], ml1[k][2], x1[k]));
-    continue;
   }
-  float M[IPT], L[IPT];
-  f32x4 acc[IPT];
-#pragma unroll
-  for (int k = 0; k < IPT; ++k) {
-    M[k] = -INFINITY;
-    L[k] = 0.f;
-    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int c0 = cf; c0 <= cl; c0 += MAXP) {
-    // every load of the batch issued back to back: a chunk past cl re-reads cl's slot and its
-    // piece is dropped below (max -inf), so no branch splits the loads
-    f32x4 ml[MAXP][IPT];
-    u32x2 xv[MAXP][IPT];
-#pragma unroll
-    for (int j = 0; j < MAXP; ++j) {
-      const int c = min(c0 + j, cl);
-      const float* sl = stream_slot<D>(const_cast<float*>(part), p, rbi, c, c == cf ? which_cf : 0);
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        ml[j][k] = *reinterpret_cast<const f32x4*>(sl + 64 * D + 4 * row[k]);
-        xv[j][k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const _Float16*>(sl) + row[k] * D + partial_col<D>(col[k]));
-      }
-    }
-#pragma unroll
-    for (int j = 1; j < MAXP; ++j)
-      if (c0 + j > cl)
-#pragma unroll
-        for (int k = 0; k < IPT; ++k) ml[j][k][0] = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      float Mn = M[k];
-#pragma unroll
-      for (int j = 0; j < MAXP; ++j) Mn = fmaxf(Mn, ml[j][k][0]);
-      const float r = (M[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
-      L[k] *= r;
-      acc[k] *= r;
-#pragma unroll
-      for (int j = 0; j < MAXP; ++j) {   // weight 0 for a dropped piece (no branch: the loads stay put)
-        const float wgt = ml[j][k][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j][k][0] - Mn);
-        L[k] += wgt * ml[j][k][1];
-        const float wo = wgt * ml[j][k][2];
-        const uint32_t lo = xv[j][k][0], hi = xv[j][k][1];
-        acc[k] += wo * f32x4{static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(lo & 0xffff))),
-                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(lo >> 16))),
-                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi & 0xffff))),
-                             static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hi >> 16)))};
-      }
-      M[k] = Mn;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < IPT; ++k)
-    if (live[k]) store_out4(out, p.out_bf16, obase[k], acc[k] * (1.f / L[k]));
   }   // token groups
 }
 
@@ -2929,6 +2872,7 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
   const NewFrame<T> nf{static_cast<const T*>(kn), static_cast<const T*>(vn),
                        kn ? const_cast<T*>(static_cast<const T*>(kc)) : nullptr,
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
+  if (mdesc && stream_view_cut_twice(p)) return FD_ERR_GEOM;   // the split never cuts a view twice
   if (kn)
     hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
                        static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf);
@@ -2941,7 +2885,7 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
     hipLaunchKernelGGL((stream_pp_kernel<D>), dim3(grid), dim3(512), 0, st, p, static_cast<const QKT*>(qrot),
                        static_cast<const QKT*>(krot), static_cast<const T*>(vc), out, part, tiles, mdesc, flags);
     if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
-    if (p.V > 1 && (p.merge_mode == 0 || stream_view_cut_twice(p)))   // a workgroup per (chunk boundary, row block)
+    if (p.V > 1 && p.merge_mode == 0)   // a workgroup per (chunk boundary, row block)
       hipLaunchKernelGGL((stream_merge_kernel<D>), dim3((p.V - 1) * (grid / p.V)), dim3(256), 0, st, p, mdesc,
                          part, out);
   } else {
