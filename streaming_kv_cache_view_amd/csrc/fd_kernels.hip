@@ -208,6 +208,19 @@ __device__ inline void wg_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// Kernel arguments wanted early, loaded together into scalar registers.  A kernel's first read
+// of each 64-byte line of its arguments otherwise waits for that line on its own, between
+// integer work and branches, and a prologue touching five lines paid ~1 us of such waits before
+// its first global load.  Naming one field per line here issues the scalar loads back to back,
+// behind a single wait, and leaves the lines in the scalar cache for the other fields.
+template <typename T>
+__device__ __forceinline__ void sreg_use(const T& x) {
+  asm volatile("" : : "s"(x));
+}
+template <typename... Ts>
+__device__ __forceinline__ void kernarg_early(const Ts&... xs) {
+  (sreg_use(xs), ...);
+}
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
 
@@ -2382,6 +2395,7 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   float2* const ang = reinterpret_cast<float2*>(pbuf);   // ang[i*32 + r] = (cos, sin)(r f_i)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  kernarg_early(p.V, p.B, p.tail_stride, p.log2_theta, qb, part);   // lines 0x00 .. 0xc0, the pointers
   const int kvh = blockIdx.x % p.Hkv, unit = blockIdx.x / p.Hkv;
   const bool tail_unit = unit >= p.n_ws;
   const int dt = tail_unit ? (unit - p.n_ws) / p.n_ts : 0;   // a tail unit's draft
@@ -2389,17 +2403,20 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
   const int slot = tail_unit ? p.n_ws + tsp : unit;           // its partial slot
   const int rb_lo = tail_unit ? dt * p.nrb_d : 0, rb_hi = tail_unit ? rb_lo + p.nrb_d : p.n_rb;
   const int n_wblk = verify_window_blocks(p.P, p.V, p.F, p.T);
-  // block jb of this unit: window block 8u + jb, or tail block 8t + jb of draft dt
+  // block jb of this unit: window block NB*u + jb, or tail block NB*t + jb of draft dt
   auto block = [&](int jb) -> VerifyBlock {
     if (tail_unit) return verify_block(p, dt, n_wblk + NB * tsp + jb);
     const int j = NB * unit + jb;
     return j < n_wblk ? verify_block(p, 0, j) : VerifyBlock{0, 0, p.W, 0};
   };
-  int bmask = 0;   // the unit's blocks that hold keys (a prefix of them)
-#pragma unroll
-  for (int jb = 0; jb < NB; ++jb) bmask |= (block(jb).len > 0 ? 1 : 0) << jb;
-  bmask = uni(bmask);
-  if (bmask == 0) return;   // a tail split past this draft's tail (whole workgroup)
+  // The unit's blocks that hold keys are a prefix of its NB blocks, counted in closed form: every
+  // window block holds keys, and draft dt's tail has ceil((n_tails[dt] + B) / 32) blocks.  (Taking
+  // block(jb).len for each jb instead put five block descriptors, their divisions and a kernel-
+  // argument load with a full wait per block ahead of the first K load: ~2 us of the kernel.)
+  const int nbu = tail_unit ? min(NB, ceil_div(p.n_tails[dt] + p.B, kVerifyBlock) - NB * tsp)
+                            : min(NB, n_wblk - NB * unit);
+  if (nbu <= 0) return;   // a tail split past this draft's tail (whole workgroup)
+  const int bmask = uni((1 << nbu) - 1);
 
   // ---- this wave's block
   const VerifyBlock bk = block(w);
@@ -2769,6 +2786,7 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   constexpr int MAXF = 4;                     // slots folded per thread per pass
   constexpr int CPR = D / 4;                  // 4-column chunks per row
   constexpr int SG = 256 / 32;                // slot groups
+  kernarg_early(p.Hkv, p.B, p.n_tails[0], part);   // lines 0x00, 0x40, 0x80, the pointers
   const int kvh = blockIdx.x % p.Hkv, r = blockIdx.x / p.Hkv;
   const int c = r % CPR, rb = r / CPR;
   const int dft = rb / p.nrb_d;               // draft
