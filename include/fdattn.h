@@ -96,8 +96,9 @@ typedef enum {
 
 /* One layer's geometry.  Constraints checked by every call:
  *   n_views, n_frames, tok_per_frame, n_q_heads, n_kv_heads >= 1; prefix_len, tail_cap >= 0;
- *   n_q_heads % n_kv_heads == 0 and the group G = n_q_heads / n_kv_heads is 1, 2 or a
- *   multiple of 4; head_dim is 64 or 128; rope_theta finite and > 1;
+ *   n_q_heads % n_kv_heads == 0 (any group G = n_q_heads / n_kv_heads; the streaming
+ *   calls take query heads four at a time, so with G > 2 not a multiple of 4 the last four
+ *   of each kv head's group are partly idle); head_dim is 64 or 128; rope_theta finite and > 1;
  *   0 <= pos_base < 2^31; S_cap * head_dim < 2^31.                                         */
 typedef struct fd_geom {
   int32_t n_views;        /* V: camera views                                  */

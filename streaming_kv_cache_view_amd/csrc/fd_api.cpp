@@ -16,8 +16,6 @@ int check_geom(const fd_geom* g) {
       g->n_q_heads < 1 || g->n_kv_heads < 1 || g->tail_cap < 0)
     return FD_ERR_GEOM;
   if (g->n_q_heads % g->n_kv_heads != 0) return FD_ERR_GEOM;
-  const int G = g->n_q_heads / g->n_kv_heads;
-  if (!(G == 1 || G == 2 || G % 4 == 0)) return FD_ERR_GEOM;
   if (g->head_dim != 64 && g->head_dim != 128) return FD_ERR_GEOM;
   if (!std::isfinite(g->rope_theta) || !(g->rope_theta > 1.0)) return FD_ERR_GEOM;
   if (g->pos_base < 0 || g->pos_base >= (int64_t(1) << 31)) return FD_ERR_GEOM;
@@ -51,9 +49,9 @@ fd::KParams make_params(const fd_geom* g, int64_t t) {
   p.S_cap = p.W + g->tail_cap;
   p.s_new = int32_t(t % p.F);
   p.out_bf16 = g->out_dtype == FD_BF16;
-  p.HPW = p.G < 4 ? p.G : 4;
+  p.HPW = p.G <= 2 ? p.G : 4;   // G > 2 not a multiple of 4: the last head subset is ragged
   p.TBW = 4 / p.HPW;
-  p.n_hsub = p.G / p.HPW;
+  p.n_hsub = fd::ceil_div(p.G, p.HPW);
   p.nqb = fd::ceil_div(p.T, 32 * p.TBW);
   p.qmode = 0;   // streaming: one segment per view (its newest frame)
   p.seg0 = 0;

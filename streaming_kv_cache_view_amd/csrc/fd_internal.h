@@ -25,9 +25,10 @@ struct KParams {
   int32_t s_new;      // slot of the newest frame: t mod F
   int32_t out_bf16;   // 1 -> bf16 output, 0 -> fp32
   // streaming kernel work decomposition
-  int32_t HPW;        // query heads per workgroup (min(G, 4))
+  int32_t HPW;        // query heads per workgroup: G if G <= 2, else 4
   int32_t TBW;        // 32-token query blocks per workgroup (4 / HPW)
-  int32_t n_hsub;     // G / HPW
+  int32_t n_hsub;     // ceil(G / HPW): with G > 2 not a multiple of 4 the last subset has G mod 4
+                      // heads, the rows of the others idle
   int32_t nqb;        // ceil(qtok / (32*TBW))
   // query segments of the bf16 attention kernel: a segment is the query tokens of one frame
   // (or of the prefix), with one key-tile sequence

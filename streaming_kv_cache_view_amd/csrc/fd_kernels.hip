@@ -522,7 +522,7 @@ struct NewFrame {
   T* kc;
   T* vc;
 };
-__host__ __device__ constexpr int rope_q_heads(int G) { return G < 4 ? G : 4; }
+__host__ __device__ constexpr int rope_q_heads(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 // Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
 // HPW heads x TBW 32-token blocks of one kv head and head subset).  The launch covers nseg
@@ -859,6 +859,9 @@ __global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const
   const int v = p.V - 1 - bid / p.nqb;
   const int tok0 = qb * 32 * p.TBW;
   const int head = kvh * p.G + hsub * p.HPW + (wr % p.HPW);
+  // the last head subset of a group of G = 4k + r heads (r != 0) holds r heads: the rows of the
+  // others read zero queries and store nothing
+  const bool head_live = hsub * p.HPW + (wr % p.HPW) < p.G;
   const int my_tok = tok0 + 32 * (wr / p.HPW) + l32;
   const int64_t qpos0 = p.pos_base + p.P + static_cast<int64_t>(v * p.F + p.F - 1) * p.T;
   const float sc = p.sm_scale_log2;
@@ -970,10 +973,11 @@ __global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const
       if (RPP > 64 && rq >= 64) continue;
       const int row = 64 * grp + rq;
       const int ww = row >> 5, r = row & 31;
-      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+      const int hl = hsub * p.HPW + (ww % p.HPW);   // head within the kv head's group (>= G: none)
+      const int hd = kvh * p.G + hl;
       const int tk = tok0 + 32 * (ww / p.HPW) + r;
       float x1[E], x2[E];
-      if (tk < p.T) {
+      if (tk < p.T && hl < p.G) {
         const T* src = q + (static_cast<int64_t>(v * p.T + tk) * p.Hq + hd) * D;
         In::unpack(ld16(src + E * kc_), x1);
         In::unpack(ld16(src + H2 + E * kc_), x2);
@@ -1145,7 +1149,7 @@ __global__ __launch_bounds__(512) void stream_attn_kernel(const KParams p, const
     const float a0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - M);
     const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
     const float inv = 1.f / (a0 * l_half + a1 * l1);
-    if (my_tok < p.T) {
+    if (my_tok < p.T && head_live) {
       const int64_t obase = (static_cast<int64_t>(v * p.T + my_tok) * p.Hq + head) * D;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
@@ -1347,7 +1351,7 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const KParams p, cons
     col[k] = 4 * (e % CG);
     row[k] = 32 * (hl + p.HPW * (tr >> 5)) + (tr & 31);   // partial row (ww = row/32: token block, head)
     const int tok = qb * 32 * p.TBW + tr;
-    live[k] = tok < p.qtok;
+    live[k] = tok < p.qtok && hsub * p.HPW + hl < p.G;   // a ragged last head subset: heads past G are none
     obase[k] = (static_cast<int64_t>(qrow0 + tok) * p.Hq + kvh * p.G + hsub * p.HPW + hl) * D + col[k];
   }
   {
@@ -1461,6 +1465,9 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
   const int w = tid >> 6;
   const int grp = w >> 2, wr = w & 3, gt = tid & 255;
   const int head = kvh * p.G + hsub * p.HPW + (wr % p.HPW);
+  // the last head subset of a group of G = 4k + r heads (r != 0) holds r heads: the rows of the
+  // others read zero queries and store nothing
+  const bool head_live = hsub * p.HPW + (wr % p.HPW) < p.G;
   const int my_tok = tok0 + 32 * (wr / p.HPW) + l32;
   // lane constants of the operand reads.  QK A operand: row l32, chunk (2u+h) ^ kswz(l32),
   // at krd0 ^ 32u.  PV A operand: keys 16c+key0 (+8), columns 32d + 16((lane>>4)&1) +
@@ -1522,8 +1529,8 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
   // the lane's query row of the segment whose token 0 is query row r0 (rotated and scaled by the
   // rotation pass)
   auto load_q = [&](int r0) {
-    const bool valid = my_tok < p.qtok;
-    const _Float16* src = qrot + (static_cast<int64_t>(r0 + (valid ? my_tok : 0)) * p.Hq + head) * D + E * h;
+    const bool valid = my_tok < p.qtok && head_live;
+    const _Float16* src = qrot + (static_cast<int64_t>(r0 + (valid ? my_tok : 0)) * p.Hq + (valid ? head : 0)) * D + E * h;
 #pragma unroll
     for (int u = 0; u < NU; ++u) qf[u] = valid ? ld16(src + 2 * E * u) : u32x4{0u, 0u, 0u, 0u};
   };
@@ -1784,7 +1791,7 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
     for (int r = tid / TPR; r < 128; r += 512 / TPR) {
       const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-      if (tk >= p.qtok) continue;
+      if (tk >= p.qtok || hsub * p.HPW + (ww % p.HPW) >= p.G) continue;
       const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
       const int c = tid % TPR;
       const float* src = rows + r * (D + 4);
@@ -1870,7 +1877,7 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
         const f32x4 r1 = role == 1 ? merge_two(m_s, l_s, s_s, x_s1, m_o, l_o, s_o, x_o1)
                                    : merge_two(m_o, l_o, s_o, x_o1, m_s, l_s, s_s, x_s1);
         const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-        if (tk >= p.qtok) continue;
+        if (tk >= p.qtok || hsub * p.HPW + (ww % p.HPW) >= p.G) continue;
         const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
         const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D + 8 * c;
         store_out4(out, p.out_bf16, obase, r0);

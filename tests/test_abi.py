@@ -84,9 +84,22 @@ def _g(**kw):
     return fd.FdGeom(**base)
 
 
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (10, 2), (12, 2), (7, 1)])
+def test_any_gqa_group_accepted(hq, hkv):
+    """Any query-head group G = n_q_heads / n_kv_heads (here 3, 5, 6, 7) is a valid geometry:
+    the streaming calls take query heads four at a time and leave the rest of the last four
+    idle; every workspace query answers."""
+    L = fd.lib()
+    g = _g(n_q_heads=hq, n_kv_heads=hkv)
+    assert L.fd_cache_rows(ctypes.byref(g)) > 0
+    assert L.fd_stream_workspace_bytes(ctypes.byref(g)) > 0
+    assert L.fd_prefill_workspace_bytes(ctypes.byref(g)) > 0
+    assert L.fd_verify_workspace_bytes(ctypes.byref(g), 8) > 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(n_views=0), -2), (dict(n_frames=0), -2), (dict(tok_per_frame=0), -2), (dict(prefix_len=-1), -2),
-    (dict(n_q_heads=3), -2), (dict(n_q_heads=6, n_kv_heads=2), -2), (dict(head_dim=96), -2),
+    (dict(n_q_heads=3), -2), (dict(n_q_heads=7, n_kv_heads=2), -2), (dict(head_dim=96), -2),
     (dict(rope_theta=float("nan")), -2), (dict(rope_theta=1.0), -2), (dict(pos_base=-1), -2),
     (dict(pos_base=1 << 31), -2), (dict(tail_cap=-1), -2), (dict(tok_per_frame=1 << 24), -2),
     (dict(in_dtype=7), -3), (dict(out_dtype=2), -3),

@@ -133,6 +133,11 @@ EXTRA = [
     Workload(205, "F=1 no prefix", Geometry(3, 1, 100, 0, 4, 1, 128, 8, 1e6, dtype=synth.BF16), first_t=2),
     Workload(206, "one view", Geometry(1, 4, 130, 70, 8, 4, 64, 8, 1e4, dtype=synth.F32), first_t=7),
     Workload(207, "G=2 T=1", Geometry(4, 3, 1, 3, 2, 1, 64, 8, 1e4, dtype=synth.F32), first_t=2),
+    # query-head groups that are not 1, 2 or a multiple of 4: the last four-head subset is ragged
+    Workload(209, "G=3", Geometry(2, 3, 40, 12, 6, 2, 128, 16, 1e6, dtype=synth.BF16), first_t=4),
+    Workload(210, "G=5", Geometry(2, 2, 64, 16, 5, 1, 128, 16, 1e6, dtype=synth.BF16), first_t=3),
+    Workload(211, "G=6 D=64", Geometry(3, 2, 33, 8, 6, 1, 64, 24, 1e4, dtype=synth.BF16), first_t=3),
+    Workload(212, "G=7 fp32", Geometry(2, 2, 29, 6, 14, 2, 128, 16, 1e6, dtype=synth.F32), first_t=3),
 ]
 
 
@@ -350,11 +355,21 @@ def test_verify_config4_block16():
     check_verify(w, 7, w.first_t, w.n_tail, 16, out_dtype="bf16")
 
 
-@pytest.mark.parametrize("w", EXTRA[:4], ids=lambda w: w.name)
+GQA_ODD = [w for w in EXTRA if w.cfg_id in (209, 210, 211, 212)]   # G = 3, 5, 6, 7
+
+
+@pytest.mark.parametrize("w", EXTRA[:4] + GQA_ODD, ids=lambda w: w.name)
 def test_verify_edge_geometries(w):
     g = w.geom
     b = max(1, min(32 // (g.n_q_heads // g.n_kv_heads), g.tail_cap))
     check_verify(w, 0, w.first_t, max(0, g.tail_cap - b), b)
+
+
+@pytest.mark.parametrize("w", GQA_ODD, ids=lambda w: w.name)
+def test_verify_gqa_block8(w):
+    """8-token blocks with G = 3, 5, 6, 7: G*8 = 24 .. 56 query rows per kv head, so the rows of
+    the last 32-row block are ragged (rows past G*B idle)."""
+    check_verify(w, 0, w.first_t, w.geom.tail_cap - 8, 8)
 
 
 # ---------------------------------------------------------------------------- batched drafts, rotated view
