@@ -62,9 +62,13 @@
  *   stored key element |x| <= 46000) and every query pair has
  *   sqrt(x^2 + y^2) * log2(e)/sqrt(D) < 65520 (D = 128: |x| <= 3.6e5).  Above
  *   that an element can round to +-inf, depending on the key's or query's
- *   position, and no error is reported: a score that becomes -inf drops its
- *   key silently, one that becomes +inf or NaN (inf * 0, inf - inf) makes the
- *   whole output row NaN.  fp32 inputs have no such bound.
+ *   position: a score that becomes -inf drops its key silently, one that
+ *   becomes +inf or NaN (inf * 0, inf - inf) makes the whole output row NaN.
+ *   The calls run on regardless; the rotation pass of a streaming or prefill
+ *   call records every operand it rounds out of the fp16 range, and
+ *   fd_stream_overflow / fd_prefill_overflow report it afterwards.  (The verify
+ *   calls rotate their reasoning-tail and block keys and their queries
+ *   themselves and record nothing.)  fp32 inputs have no such bound.
  *   fp32 inputs: both products on the fp32 matrix cores.  Outputs are fp32
  *   unless out_dtype is FD_BF16.
  */
@@ -358,6 +362,22 @@ int fd_verify_attn_noalloc(const fd_geom* g, const void* q_blk,
                            void* k_cache, void* v_cache, int64_t newest_frame,
                            int32_t n_tail, int32_t blk_len,
                            void* out, void* hip_stream);
+
+/* Range report of the last streaming (fd_stream_attn*) or prefill call made on a workspace
+ * (Technical Summary, Methodology 1, "Positional Encoding": keys are rotated when used; with
+ * bf16 inputs the rotated keys and queries are rounded to fp16, whose range ends at 65504).
+ *   ws, ws_bytes : that call's workspace (ws_bytes as for the call).
+ *   hip_stream   : the stream the call ran on (nullptr: the null stream); the report is read
+ *                  after the work queued on it, which this call waits for (a host copy of a
+ *                  few KB; no device memory is allocated).
+ *   Returns the number of waves of that call's rotation pass (64 rows x chunk pairs each)
+ *   that rounded a rotated key or query element to +-inf (|x| >= 65520), 0 if none; 0 for
+ *   fp32 inputs (fd_stream_overflow).  Errors: geometry / null / FD_ERR_WORKSPACE when
+ *   ws_bytes is too small or no bf16 call of that kind has completed on the workspace
+ *   (the record's tag is missing), FD_ERR_DTYPE for fd_prefill_overflow with fp32 inputs,
+ *   FD_ERR_HIP if the copy fails.  The report describes the workspace's last call only. */
+int fd_stream_overflow(const fd_geom* g, const void* ws, size_t ws_bytes, void* hip_stream);
+int fd_prefill_overflow(const fd_geom* g, const void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Static description of a status code. */
 const char* fd_status_str(int status);

@@ -3,6 +3,10 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include <hip/hip_runtime.h>
 
 #include "fd_internal.h"
 
@@ -164,19 +168,63 @@ size_t fd_stream_workspace_bytes(const fd_geom* g) {
   const size_t window = size_t(g->prefix_len) + size_t(g->n_views) * g->n_frames * g->tok_per_frame;
   const size_t krot = size_t(g->n_kv_heads) * window * g->head_dim * (g->in_dtype == FD_BF16 ? 2 : 4);
   if (g->in_dtype != FD_BF16) return krot;
+  // rotated keys, queries, tile table, merge descriptors and tickets, partial slots (bf16 only),
+  // then the rotation pass's range report
   const fd::KParams p = make_params(g, g->n_frames - 1);
-  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
-  return fd::align256(krot) + fd::stream_qrot_bytes(p.V * p.T, p.Hq, p.D) +
-         fd::stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + fd::stream_merge_desc_bytes(p.nqb, p.V) +
-         fd::stream_flags_bytes(n_rb, p.V) + fd::stream_partial_bytes(n_rb, p.V, p.D);
+  return fd::stream_report_offset(p) + fd::rope_report_bytes(fd::rope_max_workgroups(p, false));
 }
 
 size_t fd_prefill_workspace_bytes(const fd_geom* g) {
   if (check_geom(g) != FD_OK || g->in_dtype != FD_BF16) return 0;
+  // rotated keys, every window row's queries, tile table (every segment is attended whole by one
+  // workgroup: no partials), then the rotation pass's range report
   const fd::KParams p = make_params(g, g->n_frames - 1);
-  const size_t krot = size_t(p.Hkv) * p.W * p.D * 2;
-  // every segment is attended whole by one workgroup: no partials
-  return fd::align256(krot) + fd::stream_qrot_bytes(p.W, p.Hq, p.D) + fd::stream_tiles_bytes(1, p.P, p.T, p.V, p.F);
+  return fd::prefill_report_offset(p) + fd::rope_report_bytes(fd::rope_max_workgroups(p, true));
+}
+
+namespace {
+
+// The rotation pass's range report at byte `off` of a bf16 workspace: copied to the host on the
+// caller's stream (after the work queued before it), then the waves that left the fp16 range
+// counted.
+int read_rope_report(const void* ws, size_t off, size_t bytes, void* hip_stream) {
+  std::vector<unsigned char> h(bytes);
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (hipMemcpyAsync(h.data(), static_cast<const unsigned char*>(ws) + off, bytes, hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return FD_ERR_HIP;
+  int32_t head[2];
+  std::memcpy(head, h.data(), sizeof(head));
+  if (head[0] != fd::kRopeReportMagic || head[1] < 0 || size_t(fd::kRopeReportHeader) + size_t(head[1]) > bytes)
+    return FD_ERR_WORKSPACE;   // no bf16 call of this kind has completed on the workspace
+  int n = 0;
+  for (int32_t i = 0; i < head[1]; ++i) n += h[fd::kRopeReportHeader + i] != 0;
+  return n;
+}
+
+}  // namespace
+
+int fd_stream_overflow(const fd_geom* g, const void* ws, size_t ws_bytes, void* hip_stream) {
+  const int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (!ws) return FD_ERR_NULL;
+  if (ws_bytes < fd_stream_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  if (g->in_dtype != FD_BF16) return 0;   // fp32 operands: no fp16 rounding
+  const fd::KParams p = make_params(g, g->n_frames - 1);
+  return read_rope_report(ws, fd::stream_report_offset(p), fd::rope_report_bytes(fd::rope_max_workgroups(p, false)),
+                          hip_stream);
+}
+
+int fd_prefill_overflow(const fd_geom* g, const void* ws, size_t ws_bytes, void* hip_stream) {
+  const int st = check_geom(g);
+  if (st != FD_OK) return st;
+  if (g->in_dtype != FD_BF16) return FD_ERR_DTYPE;
+  if (!ws) return FD_ERR_NULL;
+  if (ws_bytes < fd_prefill_workspace_bytes(g)) return FD_ERR_WORKSPACE;
+  const fd::KParams p = make_params(g, g->n_frames - 1);
+  return read_rope_report(ws, fd::prefill_report_offset(p), fd::rope_report_bytes(fd::rope_max_workgroups(p, true)),
+                          hip_stream);
 }
 
 int fd_prefill_attn(const fd_geom* g, const void* q_win, const void* k_cache, const void* v_cache,

@@ -135,6 +135,19 @@ inline size_t stream_partial_bytes(int n_rb, int nseg, int D) {
   return size_t(n_rb) * nseg * 2 * stream_partial_words(D) * sizeof(float);
 }
 
+// Range report of the rotation pass (bf16 streaming and prefill workspaces, after everything
+// else): int32 kRopeReportMagic, int32 slot count n of the last launch, 8 bytes unused, then one
+// byte per wave of that launch (4 per workgroup), nonzero if a rotated operand the wave rounded
+// to fp16 reached |x| >= 65520 (fd_stream_overflow, fd_prefill_overflow).
+constexpr int32_t kRopeReportMagic = 0x564f4446;
+constexpr int kRopeReportHeader = 16;
+inline size_t rope_report_bytes(int max_workgroups) { return align256(kRopeReportHeader + size_t(max_workgroups) * 4); }
+// workgroups of the largest rotation pass a streaming (prefill: full-window) call launches, and
+// the byte offset of the report in the bf16 workspace
+int rope_max_workgroups(const KParams& p, bool prefill);
+size_t stream_report_offset(const KParams& p);
+size_t prefill_report_offset(const KParams& p);
+
 // Static device scratch of fd_verify_attn_noalloc (a file-scope __device__ array, one copy per
 // GPU, held until the process ends): the verify workspace of any call it accepts.
 constexpr size_t kVerifyScratchBytes = FD_VERIFY_SCRATCH_BYTES;

@@ -641,7 +641,8 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
                                                           int nkb, const T* __restrict__ q,
                                                           typename Path<T>::QKT* __restrict__ qrot,
                                                           int2* __restrict__ tiles, int4* __restrict__ mdesc,
-                                                          unsigned* __restrict__ flags, const NewFrame<T> nf) {
+                                                          unsigned* __restrict__ flags, const NewFrame<T> nf,
+                                                          unsigned char* __restrict__ report) {
 #pragma clang fp contract(off)   // every instantiation rounds a rotated row the same way
   using In = typename Path<T>::In;
   using QK = typename Path<T>::QK;
@@ -659,7 +660,21 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
   constexpr int CH = H2 / E;       // threads per row (RoPE chunk pairs)
   constexpr int RPW = 256 / CH;     // key rows per workgroup
   const int tid = threadIdx.x;
+  // Range report (bf16 inputs, report non-null): every wave writes its slot, 1 if a rotated
+  // operand it rounded to fp16 left the fp16 range (|x| >= 65520 rounds to inf), else 0;
+  // workgroup 0 records the slot count of this launch (rope_report)
+  auto report_wave = [&](bool bad) {
+    if (!report) return;
+    const bool any = __ballot(bad ? 1 : 0) != 0ull;
+    if ((tid & 63) == 0) report[kRopeReportHeader + 4 * blockIdx.x + (tid >> 6)] = any ? 1 : 0;
+  };
+  auto out_of_fp16 = [](float x) { return !(fabsf(x) < 65520.f); };
+  if (report && blockIdx.x == 0 && tid == 0) {
+    reinterpret_cast<int32_t*>(report)[0] = kRopeReportMagic;
+    reinterpret_cast<int32_t*>(report)[1] = static_cast<int32_t>(4 * gridDim.x);
+  }
   if (tiles && blockIdx.x == 0) {   // workgroup 0 (with a tile table): the bookkeeping only
+    report_wave(false);
     const StreamTiles tt(p);        // the attention kernel's tile table
     for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
       for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
@@ -680,7 +695,8 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
     const int G = p.G, GH = rope_q_heads(G), NTOK = p.qmode == 0 ? p.V * p.T : p.W;
     const int qb = (bx - nkb) / p.Hkv, hsub = qb % (G / GH), tok0 = (qb / (G / GH)) * kRopeQTok;
     const int tg = tok0 + tl;
-    if (tl >= kRopeQTok || tg >= NTOK) return;
+    bool bad = false;
+    if (tl < kRopeQTok && tg < NTOK) {
     const float sc = p.sm_scale_log2;
     double fr[E];
 #pragma unroll
@@ -712,10 +728,13 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
         const float2 r = rot2(x1[e], x2[e], cs[e]);
         x1[e] = r.x * sc;
         x2[e] = r.y * sc;
+        bad |= out_of_fp16(x1[e]) | out_of_fp16(x2[e]);
       }
       st16(qrot + base + hh * D + E * c, pack_rounded(x1));
       st16(qrot + base + hh * D + H2 + E * c, pack_rounded(x2));
     }
+    }
+    report_wave(bad);
     return;
   }
   // ---- keys: thread (row r, RoPE chunk pair c) of the workgroup's RPW rows, for HG kv heads
@@ -739,6 +758,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
     }
   }
   u32x4 raw[kRopeHeads][2], vraw[kRopeHeads][2];
+  bool kbad = false;
 #pragma unroll
   for (int hh = 0; hh < kRopeHeads; ++hh) {
     const int kvh = hg * kRopeHeads + hh;
@@ -770,6 +790,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       const float2 rr2 = rot2(x1[e], x2[e], cs[e]);
       x1[e] = rr2.x;
       x2[e] = rr2.y;
+      kbad |= out_of_fp16(rr2.x) | out_of_fp16(rr2.y);
     }
     QKT* dst = krot + (static_cast<int64_t>(kvh) * p.W + x) * D;
     st16(dst + E * c, pack_rounded(x1));
@@ -782,6 +803,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
       st16(nf.vc + cdst + H2 + E * c, vraw[hh][1]);
     }
   }
+  report_wave(kbad);
 }
 
 
@@ -2898,12 +2920,15 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                        kn ? const_cast<T*>(static_cast<const T*>(kc)) : nullptr,
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
   if (mdesc && stream_view_cut_twice(p)) return FD_ERR_GEOM;   // the split never cuts a view twice
+  unsigned char* report = b16 ? static_cast<unsigned char*>(ws) + stream_report_offset(p) : nullptr;
   if (kn)
     hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf);
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf,
+                       report);
   else
     hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
-                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf);
+                       static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf,
+                       report);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   const int grid = p.Hkv * p.n_hsub * p.nqb * p.V;   // p.nseg == p.V for a streaming call
   if constexpr (std::is_same<T, bf16>::value) {
@@ -2935,7 +2960,8 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   const int nkb = rope_key_workgroups<bf16, D>(p), nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
   hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(1 + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
                      static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles, nullptr, nullptr,
-                     NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr});
+                     NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr},
+                     static_cast<unsigned char*>(ws) + prefill_report_offset(p));
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
   KParams pf = p;   // the frame segments
   pf.seg0 = 0;
@@ -2996,7 +3022,7 @@ int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStr
   hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nkb), dim3(256), 0, st, p, static_cast<const T*>(kc),
                      static_cast<typename Path<T>::QKT*>(kview), nkb, static_cast<const T*>(nullptr),
                      static_cast<typename Path<T>::QKT*>(nullptr), static_cast<int2*>(nullptr), nullptr, nullptr,
-                     NewFrame<T>{nullptr, nullptr, nullptr, nullptr});
+                     NewFrame<T>{nullptr, nullptr, nullptr, nullptr}, nullptr);
   return hipGetLastError() == hipSuccess ? FD_OK : FD_ERR_HIP;
 }
 
@@ -3006,6 +3032,26 @@ int launch_rotate_window_t(const KParams& p, const void* kc, void* kview, hipStr
 static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
 
 }  // namespace
+
+int rope_max_workgroups(const KParams& p, bool prefill) {
+  KParams q = p;
+  q.rot_new = 0;   // the whole window: the largest key grid
+  const int nkb = p.D == 128 ? rope_key_workgroups<bf16, 128>(q) : rope_key_workgroups<bf16, 64>(q);
+  const int rows = prefill ? p.W : p.V * p.T;
+  return 1 + nkb + ceil_div(rows, kRopeQTok) * (p.G / rope_q_heads(p.G)) * p.Hkv;
+}
+
+size_t stream_report_offset(const KParams& p) {
+  const int n_rb = p.Hkv * p.n_hsub * p.nqb;
+  return align256(size_t(p.Hkv) * p.W * p.D * 2) + stream_qrot_bytes(p.V * p.T, p.Hq, p.D) +
+         stream_tiles_bytes(0, p.P, p.T, p.V, p.F) + stream_merge_desc_bytes(p.nqb, p.V) + stream_flags_bytes(n_rb, p.V) +
+         stream_partial_bytes(n_rb, p.V, p.D);
+}
+
+size_t prefill_report_offset(const KParams& p) {
+  return align256(size_t(p.Hkv) * p.W * p.D * 2) + stream_qrot_bytes(p.W, p.Hq, p.D) +
+         stream_tiles_bytes(1, p.P, p.T, p.V, p.F);
+}
 
 void* verify_scratch(int* status) {
   constexpr int kMaxDevices = 64;

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.fd_view_shift.argtypes, L.fd_view_shift.restype = [G, i64], i64
         L.fd_stream_merge_mode.argtypes, L.fd_stream_merge_mode.restype = [i32], i32
         L.fd_prefill_workspace_bytes.argtypes, L.fd_prefill_workspace_bytes.restype = [G], sz
+        for fn in ("fd_stream_overflow", "fd_prefill_overflow"):
+            getattr(L, fn).argtypes, getattr(L, fn).restype = [G, vp, sz, vp], ctypes.c_int
         L.fd_prefill_attn.argtypes = [G, vp, vp, vp, i64, vp, vp, sz, vp]
         L.fd_prefill_attn.restype = ctypes.c_int
         L.fd_verify_workspace_bytes.argtypes, L.fd_verify_workspace_bytes.restype = [G, i32], sz
@@ -87,7 +89,7 @@ EXPORTS = ("fd_cache_rows", "fd_key_position", "fd_kv_insert_frame", "fd_kv_proj
            "fd_stream_attn", "fd_stream_attn_insert", "fd_stream_attn_view", "fd_stream_attn_insert_view",
            "fd_view_shift", "fd_stream_merge_mode", "fd_prefill_workspace_bytes", "fd_prefill_attn", "fd_verify_workspace_bytes",
            "fd_verify_attn", "fd_verify_batched_workspace_bytes", "fd_verify_attn_batched", "fd_rotate_window",
-           "fd_verify_attn_noalloc", "fd_status_str")
+           "fd_verify_attn_noalloc", "fd_stream_overflow", "fd_prefill_overflow", "fd_status_str")
 
 
 def make_geom(g, out_dtype: str = "f32") -> FdGeom:
@@ -219,6 +221,25 @@ def prefill_attn(g, q_win, k_cache, v_cache, newest_frame: int, out, ws, ws_byte
     _check("fd_prefill_attn", lib().fd_prefill_attn(
         ctypes.byref(make_geom(g, out_dtype)), _ptr(q_win), _ptr(k_cache), _ptr(v_cache),
         int(newest_frame), _ptr(out), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def _overflow(fn: str, g, ws, ws_bytes, stream) -> int:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    r = getattr(lib(), fn)(ctypes.byref(make_geom(g)), _ptr(ws), int(ws_bytes), _stream(stream))
+    if r < 0:
+        raise FdError(fn, r)
+    return r
+
+
+def stream_overflow(g, ws, ws_bytes: int | None = None, stream=None) -> int:
+    """Waves of the last streaming call's rotation pass on ws that rounded an operand out of fp16."""
+    return _overflow("fd_stream_overflow", g, ws, ws_bytes, stream)
+
+
+def prefill_overflow(g, ws, ws_bytes: int | None = None, stream=None) -> int:
+    """Waves of the last prefill call's rotation pass on ws that rounded an operand out of fp16."""
+    return _overflow("fd_prefill_overflow", g, ws, ws_bytes, stream)
 
 
 def verify_workspace_bytes(g, blk_len: int) -> int:

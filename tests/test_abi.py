@@ -126,13 +126,20 @@ def test_call_errors():
     # attention kernel's tile table (8 bytes per tile of each view's key sequence: view 0 prefix
     # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal), the merge descriptors (16
     # bytes per token block and chunk boundary: one here) and the merge tickets (a 4-byte counter
-    # per row block and chunk)
+    # per row block and chunk); last the rotation pass's range report: a 16-byte header and 4
+    # bytes per workgroup of its largest launch (bookkeeping 1, keys 3 (64 rows each over the
+    # 136 window rows, both kv heads at once), queries 2 (32 tokens each, per kv head))
     krot = g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
     qrot = 2 * 16 * 4 * 64 * 2
     n_rb = g.n_kv_heads * 1 * 1
     align = lambda x: (x + 255) // 256 * 256
     assert sws == (align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + align(n_rb * 2 * 4)
-                   + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16))
+                   + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16) + align(16 + 4 * (1 + 3 + 2)))
+    O = L.fd_stream_overflow
+    assert O(None, FAKE, sws, None) == -1 and O(gp, None, sws, None) == -1
+    assert O(gp, FAKE, sws - 1, None) == -7
+    g32 = _g(in_dtype=fd.FD_F32)
+    assert O(ctypes.byref(g32), FAKE, L.fd_stream_workspace_bytes(ctypes.byref(g32)), None) == 0   # fp32: no fp16 operands
     assert L.fd_stream_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 4
     assert L.fd_stream_attn(None, FAKE, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
     assert L.fd_stream_attn(gp, None, FAKE, FAKE, 5, FAKE, FAKE, sws, None) == -1
@@ -254,11 +261,16 @@ def test_prefill_call_errors():
     pws = L.fd_prefill_workspace_bytes(gp)
     # rotated keys, every window row's rotated queries (W = 8 + 2*4*16 = 136 rows) and the tile
     # table (frame (v, j): prefix + v*F + j earlier frames + diagonal, one 64-key tile each here;
-    # then the prefix segment); every segment is attended whole, so no partial slots
+    # then the prefix segment); every segment is attended whole, so no partial slots; last the
+    # range report (bookkeeping 1, keys 3, queries ceil(136 / 32) = 5 per kv head)
     W = 8 + 2 * 4 * 16
     align = lambda x: (x + 255) // 256 * 256
     n_tiles = sum(1 + sg + 1 for sg in range(2 * 4)) + 1
-    assert pws == align(g.n_kv_heads * W * 64 * 2) + align(W * 4 * 64 * 2) + align(n_tiles * 8)
+    assert pws == (align(g.n_kv_heads * W * 64 * 2) + align(W * 4 * 64 * 2) + align(n_tiles * 8)
+                   + align(16 + 4 * (1 + 3 + 5 * 2)))
+    O = L.fd_prefill_overflow
+    assert O(None, FAKE, pws, None) == -1 and O(gp, None, pws, None) == -1 and O(gp, FAKE, pws - 1, None) == -7
+    assert O(ctypes.byref(_g(in_dtype=fd.FD_F32)), FAKE, pws, None) == -3
     assert L.fd_prefill_workspace_bytes(ctypes.byref(_g(in_dtype=fd.FD_F32))) == 0
     assert L.fd_prefill_attn(ctypes.byref(_g(in_dtype=fd.FD_F32)), FAKE, FAKE, FAKE, 5, FAKE, FAKE, pws,
                              None) == -3                                        # bf16 only

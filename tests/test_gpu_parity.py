@@ -828,6 +828,52 @@ def _big_q(a, seed):
     return a
 
 
+def test_rotation_overflow_report():
+    """fd_stream_overflow / fd_prefill_overflow (config-2 shapes): 0 for ordinary inputs; a key
+    (prefix row) or a query element beyond the fp16 operand bound is counted; a later call on
+    the same workspace reports afresh, also a view call whose rotation pass launches fewer
+    workgroups than the overflowing whole-window call before it (the last query workgroup of
+    that call lies past the smaller grid); the prefill call likewise; a workspace no call has
+    written is refused."""
+    w = synth.CONFIGS[2]
+    g = w.geom
+    t = w.first_t
+    kc, vc = H.window_caches(w, 0, t)
+    q = H.q_new(w, 0, t)
+    out = torch.empty((g.n_new, g.n_q_heads, g.head_dim), device=H.DEV)
+    ws = torch.zeros(fd.stream_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    with pytest.raises(fd.FdError):
+        fd.stream_overflow(g, ws)                       # never written: no report
+    fd.stream_attn(g, q, kc, vc, t, out, ws)
+    assert fd.stream_overflow(g, ws) == 0
+    kbig = kc.clone()
+    kbig[1, 3, 5] = 1.0e5                               # prefix row 3 of kv head 1
+    fd.stream_attn(g, q, kbig, vc, t, out, ws)
+    assert fd.stream_overflow(g, ws) >= 1
+    qbig = q.clone()
+    qbig[g.n_new - 1, g.n_q_heads - 1, 9] = 4.0e6       # x log2(e)/sqrt(128): ~5e5 in fp16 units
+    fd.stream_attn(g, qbig, kc, vc, t, out, ws)
+    assert fd.stream_overflow(g, ws) >= 1
+    fd.stream_attn(g, q, kc, vc, t, out, ws)
+    assert fd.stream_overflow(g, ws) == 0
+    view = _key_view(g)
+    fd.stream_attn_view(g, qbig, kc, vc, t, view, -1, out, ws)      # whole window rotated
+    assert fd.stream_overflow(g, ws) >= 1
+    fd.stream_attn_view(g, q, kc, vc, t, view, t, out, ws)          # prefix and new frames only
+    assert fd.stream_overflow(g, ws) == 0
+    pws = torch.empty(fd.prefill_workspace_bytes(g), dtype=torch.uint8, device=H.DEV)
+    gen = torch.Generator(device=H.DEV)
+    gen.manual_seed(5)
+    qw = torch.randn((g.window, g.n_q_heads, g.head_dim), generator=gen, device=H.DEV).to(torch.bfloat16)
+    ow = torch.empty((g.window, g.n_q_heads, g.head_dim), device=H.DEV)
+    fd.prefill_attn(g, qw, kc, vc, t, ow, pws)
+    assert fd.prefill_overflow(g, pws) == 0
+    fd.prefill_attn(g, qw, kbig, vc, t, ow, pws)
+    assert fd.prefill_overflow(g, pws) >= 1
+    fd.prefill_attn(g, qw, kc, vc, t, ow, pws)
+    assert fd.prefill_overflow(g, pws) == 0
+
+
 def test_fp16_operand_bound():
     """Streaming, batched verify with and without a rotated view, and single verify at the
     fp16 operand bound (config-2 shapes, two ring phases): finite and within the bf16
