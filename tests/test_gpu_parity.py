@@ -247,8 +247,8 @@ def test_deterministic():
 MANY_WG = Workload(208, "512 workgroups", Geometry(4, 2, 512, 64, 32, 8, 128, 16, 1e6, dtype=synth.BF16), first_t=2)
 
 
-@pytest.mark.parametrize("w", [synth.CONFIGS[2], synth.CONFIGS[3], synth.CONFIGS[5], MANY_WG],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [synth.CONFIGS[2], synth.CONFIGS[3], synth.CONFIGS[5], MANY_WG]
+                         + [x for x in EXTRA if x.cfg_id in (209, 210)], ids=lambda w: w.name)
 def test_merge_modes_same_bits(w):
     """A view that two workgroups share is merged in the attention kernel by whichever piece
     finishes second (mode 1, the default), by the second piece (mode 2, which makes it finish
