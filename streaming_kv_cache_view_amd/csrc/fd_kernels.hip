@@ -522,6 +522,11 @@ struct NewFrame {
   T* kc;
   T* vc;
 };
+// Bookkeeping workgroups at the front of the rotation pass: one for the tile table, one more for
+// the merge descriptors and tickets when there are any
+__host__ __device__ constexpr int rope_bookkeeping_workgroups(bool tiles, bool mdesc) {
+  return tiles ? (mdesc ? 2 : 1) : 0;
+}
 __host__ __device__ constexpr int rope_q_heads(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 // Work split of the streaming kernel (bf16 path).  A row block is 128 query rows (the
@@ -673,20 +678,24 @@ __global__ __launch_bounds__(256) void rope_window_kernel(const KParams p, const
     reinterpret_cast<int32_t*>(report)[0] = kRopeReportMagic;
     reinterpret_cast<int32_t*>(report)[1] = static_cast<int32_t>(4 * gridDim.x);
   }
-  if (tiles && blockIdx.x == 0) {   // workgroup 0 (with a tile table): the bookkeeping only
+  // bookkeeping workgroups (with a tile table): 0 the attention kernel's tile table, 1 (with
+  // merge descriptors) the descriptors and the cleared merge tickets, side by side
+  const int nbk = rope_bookkeeping_workgroups(tiles != nullptr, mdesc != nullptr);
+  if (static_cast<int>(blockIdx.x) < nbk) {
     report_wave(false);
-    const StreamTiles tt(p);        // the attention kernel's tile table
-    for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
-      for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
-    if (mdesc) {   // the merge kernel's descriptors, [nqb][nseg - 1]
-      const int nb = p.nseg - 1;
+    if (blockIdx.x == 0) {
+      const StreamTiles tt(p);
+      for (int sg = 0, o = 0; sg < tt.segments(); o += tt.view_len(sg), ++sg)
+        for (int t = tid; t < tt.view_len(sg); t += 256) tiles[o + t] = tt.desc(p, sg, t);
+    } else {
+      const int nb = p.nseg - 1;   // the merge kernel's descriptors, [nqb][nseg - 1]
       for (int e = tid; e < p.nqb * nb; e += 256) mdesc[e] = stream_merge_desc(p, e / nb, e % nb + 1);
+      if (flags)   // the attention kernel's merge tickets, cleared for this call
+        for (int e = tid; e < p.Hkv * p.n_hsub * p.nqb * p.nseg; e += 256) flags[e] = 0u;
     }
-    if (flags)   // the attention kernel's merge tickets, cleared for this call
-      for (int e = tid; e < p.Hkv * p.n_hsub * p.nqb * p.nseg; e += 256) flags[e] = 0u;
     return;
   }
-  const int bx = static_cast<int>(blockIdx.x) - (tiles ? 1 : 0);   // rotation workgroup
+  const int bx = static_cast<int>(blockIdx.x) - nbk;   // rotation workgroup
   if (bx >= nkb) {   // query rows (token, head kvh*G + hh)
     // thread (token tl, RoPE chunk pair c) for the workgroup's GH heads of kv head kvh, which
     // share the token's angles; frequencies loaded first, angles computed while the rows fly.
@@ -2921,12 +2930,13 @@ int launch_stream_t(const KParams& p, const void* q, const void* kc, const void*
                        kn ? const_cast<T*>(static_cast<const T*>(vc)) : nullptr};
   if (mdesc && stream_view_cut_twice(p)) return FD_ERR_GEOM;   // the split never cuts a view twice
   unsigned char* report = b16 ? static_cast<unsigned char*>(ws) + stream_report_offset(p) : nullptr;
+  const int nbk = rope_bookkeeping_workgroups(tiles != nullptr, mdesc != nullptr);
   if (kn)
-    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((rope_window_kernel<T, D, true>), dim3(nbk + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
                        static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf,
                        report);
   else
-    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3((tiles ? 1 : 0) + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+    hipLaunchKernelGGL((rope_window_kernel<T, D, false>), dim3(nbk + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
                        static_cast<const T*>(kc), krot, nkb, static_cast<const T*>(q), qrot, tiles, mdesc, flags, nf,
                        report);
   if (hipGetLastError() != hipSuccess) return FD_ERR_HIP;
@@ -2958,7 +2968,8 @@ int launch_prefill_t(const KParams& p, const void* q, const void* kc, const void
   QKT* qrot = reinterpret_cast<QKT*>(static_cast<unsigned char*>(ws) + align256(size_t(p.Hkv) * p.W * D * sizeof(QKT)));
   int2* tiles = reinterpret_cast<int2*>(reinterpret_cast<unsigned char*>(qrot) + stream_qrot_bytes(p.W, p.Hq, D));
   const int nkb = rope_key_workgroups<bf16, D>(p), nqk = ceil_div(p.W, kRopeQTok) * (p.G / rope_q_heads(p.G));
-  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(1 + nkb + nqk * p.Hkv), dim3(256), 0, st, p,
+  hipLaunchKernelGGL((rope_window_kernel<bf16, D, false>), dim3(rope_bookkeeping_workgroups(true, false) + nkb + nqk * p.Hkv),
+                     dim3(256), 0, st, p,
                      static_cast<const bf16*>(kc), krot, nkb, static_cast<const bf16*>(q), qrot, tiles, nullptr, nullptr,
                      NewFrame<bf16>{nullptr, nullptr, nullptr, nullptr},
                      static_cast<unsigned char*>(ws) + prefill_report_offset(p));
@@ -3038,7 +3049,8 @@ int rope_max_workgroups(const KParams& p, bool prefill) {
   q.rot_new = 0;   // the whole window: the largest key grid
   const int nkb = p.D == 128 ? rope_key_workgroups<bf16, 128>(q) : rope_key_workgroups<bf16, 64>(q);
   const int rows = prefill ? p.W : p.V * p.T;
-  return 1 + nkb + ceil_div(rows, kRopeQTok) * (p.G / rope_q_heads(p.G)) * p.Hkv;
+  return rope_bookkeeping_workgroups(true, !prefill && p.V > 1) + nkb +
+         ceil_div(rows, kRopeQTok) * (p.G / rope_q_heads(p.G)) * p.Hkv;
 }
 
 size_t stream_report_offset(const KParams& p) {

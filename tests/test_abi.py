@@ -127,14 +127,14 @@ def test_call_errors():
     # + 3 frames + diagonal, view 1 prefix + 7 frames + diagonal), the merge descriptors (16
     # bytes per token block and chunk boundary: one here) and the merge tickets (a 4-byte counter
     # per row block and chunk); last the rotation pass's range report: a 16-byte header and 4
-    # bytes per workgroup of its largest launch (bookkeeping 1, keys 3 (64 rows each over the
+    # bytes per workgroup of its largest launch (bookkeeping 2, keys 3 (64 rows each over the
     # 136 window rows, both kv heads at once), queries 2 (32 tokens each, per kv head))
     krot = g.n_kv_heads * (8 + 2 * 4 * 16) * 64 * 2
     qrot = 2 * 16 * 4 * 64 * 2
     n_rb = g.n_kv_heads * 1 * 1
     align = lambda x: (x + 255) // 256 * 256
     assert sws == (align(krot) + align(qrot) + align((5 + 9) * 8) + align(1 * 16) + align(n_rb * 2 * 4)
-                   + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16) + align(16 + 4 * (1 + 3 + 2)))
+                   + n_rb * 2 * 2 * (128 * 64 * 2 + 128 * 16) + align(16 + 4 * (2 + 3 + 2)))
     O = L.fd_stream_overflow
     assert O(None, FAKE, sws, None) == -1 and O(gp, None, sws, None) == -1
     assert O(gp, FAKE, sws - 1, None) == -7
