@@ -2587,12 +2587,24 @@ __global__ __launch_bounds__(64 * kVerifyWavesDma) void verify_dma_kernel(
       float fk[2][E];
 #pragma unroll
       for (int u = 0; u < NU / 2; ++u) {
-        BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4)), fk[0]);
-        BF16Ops::unpack(ld16(Kt + l32 * ROWB + (((2 * (u + NU / 2) + h) ^ kswz(l32)) << 4)), fk[1]);
+        // this step's K chunks and the 16 angle factors it needs, read before any is used: left
+        // to itself the compiler waited after nearly every LDS read here (~40 serialized round
+        // trips per wave over the four steps)
+        const u32x4 k0 = ld16(Kt + l32 * ROWB + (((2 * u + h) ^ kswz(l32)) << 4));
+        const u32x4 k1 = ld16(Kt + l32 * ROWB + (((2 * (u + NU / 2) + h) ^ kswz(l32)) << 4));
+        float2 cb[E], an[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int i = 2 * E * u + E * h + e;
-          const float2 ck = cmul(cbase[w][i], ang[i * 32 + l32]);
+          cb[e] = cbase[w][i];
+          an[e] = ang[i * 32 + l32];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        BF16Ops::unpack(k0, fk[0]);
+        BF16Ops::unpack(k1, fk[1]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float2 ck = cmul(cb[e], an[e]);
           const float a = fk[0][e], c = fk[1][e];
           fk[0][e] = a * ck.x - c * ck.y;
           fk[1][e] = c * ck.x + a * ck.y;
