@@ -1751,14 +1751,22 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     const float lsum = a0 * l_half + a1 * l1;
     const float inv = whole ? 1.f / lsum : 1.f;
     const float f0 = a0 * inv, f1 = a1 * inv;
+    // the other group's rows read all at once, then combined and written back: left to itself
+    // the compiler read, waited and wrote one cell at a time (16 serialized LDS round trips)
+    f32x4 ov[ND][4];
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) ov[d][ig] = *reinterpret_cast<const f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         f32x4* cell = reinterpret_cast<f32x4*>(mb + l32 * (D + 4) + 32 * d + 8 * ig + 4 * h);
-        const f32x4 ov = *cell;
-        *cell = f32x4{o[d][4 * ig] * f0 + ov[0] * f1, o[d][4 * ig + 1] * f0 + ov[1] * f1,
-                      o[d][4 * ig + 2] * f0 + ov[2] * f1, o[d][4 * ig + 3] * f0 + ov[3] * f1};
+        const f32x4 v = ov[d][ig];
+        *cell = f32x4{o[d][4 * ig] * f0 + v[0] * f1, o[d][4 * ig + 1] * f0 + v[1] * f1,
+                      o[d][4 * ig + 2] * f0 + v[2] * f1, o[d][4 * ig + 3] * f0 + v[3] * f1};
       }
     }
     if (h == 0) {   // (each lane has read its own entries above)
@@ -1819,22 +1827,36 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     return F16Ops::pack(x8);
   };
   if (whole) {
-    const int TPR = p.out_bf16 ? D / 8 : D / 4;   // lanes per row
-    for (int r = tid / TPR; r < 128; r += 512 / TPR) {
-      const int ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
-      if (tk >= p.qtok || hsub * p.HPW + (ww % p.HPW) >= p.G) continue;
-      const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
-      const int c = tid % TPR;
-      const float* src = rows + r * (D + 4);
-      const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D;
-      if (p.out_bf16) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(src + 8 * c), hi = *reinterpret_cast<const f32x4*>(src + 8 * c + 4);
-        float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        st16(static_cast<bf16*>(out) + obase + 8 * c, BF16Ops::pack(x8));
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + 4 * c) = *reinterpret_cast<const f32x4*>(src + 4 * c);
+    // every row this thread writes read from LDS first, then stored (one LDS round trip, not one
+    // per row pass): TPR lanes per row, 512 / TPR rows per pass
+    auto store_rows = [&](auto bf16_out) {
+      constexpr bool B16 = decltype(bf16_out)::value;
+      constexpr int TPR = B16 ? D / 8 : D / 4, RPP = 512 / TPR, NPASS = 128 / RPP, NV = B16 ? 2 : 1;
+      const int c = tid % TPR, r0 = tid / TPR;
+      f32x4 vals[NPASS][NV];
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          vals[k][j] = *reinterpret_cast<const f32x4*>(rows + (r0 + RPP * k) * (D + 4) + (B16 ? 8 * c + 4 * j : 4 * c));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < NPASS; ++k) {
+        const int r = r0 + RPP * k, ww = r >> 5, tk = tok0 + 32 * (ww / p.HPW) + (r & 31);
+        if (tk >= p.qtok || hsub * p.HPW + (ww % p.HPW) >= p.G) continue;
+        const int hd = kvh * p.G + hsub * p.HPW + (ww % p.HPW);
+        const int64_t obase = (static_cast<int64_t>(qrow0 + tk) * p.Hq + hd) * D;
+        if constexpr (B16) {
+          float x8[8] = {vals[k][0][0], vals[k][0][1], vals[k][0][2], vals[k][0][3],
+                         vals[k][1][0], vals[k][1][1], vals[k][1][2], vals[k][1][3]};
+          st16(static_cast<bf16*>(out) + obase + 8 * c, BF16Ops::pack(x8));
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + obase + 4 * c) = vals[k][0];
+        }
       }
-    }
+    };
+    if (p.out_bf16) store_rows(std::true_type{});
+    else store_rows(std::false_type{});
   } else {   // this job's piece of view v: unnormalised O scaled per row and rounded to fp16,
              // then (row max M, row sum l, 1 / scale) (stream_slot)
     unsigned* const cnt = role != 0 ? flags + rbi * p.nseg + (role == 1 ? chunk + 1 : chunk) : nullptr;
