@@ -2915,16 +2915,28 @@ __global__ __launch_bounds__(256) void verify_merge_dma_kernel(const KParams p, 
   sA[threadIdx.x] = acc;
   __syncthreads();
   if (sg != 0 || hh >= p.G) return;
+  // every group's (M, L, acc) read first, then folded in group order (read one group at a time
+  // under the branch, the LDS round trips ran back to back)
+  float mgs[SG], lgs[SG];
+  f32x4 ags[SG];
+#pragma unroll
+  for (int g = 0; g < SG; ++g) {
+    mgs[g] = sM[g * 32 + q];
+    lgs[g] = sL[g * 32 + q];
+    ags[g] = sA[g * 32 + q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float Mt = -INFINITY;
-  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, sM[g * 32 + q]);
+#pragma unroll
+  for (int g = 0; g < SG; ++g) Mt = fmaxf(Mt, mgs[g]);
   float Lt = 0.f;
   f32x4 At = f32x4{};
+#pragma unroll
   for (int g = 0; g < SG; ++g) {
-    const float mg = sM[g * 32 + q];
-    if (mg == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(mg - Mt);
-    Lt += f * sL[g * 32 + q];
-    At += f * sA[g * 32 + q];
+    if (mgs[g] == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(mgs[g] - Mt);
+    Lt += f * lgs[g];
+    At += f * ags[g];
   }
   const f32x4 res = At * (1.f / Lt);
   const int64_t oidx = (static_cast<int64_t>(dft * p.B + b) * p.Hq + kvh * p.G + hh) * p.D + 4 * c;
