@@ -1809,22 +1809,42 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
   // is token tok0 + 32*((r/32)/HPW) + r%32 of query head kvh*G + hsub*HPW + (r/32)%HPW.
   const float* rows = reinterpret_cast<const float*>(buf);
   constexpr int TPQ = D / 8;   // lanes per row of a partial (aligned groups within a wave), 8 values each
-  // row r's 8 values from lane c of its group, scaled by its row's power of two 2^sc (the
-  // largest magnitude over the row's lanes) and rounded to fp16: the stored partial's values
-  auto quant_row = [&](int r, int c, int& sc) -> u32x4 {
-    const float* src = rows + r * (D + 4) + 8 * c;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
-    float x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    float mx = 0.f;
+  // lane c of its group holds 8 values of a row, scaled by that row's power of two 2^sc (the
+  // largest magnitude over the row's lanes) and rounded to fp16: the stored partial's values.
+  // Each thread covers rows rb + RPQ*k; all of them are read from LDS before any is scaled.
+  constexpr int RPQ = 512 / TPQ, NPQ = 128 / RPQ;
+  const int qc = tid % TPQ, rb = tid / TPQ;
+  f32x4 qv[NPQ][2];
+  auto read_rows = [&]() {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x8[e]));
+    for (int k = 0; k < NPQ; ++k) {
+      const float* src = rows + (rb + RPQ * k) * (D + 4) + 8 * qc;
+      qv[k][0] = *reinterpret_cast<const f32x4*>(src);
+      qv[k][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+  };
+  auto quant_rows = [&](u32x4 (&pk)[NPQ], int (&sc)[NPQ]) {
+    float mx[NPQ];
 #pragma unroll
-    for (int o = 1; o < TPQ; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    sc = partial_row_scale(mx);
-    const float mul = exp2_int(sc);
+    for (int k = 0; k < NPQ; ++k) {
+      mx[k] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x8[e] *= mul;
-    return F16Ops::pack(x8);
+      for (int e = 0; e < 4; ++e) mx[k] = fmaxf(mx[k], fmaxf(fabsf(qv[k][0][e]), fabsf(qv[k][1][e])));
+    }
+#pragma unroll
+    for (int o = 1; o < TPQ; o <<= 1)
+#pragma unroll
+      for (int k = 0; k < NPQ; ++k) mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o));
+#pragma unroll
+    for (int k = 0; k < NPQ; ++k) {
+      sc[k] = partial_row_scale(mx[k]);
+      const float mul = exp2_int(sc[k]);
+      float x8[8] = {qv[k][0][0], qv[k][0][1], qv[k][0][2], qv[k][0][3],
+                     qv[k][1][0], qv[k][1][1], qv[k][1][2], qv[k][1][3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x8[e] *= mul;
+      pk[k] = F16Ops::pack(x8);
+    }
   };
   if (whole) {
     // every row this thread writes read from LDS first, then stored (one LDS round trip, not one
@@ -1869,11 +1889,16 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     }
     if (!merge_now) {
       float* slot = stream_slot<D>(part, p, rbi, chunk, (sv + ja == c0) ? 0 : 1);   // first job, or last
-      for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
-        const int c = tid % TPQ;
-        int sc;
-        const u32x4 pk = quant_row(r, c, sc);
-        const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-sc), 0.f};
+      u32x4 pkq[NPQ];
+      int scq[NPQ];
+      read_rows();
+      __builtin_amdgcn_sched_barrier(0);
+      quant_rows(pkq, scq);
+#pragma unroll
+      for (int k = 0; k < NPQ; ++k) {
+        const int r = rb + RPQ * k, c = qc;
+        const u32x4 pk = pkq[k];
+        const f32x4 mlv = f32x4{red_m[r >> 5][r & 31], red_l[r >> 5][r & 31], exp2_int(-scq[k]), 0.f};
         uint64_t* dst = reinterpret_cast<uint64_t*>(reinterpret_cast<_Float16*>(slot) + r * D);   // partial_col
         const uint64_t lo = (static_cast<uint64_t>(pk[1]) << 32) | pk[0], hi = (static_cast<uint64_t>(pk[3]) << 32) | pk[2];
         if (role != 0) {   // read by the other piece's workgroup within this launch: device scope
@@ -1909,21 +1934,32 @@ __device__ __forceinline__ void stream_pp_body(const KParams& p, const int block
     if (merge_now) {
       const float* other = role == 1 ? stream_slot<D>(part, p, rbi, chunk + 1, 0)
                                      : stream_slot<D>(part, p, rbi, chunk - 1, which_a);
-      for (int r = tid / TPQ; r < 128; r += 512 / TPQ) {
-        const int c = tid % TPQ;
-        int sc;
-        const u32x4 own = quant_row(r, c, sc);
+      // the other piece's rows and this piece's rows all requested before the first is used
+      uint64_t o0[NPQ], o1[NPQ], om[NPQ], os[NPQ];
+#pragma unroll
+      for (int k = 0; k < NPQ; ++k) {
+        const int r = rb + RPQ * k;
         const uint64_t* osrc = reinterpret_cast<const uint64_t*>(reinterpret_cast<const _Float16*>(other) + r * D);
         const uint64_t* oml = reinterpret_cast<const uint64_t*>(other + 64 * D + 4 * r);
-        const uint64_t o0 = __hip_atomic_load(osrc + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // partial_col
-        const uint64_t o1 = __hip_atomic_load(osrc + TPQ + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t om = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t os = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float m_o = __uint_as_float(static_cast<uint32_t>(om)), l_o = __uint_as_float(static_cast<uint32_t>(om >> 32));
-        const float s_o = __uint_as_float(static_cast<uint32_t>(os));
-        const float m_s = red_m[r >> 5][r & 31], l_s = red_l[r >> 5][r & 31], s_s = exp2_int(-sc);
-        const u32x2 x_o0{static_cast<uint32_t>(o0), static_cast<uint32_t>(o0 >> 32)};
-        const u32x2 x_o1{static_cast<uint32_t>(o1), static_cast<uint32_t>(o1 >> 32)};
+        o0[k] = __hip_atomic_load(osrc + qc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // partial_col
+        o1[k] = __hip_atomic_load(osrc + TPQ + qc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        om[k] = __hip_atomic_load(oml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        os[k] = __hip_atomic_load(oml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      read_rows();
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 ownq[NPQ];
+      int scq[NPQ];
+      quant_rows(ownq, scq);
+#pragma unroll
+      for (int k = 0; k < NPQ; ++k) {
+        const int r = rb + RPQ * k, c = qc;
+        const u32x4 own = ownq[k];
+        const float m_o = __uint_as_float(static_cast<uint32_t>(om[k])), l_o = __uint_as_float(static_cast<uint32_t>(om[k] >> 32));
+        const float s_o = __uint_as_float(static_cast<uint32_t>(os[k]));
+        const float m_s = red_m[r >> 5][r & 31], l_s = red_l[r >> 5][r & 31], s_s = exp2_int(-scq[k]);
+        const u32x2 x_o0{static_cast<uint32_t>(o0[k]), static_cast<uint32_t>(o0[k] >> 32)};
+        const u32x2 x_o1{static_cast<uint32_t>(o1[k]), static_cast<uint32_t>(o1[k] >> 32)};
         const u32x2 x_s0{own[0], own[1]}, x_s1{own[2], own[3]};
         const f32x4 r0 = role == 1 ? merge_two(m_s, l_s, s_s, x_s0, m_o, l_o, s_o, x_o0)
                                    : merge_two(m_o, l_o, s_o, x_o0, m_s, l_s, s_s, x_s0);
